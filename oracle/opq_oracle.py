@@ -1,0 +1,242 @@
+"""Plain, slow CPU oracle for OPQ (Optimal Power Quantization), 4-bit, per output row.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no code,
+table or constant generator with the HIP library and imports nothing from it.
+
+Source of every step: the model card "OPQ INT4 Z-Image: 最优幂次量化扩散模型推理"
+(huggingpeers.co/models/dfytensor/OPQ-INT4-Z-Image):
+
+* section "OPQ 原理" (OPQ principle): normalise u = |w| / max|w|, compand
+  v = u^alpha, code q = round(15 v), reconstruct w' = sign(w) (q/15)^(1/alpha) max|w|;
+* section "技术细节 / 存储格式" (storage format): a 4-bit magnitude, eight per
+  uint32; a 1-bit sign plane, thirty-two per uint32; one max per group;
+* section "技术细节 / 推理解码" (decode): q/15, raised to 1/alpha, times sign
+  and the group max.
+
+Readings taken where the page is silent (each is listed in the design doc):
+
+* the max is taken per output row and kept as an fp32 scale (the card keeps an
+  fp16 max per group of 128; the per-row form is the workload's);
+* alpha is the exact binary32 value the caller passes;
+* u is the IEEE binary32 quotient |w| / m rounded to nearest even, with
+  subnormals kept; q is the integer nearest to 15 u^alpha evaluated exactly,
+  halves going up (an exact half happens only for alpha = 1, u = 1/2);
+* the sign bit is 1 exactly when w < 0 (so -0.0 gives 0), and a code of 0
+  always reconstructs to +0.0;
+* packing is little-endian along K: code k of a row sits in bits 4(k%8)..4(k%8)+3
+  of word k//8, sign k in bit k%32 of word k//32;
+* a row whose max is 0 gets scale 0, all codes 0 and all signs 0;
+* the reconstruction is the real value sign (q/15)^(1/alpha) m rounded once to
+  bfloat16 (round to nearest even); here it is evaluated in float64 first;
+* the linear layer is y = x W'^T (+ bias) over the bf16 reconstructions,
+  accumulated here in float64.
+
+Every function below is pinned by the CPU tests in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import math
+
+import mpmath
+import numpy as np
+
+LEVELS = 15          # 4-bit magnitude codes 0..15 ("q = round(v x 15)")
+CODES_PER_WORD = 8   # "8 个打包进 1 个 uint32"
+SIGNS_PER_WORD = 32  # "32 个打包进 1 个 uint32"
+
+__all__ = [
+    "LEVELS", "alpha_f32", "bf16_bits_to_f32", "f64_to_bf16_bits", "row_absmax",
+    "encode", "pack", "unpack", "quantize", "reconstruct", "dequantize",
+    "linear", "snr_db", "decision_thresholds_f32",
+]
+
+
+# ---------------------------------------------------------------- number formats
+
+def alpha_f32(alpha: float) -> float:
+    """The exact binary32 value of alpha, as a Python float."""
+    return float(np.float32(alpha))
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """Widen bfloat16 bit patterns (uint16) to float32; exact."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32)
+
+
+def f64_to_bf16_bits(d) -> np.ndarray:
+    """Round float64 values to bfloat16 (nearest, ties to even) in one step.
+
+    bfloat16 has 8 significant bits and binary32's exponent range; below
+    2^-126 its spacing is the fixed 2^-133.  Values past the largest finite
+    bfloat16 after rounding become infinity.  NaN is not expected here.
+    """
+    d = np.asarray(d, dtype=np.float64)
+    neg = np.signbit(d)
+    a = np.abs(d)
+    _, e = np.frexp(a)                       # a = f * 2^e with f in [0.5, 1)
+    quantum_exp = np.maximum(e.astype(np.int64) - 8, -133)
+    k = np.rint(np.ldexp(a, -quantum_exp))   # exact scaling, ties to even
+    val = np.ldexp(k, quantum_exp)           # representable in bfloat16 (or 2^128)
+    with np.errstate(over="ignore"):
+        f32 = val.astype(np.float32)         # exact, or inf past the range
+    bits = (f32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return np.where(neg, bits | np.uint16(0x8000), bits).astype(np.uint16)
+
+
+# ---------------------------------------------------------------- quantizer
+
+def row_absmax(w32: np.ndarray) -> np.ndarray:
+    """m_n = max_k |w[n,k]| in float32 ("max(|w|)"); exact in any order."""
+    w32 = np.asarray(w32, dtype=np.float32)
+    if w32.shape[1] == 0:
+        return np.zeros(w32.shape[0], np.float32)
+    return np.max(np.abs(w32), axis=1).astype(np.float32)
+
+
+def _nearest_code_exact(u: float, alpha: float) -> int:
+    """round(15 u^alpha) at 200 bits; halves go up."""
+    with mpmath.workprec(200):
+        v = mpmath.mpf(LEVELS) * mpmath.power(mpmath.mpf(u), mpmath.mpf(alpha))
+        fl = mpmath.floor(v)
+        q = int(fl) + (1 if v - fl >= mpmath.mpf(0.5) else 0)
+    return min(max(q, 0), LEVELS)
+
+
+def encode(w32: np.ndarray, alpha: float):
+    """Codes, signs and scales of a float32 matrix w[N, K].
+
+    Steps of the card's "OPQ 原理": u = |w| / max|w| (binary32 division),
+    v = u^alpha, q = round(15 v).  Returns (q uint8 [N,K], s uint8 [N,K],
+    scale float32 [N]).
+    """
+    w32 = np.ascontiguousarray(w32, dtype=np.float32)
+    a64 = alpha_f32(alpha)
+    m = row_absmax(w32)
+    absw = np.abs(w32)
+    u = np.zeros_like(absw)
+    live = m > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u[live] = absw[live] / m[live, None]          # IEEE binary32 quotient
+    v = LEVELS * np.power(u.astype(np.float64), a64)
+    q = np.floor(v + 0.5)
+    # Values whose float64 v sits next to a half are settled exactly.
+    frac = v - np.floor(v)
+    for r, c in np.argwhere(np.abs(frac - 0.5) < 1e-9):
+        q[r, c] = _nearest_code_exact(float(u[r, c]), a64)
+    q = np.clip(q, 0, LEVELS).astype(np.uint8)
+    s = (w32 < 0).astype(np.uint8)                    # -0.0 is not < 0
+    return q, s, m
+
+
+def pack(q: np.ndarray, s: np.ndarray):
+    """Pack codes eight per uint32 and signs thirty-two per uint32 (K order,
+    least significant first).  K must be a multiple of 32."""
+    q = np.asarray(q, dtype=np.uint32)
+    s = np.asarray(s, dtype=np.uint32)
+    n, k = q.shape
+    assert k % SIGNS_PER_WORD == 0
+    qg = q.reshape(n, k // CODES_PER_WORD, CODES_PER_WORD)
+    packed = np.zeros((n, k // CODES_PER_WORD), np.uint32)
+    for i in range(CODES_PER_WORD):
+        packed |= (qg[:, :, i] & np.uint32(0xF)) << np.uint32(4 * i)
+    sg = s.reshape(n, k // SIGNS_PER_WORD, SIGNS_PER_WORD)
+    sign = np.zeros((n, k // SIGNS_PER_WORD), np.uint32)
+    for i in range(SIGNS_PER_WORD):
+        sign |= (sg[:, :, i] & np.uint32(1)) << np.uint32(i)
+    return packed, sign
+
+
+def unpack(packed: np.ndarray, sign: np.ndarray):
+    """Inverse of :func:`pack`: (q uint8 [N,K], s uint8 [N,K])."""
+    packed = np.asarray(packed, dtype=np.uint32)
+    sign = np.asarray(sign, dtype=np.uint32)
+    n, kw = packed.shape
+    q = np.zeros((n, kw, CODES_PER_WORD), np.uint8)
+    for i in range(CODES_PER_WORD):
+        q[:, :, i] = (packed >> np.uint32(4 * i)) & np.uint32(0xF)
+    s = np.zeros((n, sign.shape[1], SIGNS_PER_WORD), np.uint8)
+    for i in range(SIGNS_PER_WORD):
+        s[:, :, i] = (sign >> np.uint32(i)) & np.uint32(1)
+    return q.reshape(n, -1), s.reshape(n, -1)
+
+
+def quantize(w32: np.ndarray, alpha: float):
+    """Quantize w[N, K] (float32 values) to (packed, sign, scale)."""
+    q, s, m = encode(w32, alpha)
+    packed, sign = pack(q, s)
+    return packed, sign, m
+
+
+# ---------------------------------------------------------------- dequantizer
+
+def reconstruct(q: np.ndarray, s: np.ndarray, scale: np.ndarray, alpha: float) -> np.ndarray:
+    """w' = sign (q/15)^(1/alpha) m in float64 (section "推理解码"); q = 0 gives +0."""
+    a64 = alpha_f32(alpha)
+    q64 = np.asarray(q, dtype=np.float64)
+    mag = np.power(q64 / LEVELS, 1.0 / a64) * np.asarray(scale, np.float64)[:, None]
+    neg = (np.asarray(s) != 0) & (np.asarray(q) != 0)
+    return np.where(neg, -mag, mag)
+
+
+def dequantize(packed: np.ndarray, sign: np.ndarray, scale: np.ndarray, alpha: float) -> np.ndarray:
+    """Dequantize to bfloat16 bit patterns (uint16 [N, K]), rounded once."""
+    q, s = unpack(packed, sign)
+    return f64_to_bf16_bits(reconstruct(q, s, scale, alpha))
+
+
+# ---------------------------------------------------------------- linear layer
+
+def linear(x_bf16: np.ndarray, wdq_bf16: np.ndarray, bias=None) -> np.ndarray:
+    """y[M, N] = x[M, K] . W'[N, K]^T (+ bias[N]) over bf16 inputs, in float64.
+
+    x and W' are bfloat16 bit patterns; every product is exact in float64.
+    """
+    x = bf16_bits_to_f32(x_bf16).astype(np.float64)
+    w = bf16_bits_to_f32(wdq_bf16).astype(np.float64)
+    y = x @ w.T
+    if bias is not None:
+        y = y + np.asarray(bias, dtype=np.float64)[None, :]
+    return y
+
+
+def snr_db(w: np.ndarray, w_rec: np.ndarray) -> float:
+    """10 log10(sum w^2 / sum (w - w')^2) over a whole tensor, in float64."""
+    w = np.asarray(w, np.float64)
+    e = w - np.asarray(w_rec, np.float64)
+    num = float(np.sum(w * w))
+    den = float(np.sum(e * e))
+    if den == 0.0:
+        return math.inf
+    return 10.0 * math.log10(num / den)
+
+
+# ---------------------------------------------------------------- decision points
+
+def decision_thresholds_f32(alpha: float) -> np.ndarray:
+    """T_k = the smallest binary32 t with 15 t^alpha >= k - 1/2, k = 1..15.
+
+    For binary32 u in [0, 1], round(15 u^alpha) (halves up) equals the number
+    of k with u >= T_k.  Computed with mpmath at 200 bits: the real boundary
+    ((2k-1)/30)^(1/alpha) is rounded to binary32 and stepped up or down by one
+    ulp until the condition holds at T_k and fails one ulp below.
+    """
+    a = alpha_f32(alpha)
+    out = np.zeros(LEVELS, np.float32)
+    with mpmath.workprec(200):
+        A = mpmath.mpf(a)
+
+        def ok(t: np.float32, k: int) -> bool:
+            v = LEVELS * mpmath.power(mpmath.mpf(float(t)), A)
+            return v >= k - mpmath.mpf(0.5)
+
+        for k in range(1, LEVELS + 1):
+            b = mpmath.power(mpmath.mpf(2 * k - 1) / 30, 1 / A)
+            t = np.float32(float(b))
+            while not ok(t, k):
+                t = np.nextafter(t, np.float32(np.inf))
+            while t > 0 and ok(np.nextafter(t, np.float32(0)), k):
+                t = np.nextafter(t, np.float32(0))
+            out[k - 1] = t
+    return out

@@ -1,0 +1,419 @@
+"""Pins for the CPU oracle: closed forms, exact rational special cases,
+brute force and invariants, each independent of the oracle's own code path.
+
+The method is the model card "OPQ INT4 Z-Image" (section "OPQ 原理" for the
+quantizer, "技术细节 / 存储格式" for packing, "技术细节 / 推理解码" for the
+decode).  The card prints no worked numeric example, so the fixtures here are
+closed forms and hand-built words (tests/golden/packing_example.txt).
+"""
+import math
+import os
+from fractions import Fraction
+
+import mpmath
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from tests.exact import bf16_bits_of, exact_quotient_f32, f32_of, round_fraction
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_rows(seed, n, k, scale=0.02):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_t(4, size=(n, k)) * scale).astype(np.float32)
+
+
+def _to_bf16_values(w32):
+    """Round float32 to bf16 with torch's cast, back to float32 values."""
+    t = torch.from_numpy(np.ascontiguousarray(w32)).to(torch.bfloat16).to(torch.float32)
+    return t.numpy()
+
+
+# ------------------------------------------------------------------ number formats
+
+def test_f64_to_bf16_agrees_with_torch_cast():
+    rng = np.random.default_rng(11)
+    vals = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),     # subnormal range
+        (rng.standard_normal(2000) * 1e37).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, -2.0, 3.3895314e38, 1e-45, -1e-45], np.float32),
+    ])
+    # exact midpoints between neighbouring bf16 values: ties to even
+    base = rng.integers(0x0080, 0x7F00, 4000).astype(np.uint32) << 16
+    mids = (base | 0x8000).view(np.float32)
+    vals = np.concatenate([vals, mids, -mids])
+    mine = O.f64_to_bf16_bits(vals.astype(np.float64))
+    ref = torch.from_numpy(vals).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+def test_f64_to_bf16_exact_rational():
+    """Float64 inputs that no float32 holds: compare with exact rounding."""
+    rng = np.random.default_rng(12)
+    d = rng.standard_normal(3000) * np.exp2(rng.integers(-130, 100, 3000))
+    mine = O.f64_to_bf16_bits(d)
+    ref = np.array([bf16_bits_of(Fraction(float(x))) for x in d], np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+def test_bf16_widen_known_patterns():
+    bits = np.array([0x3F80, 0xC000, 0x0001, 0x7F80, 0x0000, 0x8000], np.uint16)
+    v = O.bf16_bits_to_f32(bits)
+    assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 2.0 ** -133
+    assert np.isinf(v[3]) and v[4] == 0.0 and np.signbit(v[5])
+
+
+# ------------------------------------------------------------------ absmax
+
+def test_absmax_planted():
+    w = _rand_rows(1, 17, 96)
+    planted = np.float32(-0.731)
+    w[5, 40] = planted
+    m = O.row_absmax(w)
+    assert m[5] == np.float32(0.731)
+    assert np.all(m >= np.abs(w).max(axis=1)) and np.all(m <= np.abs(w).max(axis=1))
+
+
+# ------------------------------------------------------------------ codes: exact closed forms
+
+def _exact_u(w, m):
+    return [[exact_quotient_f32(np.float32(abs(x)), np.float32(mm)) for x in row]
+            for row, mm in zip(w, m)]
+
+
+def _codes_closed_form(w, rule):
+    m = np.max(np.abs(w), axis=1)
+    us = _exact_u(w, m)
+    return np.array([[rule(u) for u in row] for row in us], np.uint8)
+
+
+def test_alpha_one_is_uniform_absmax_rounding():
+    """alpha = 1: q = rint(15 u), the textbook symmetric absmax quantizer
+    (the card's "传统均匀量化" baseline)."""
+    w = _rand_rows(2, 6, 64)
+    w[0, 3] = np.float32(0.5) * np.abs(w[0]).max()      # exact tie u = 1/2 -> 8
+    q, _, _ = O.encode(w, 1.0)
+    ref = _codes_closed_form(w, lambda u: int(np.rint(15 * float(u))))
+    assert np.array_equal(q, ref)
+    assert q[0, 3] == 8
+
+
+@pytest.mark.parametrize("alpha,rule", [
+    # 15 sqrt(u) >= k - 1/2  <=>  900 u >= (2k-1)^2
+    (0.5, lambda u: sum(1 for k in range(1, 16) if 900 * u >= (2 * k - 1) ** 2)),
+    # 15 u^2 >= k - 1/2      <=>  30 u^2 >= 2k-1
+    (2.0, lambda u: sum(1 for k in range(1, 16) if 30 * u * u >= 2 * k - 1)),
+    # 15 u^(1/4) >= k - 1/2  <=>  30^4 u >= (2k-1)^4
+    (0.25, lambda u: sum(1 for k in range(1, 16) if 810000 * u >= (2 * k - 1) ** 4)),
+])
+def test_dyadic_alpha_exact_rational_codes(alpha, rule):
+    w = _rand_rows(3, 6, 64)
+    q, _, _ = O.encode(w, alpha)
+    assert np.array_equal(q, _codes_closed_form(w, rule))
+
+
+def test_special_values():
+    w = _rand_rows(4, 4, 64)
+    w[1, :] = 0.0
+    w[1, 7] = -0.0
+    w[2, 9] = -np.abs(w[2]).max() * 2          # the row max, negative
+    w[3, 0] = -0.0
+    w[3, 1] = np.float32(-1e-30)               # tiny negative: q = 0 but sign 1
+    q, s, m = O.encode(w, 0.73)
+    assert m[1] == 0 and not q[1].any() and not s[1].any()
+    assert q[2, 9] == 15 and s[2, 9] == 1
+    at_max = (np.abs(w) == m[:, None]) & (m[:, None] > 0)
+    assert at_max.sum() >= 3 and np.all(q[at_max] == 15)
+    assert q[3, 0] == 0 and s[3, 0] == 0
+    assert q[3, 1] == 0 and s[3, 1] == 1
+    assert np.all(q[w == 0] == 0)
+
+
+@pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0])
+def test_codes_monotone_in_magnitude(alpha):
+    w = _rand_rows(5, 8, 512)
+    q, _, _ = O.encode(w, alpha)
+    for r in range(w.shape[0]):
+        order = np.argsort(np.abs(w[r]), kind="stable")
+        assert np.all(np.diff(q[r, order].astype(int)) >= 0)
+
+
+@pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0])
+def test_bruteforce_nearest_level(alpha):
+    """Every code is the nearest of the 16 levels j in v-space,
+    argmin_j |15 u^alpha - j| (ties to the larger j), in mpmath."""
+    w = _rand_rows(6, 3, 32)
+    q, _, m = O.encode(w, alpha)
+    a = mpmath.mpf(O.alpha_f32(alpha))
+    with mpmath.workprec(120):
+        for r in range(w.shape[0]):
+            for c in range(w.shape[1]):
+                u = exact_quotient_f32(np.float32(abs(w[r, c])), m[r])
+                v = 15 * mpmath.power(mpmath.mpf(u.numerator) / u.denominator, a)
+                d = [abs(v - j) for j in range(16)]
+                best = min(range(16), key=lambda j: (d[j], -j))
+                assert q[r, c] == best, (r, c)
+
+
+@pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0])
+@pytest.mark.parametrize("m_bits", [0x3DCD, 0x3F80, 0x0100, 0x7F7F])
+def test_exhaustive_bf16_sweep_against_inverse_boundaries(alpha, m_bits):
+    """All non-negative bf16 a <= m: the code equals the count of real
+    boundaries ((2k-1)/30)^(1/alpha) that u = fl32(a/m) reaches."""
+    m = O.bf16_bits_to_f32(np.array([m_bits], np.uint16))[0]
+    a_bits = np.arange(0, m_bits + 1, dtype=np.uint16)
+    a = O.bf16_bits_to_f32(a_bits)
+    w = a[None, :].astype(np.float32)
+    q, _, mm = O.encode(w, alpha)
+    assert mm[0] == m
+    al = mpmath.mpf(O.alpha_f32(alpha))
+    with mpmath.workprec(120):
+        bounds = [mpmath.power(mpmath.mpf(2 * k - 1) / 30, 1 / al) for k in range(1, 16)]
+    bf = np.array([float(b) for b in bounds])
+    u32 = (a / m).astype(np.float32).astype(np.float64)
+    ref = np.zeros(a.shape, np.int64)
+    for k, b in enumerate(bf):
+        near = np.abs(u32 - b) <= 1e-12 * b
+        ref += (u32 >= b) & ~near
+        for i in np.nonzero(near)[0]:
+            uq = exact_quotient_f32(np.float32(a[i]), np.float32(m))
+            with mpmath.workprec(120):
+                ref[i] += int(mpmath.mpf(uq.numerator) / uq.denominator >= bounds[k])
+    # the float32 quotient used for the bulk compare is the exact one
+    for i in np.linspace(0, len(a) - 1, 97).astype(int):
+        assert Fraction(float(u32[i])) == exact_quotient_f32(np.float32(a[i]), np.float32(m))
+    assert np.array_equal(q[0].astype(np.int64), ref)
+
+
+@pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0])
+def test_fp32_near_threshold_sweep(alpha):
+    """Inputs within +-40 ulps of each decision point in |w|-space: the code
+    switches exactly where exact arithmetic on fl32(|w|/m) says."""
+    m = np.float32(0.0371)
+    al = mpmath.mpf(O.alpha_f32(alpha))
+    vals = []
+    for k in range(1, 16):
+        with mpmath.workprec(120):
+            b = mpmath.power(mpmath.mpf(2 * k - 1) / 30, 1 / al) * mpmath.mpf(float(m))
+        c = np.float32(float(b))
+        x = c
+        for _ in range(40):
+            x = np.nextafter(x, np.float32(0))
+        for _ in range(81):
+            if x <= m:
+                vals.append(x)
+            x = np.nextafter(x, np.float32(1))
+    w = np.array([list(vals) + [m]], np.float32)
+    q, _, mm = O.encode(w, alpha)
+    assert mm[0] == m
+    with mpmath.workprec(160):
+        for i, x in enumerate(vals):
+            u = exact_quotient_f32(x, m)
+            uu = mpmath.mpf(u.numerator) / u.denominator
+            ref = sum(1 for k in range(1, 16)
+                      if 15 * mpmath.power(uu, al) >= k - mpmath.mpf(0.5))
+            assert q[0, i] == ref, (k, i)
+
+
+def test_decision_thresholds_rational_cases():
+    """T_k for alpha = 1 and 1/2 are binary32 roundings up of rationals."""
+    def up(fr):
+        t = f32_of(fr)
+        if Fraction(float(t)) < fr:
+            t = np.nextafter(t, np.float32(2))
+        return t
+    t1 = O.decision_thresholds_f32(1.0)
+    t_half = O.decision_thresholds_f32(0.5)
+    for k in range(1, 16):
+        assert t1[k - 1] == up(Fraction(2 * k - 1, 30))
+        assert t_half[k - 1] == up(Fraction((2 * k - 1) ** 2, 900))
+    assert t1[7] == np.float32(0.5)
+
+
+@pytest.mark.parametrize("alpha", [0.45, 0.73])
+def test_encode_equals_threshold_count(alpha):
+    w = _rand_rows(7, 16, 256)
+    q, _, m = O.encode(w, alpha)
+    u = (np.abs(w) / m[:, None]).astype(np.float32)
+    t = O.decision_thresholds_f32(alpha)
+    cnt = (u[:, :, None] >= t[None, None, :]).sum(axis=2)
+    assert np.array_equal(q, cnt)
+
+
+# ------------------------------------------------------------------ packing
+
+def _golden_words():
+    out = {}
+    with open(os.path.join(GOLDEN, "packing_example.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if line:
+                key, words = line.split(":")
+                out[key.strip()] = [int(x, 16) for x in words.split()]
+    return out
+
+
+def test_packing_worked_example():
+    g = _golden_words()
+    k = np.arange(64)
+    q = (k % 16).astype(np.uint8)[None, :]
+    s = (k % 2).astype(np.uint8)[None, :]
+    packed, sign = O.pack(q, s)
+    assert list(packed[0]) == g["codes_k_mod_16"]
+    assert list(sign[0]) == g["signs_odd_negative"]
+    q2 = np.zeros((1, 64), np.uint8)
+    q2[0, 37] = 0xB
+    p2, _ = O.pack(q2, np.zeros_like(q2))
+    assert list(p2[0]) == g["single_code_at_37"]
+
+
+def test_pack_unpack_roundtrip():
+    rng = np.random.default_rng(8)
+    q = rng.integers(0, 16, (5, 96)).astype(np.uint8)
+    s = rng.integers(0, 2, (5, 96)).astype(np.uint8)
+    p, sg = O.pack(q, s)
+    q2, s2 = O.unpack(p, sg)
+    assert np.array_equal(q, q2) and np.array_equal(s, s2)
+
+
+# ------------------------------------------------------------------ dequant
+
+@pytest.mark.parametrize("alpha,level", [
+    (1.0, lambda q: Fraction(q, 15)),
+    (0.5, lambda q: Fraction(q, 15) ** 2),
+    (0.25, lambda q: Fraction(q, 15) ** 4),
+])
+def test_dequant_exact_rational(alpha, level):
+    """For alpha = 1, 1/2, 1/4 the level (q/15)^(1/alpha) is rational: the
+    bf16 reconstruction must be the exactly rounded value, bit for bit."""
+    w = _to_bf16_values(_rand_rows(9, 8, 64))
+    packed, sign, m = O.quantize(w, alpha)
+    got = O.dequantize(packed, sign, m, alpha)
+    q, s = O.unpack(packed, sign)
+    for r in range(w.shape[0]):
+        for c in range(w.shape[1]):
+            v = level(int(q[r, c])) * Fraction(float(m[r]))
+            if s[r, c] and q[r, c]:
+                v = -v
+            assert got[r, c] == bf16_bits_of(v), (r, c)
+
+
+def test_dequant_rounds_once_near_midpoints():
+    """Cases where the reconstruction lies just above a bf16 midpoint, within
+    half a binary32 ulp: rounding through binary32 first would land on the
+    midpoint and tie to even (down); rounding once goes up."""
+    rng = np.random.default_rng(16)
+    m = (1 + rng.random(1 << 20)).astype(np.float32)
+    qs, ms = [], []
+    for q in range(1, 15):
+        v = q * m.astype(np.float64) / 15
+        v32 = v.astype(np.float32)
+        b = v32.view(np.uint32)
+        hit = ((b & 0xFFFF) == 0x8000) & (v > v32) & (((b >> 16) & 1) == 0)
+        qs += [q] * int(hit.sum())
+        ms += list(m[hit])
+    assert len(qs) >= 8
+    n = len(qs)
+    k = 32
+    qq = np.zeros((n, k), np.uint8)
+    qq[:, 0] = qs
+    packed, sign = O.pack(qq, np.zeros_like(qq))
+    scale = np.array(ms, np.float32)
+    d = O.dequantize(packed, sign, scale, 1.0)
+    for i in range(n):
+        exact = Fraction(int(qs[i]), 15) * Fraction(float(scale[i]))
+        assert d[i, 0] == bf16_bits_of(exact), i
+
+
+def test_dequant_special_values():
+    w = _to_bf16_values(_rand_rows(10, 4, 64))
+    w[2, 5] = -0.0
+    w[3, :] = 0
+    packed, sign, m = O.quantize(w, 0.73)
+    d = O.dequantize(packed, sign, m, 0.73)
+    q, s = O.unpack(packed, sign)
+    mbits = (m.view(np.uint32) >> 16).astype(np.uint16)
+    for r in range(4):
+        top = q[r] == 15
+        assert np.all((d[r][top] & 0x7FFF) == mbits[r])      # max reconstructs exactly
+    assert np.all(d[q == 0] == 0)                              # +0.0, never -0.0
+    assert not d[3].any()
+
+
+@pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0])
+def test_quantize_dequantize_idempotent(alpha):
+    w = _to_bf16_values(_rand_rows(11, 32, 512))
+    p1, s1, m1 = O.quantize(w, alpha)
+    d1 = O.dequantize(p1, s1, m1, alpha)
+    w2 = O.bf16_bits_to_f32(d1)
+    p2, s2, m2 = O.quantize(w2, alpha)
+    d2 = O.dequantize(p2, s2, m2, alpha)
+    assert np.array_equal(p1, p2)                  # codes unchanged
+    assert np.array_equal(m1, m2)                  # the max is itself a level
+    assert np.array_equal(d1, d2)
+
+
+def test_reconstruction_error_bound():
+    """|w - w'| <= half the gap to the neighbouring level plus a bf16 ulp
+    (the quantizer is a nearest-level rule in v-space, so in w-space the
+    error is bounded by the largest level gap)."""
+    alpha = 0.73
+    w = _to_bf16_values(_rand_rows(12, 8, 256))
+    p, s, m = O.quantize(w, alpha)
+    d = O.bf16_bits_to_f32(O.dequantize(p, s, m, alpha)).astype(np.float64)
+    levels = (np.arange(16) / 15.0) ** (1 / O.alpha_f32(alpha))
+    gap = np.max(np.diff(levels))
+    err = np.abs(w.astype(np.float64) - d) / m[:, None]
+    assert np.all(err <= gap + 2 ** -7)
+
+
+# ------------------------------------------------------------------ linear
+
+def test_linear_one_hot_rows_pick_columns():
+    w = _to_bf16_values(_rand_rows(13, 24, 64))
+    p, s, m = O.quantize(w, 0.73)
+    wd = O.dequantize(p, s, m, 0.73)
+    x = np.zeros((64, 64), np.float32)
+    x[np.arange(64), np.arange(64)] = 1.0
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    y = O.linear(xb, wd)
+    assert np.array_equal(y.T.astype(np.float32), O.bf16_bits_to_f32(wd))
+
+
+def test_linear_exact_small():
+    rng = np.random.default_rng(14)
+    x = _to_bf16_values(rng.standard_normal((3, 32)).astype(np.float32))
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    w = _to_bf16_values(_rand_rows(15, 5, 32))
+    p, s, m = O.quantize(w, 0.73)
+    wd = O.dequantize(p, s, m, 0.73)
+    wv = O.bf16_bits_to_f32(wd)
+    bias = np.array([0.5, -1, 0, 2, 0.25], np.float32)
+    y = O.linear(xb, wd, bias)
+    for i in range(3):
+        for j in range(5):
+            ex = sum(Fraction(float(x[i, k])) * Fraction(float(wv[j, k])) for k in range(32))
+            ex += Fraction(float(bias[j]))
+            assert abs(Fraction(float(y[i, j])) - ex) <= Fraction(1, 2 ** 40)
+
+
+# ------------------------------------------------------------------ SNR
+
+def test_snr_closed_form():
+    m = 0.8
+    w = np.zeros((1, 32), np.float32)
+    w[0, 0], w[0, 1] = m, m / 2                 # u = 1/2 exactly: q = round(7.5) = 8
+    p, s, mm = O.quantize(w, 1.0)
+    d = O.bf16_bits_to_f32(O.dequantize(p, s, mm, 1.0))
+    mf = Fraction(float(np.float32(m)))
+    assert d[0, 0] == float(round_fraction(mf, 8))
+    assert d[0, 1] == float(round_fraction(Fraction(8, 15) * mf, 8))
+    assert not d[0, 2:].any()
+    snr = O.snr_db(w, d)
+    e = w.astype(np.float64) - d.astype(np.float64)
+    assert math.isclose(snr, 10 * math.log10(np.sum(w.astype(np.float64) ** 2) / np.sum(e ** 2)))
+    assert O.snr_db(d, d) == math.inf
