@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Benchmark of the OPQ W4A16 hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+    opq_quantize(W bf16) -> opq_dequantize -> opq_linear(x, stored W)
+on the skinny DiT-shaped workload (W 3840x3840 Student-t(4) std 0.02,
+x bf16 [32, 3840], alpha 0.73) unless --workload names another.
+
+Prints ONE JSON line.  `value` is the step's fraction of the MI355X roofline
+in percent: the sum of each kernel's ideal time (algorithmic bytes / 8 TB/s,
+or flops / 2.5 PFLOP/s for MFMA-bound shapes) over the measured step time.
+Per-kernel absolute GB/s and TFLOP/s are under "kernels".  Inputs are
+resident in HBM before timing starts; every step rotates to another set of
+input/output buffers so that the 256 MB Infinity Cache cannot serve repeats.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "opq_linear TFLOP/s + quantize/dequant GB/s, as % of MI355X roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+SKINNY_MAX_M = 64              # opq_linear switches to the tiled MFMA kernel above this
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "w4a16_linear_amd", "csrc")
+KERNEL_SOURCE = {"quantize": "quantize.hip", "dequantize": "dequantize.hip",
+                 "linear": "linear.hip"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="skinny", choices=["skinny", "qkv", "ffn_up", "ffn_down", "tiny"])
+    ap.add_argument("--alpha", type=float, default=0.73)
+    ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for > 768 MB)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ workload
+
+def workload(name):
+    from w4a16_linear_amd import workloads as WL
+    if name == "skinny":
+        L = WL.config("skinny").layers[0]
+    elif name == "qkv":
+        L = WL.config("qkv").layers[0]
+    elif name == "ffn_up":
+        L = WL.config("ffn").layers[0]
+    elif name == "ffn_down":
+        L = WL.config("ffn").layers[1]
+    else:
+        L = WL.config("tiny").layers[0]
+    return L
+
+
+def algorithmic(m, n, k, w_bytes):
+    """Per-launch algorithmic bytes / flops (what the method must move)."""
+    quant = {"bytes": n * k * (w_bytes + 0.625) + 4 * n, "flops": 0}
+    dequant = {"bytes": n * k * (0.625 + 2) + 4 * n, "flops": 0}
+    lin = {"bytes": 0.625 * n * k + 4 * n + 2 * m * k + 4 * m * n, "flops": 2 * m * n * k}
+    return {"quantize": quant, "dequantize": dequant, "linear": lin}
+
+
+def ideal_us(kind, alg, m):
+    if kind == "linear" and m > SKINNY_MAX_M:
+        return alg["flops"] / (BF16_PEAK_TFLOPS * 1e12) * 1e6, "mfma"
+    return alg["bytes"] / (HBM_PEAK_GBS * 1e9) * 1e6, "hbm"
+
+
+def source_hash(kind):
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCE[kind], "device_common.hpp"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind, workload_name):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kind}_{workload_name}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            key, v = line.split(":", 1)
+            vals[key.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_hash(kind):
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(L, x_bits, w_vals, alpha, seconds, ideal_total_us):
+    """The oracle, as it stands, over the whole workload, repeated until
+    `seconds` have passed (at least once); BLAS limited to one thread."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=1)
+    except Exception:  # pragma: no cover
+        limiter = None
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        p, s, m = O.quantize(w_vals, alpha)
+        d = O.dequantize(p, s, m, alpha)
+        O.linear(x_bits, d)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 20:
+            break
+    if limiter is not None:
+        limiter.unregister() if hasattr(limiter, "unregister") else None
+    per_step = el / reps
+    return {
+        "value": round(100.0 * ideal_total_us * 1e-6 / per_step, 6),
+        "unit": "% of MI355X roofline",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": f"{reps} full oracle step(s) (quantize, dequantize, linear) on the whole "
+                  f"{L.n}x{L.k} weight and x[{L.m},{L.k}], {el:.1f} s total, "
+                  f"{per_step * 1e3:.1f} ms per step",
+        "ms_per_step": round(per_step * 1e3, 3),
+        "host_cpu": platform.processor() or platform.machine(),
+        "host_threads_available": os.cpu_count(),
+    }
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the OPQ hot path here has no multi-GPU "
+              "path (rows shard without exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from w4a16_linear_amd import opq
+    from w4a16_linear_amd import workloads as WL
+
+    opq.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = workload(args.workload)
+    m, n, k = L.m, L.n, L.k
+    alpha = args.alpha
+
+    w32 = L.make_w()
+    if L.w_dtype == "bf16":
+        w_host = WL.to_bf16(w32)
+        w_vals = None
+        w_bytes = 2
+    else:
+        w_host = torch.from_numpy(w32)
+        w_bytes = 4
+    x_host = WL.to_bf16(L.make_x())
+
+    alg = algorithmic(m, n, k, w_bytes)
+    per_set = (n * k * w_bytes + n * k * 0.625 + 4 * n + n * k * 2 + m * k * 2 + m * n * 4)
+    rot = args.rotate or max(2, int(np.ceil(800e6 / per_set)))
+    sets = []
+    for _ in range(rot):
+        w = w_host.to(dev)
+        qw = opq.QuantizedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
+                                 torch.empty((n, k // 32), dtype=torch.int32, device=dev),
+                                 torch.empty((n,), dtype=torch.float32, device=dev))
+        d = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+        x = x_host.to(dev)
+        y = torch.empty((m, n), dtype=torch.float32, device=dev)
+        sets.append((w, qw, d, x, y))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i, ev=None):
+        w, qw, d, x, y = sets[i % rot]
+        if ev is not None:
+            ev[0].record(stream)
+        opq.quantize(w, alpha, out=qw)
+        if ev is not None:
+            ev[1].record(stream)
+        opq.dequantize(qw, alpha, out=d)
+        if ev is not None:
+            ev[2].record(stream)
+        opq.linear(x, qw, alpha, out=y)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i, events[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+
+    kinds = ["quantize", "dequantize", "linear"]
+    kern = {}
+    ideal_total = 0.0
+    for j, kind in enumerate(kinds):
+        us = float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events])) * 1e3
+        ideal, bound = ideal_us(kind, alg[kind], m)
+        ideal_total += ideal
+        a = alg[kind]
+        rec = {"us": round(us, 3), "bound": bound, "ideal_us": round(ideal, 3),
+               "frac": round(ideal / us, 4),
+               "GBps": round(a["bytes"] / (us * 1e-6) / 1e9, 1),
+               "algorithmic_bytes": int(a["bytes"])}
+        if a["flops"]:
+            rec["TFLOPs"] = round(a["flops"] / (us * 1e-6) / 1e12, 2)
+        kern[kind] = rec
+
+    dom = max(kinds, key=lambda kk: kern[kk]["us"])
+    dk = kern[dom]
+    if dk["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": dk["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(dk["TFLOPs"] / BF16_PEAK_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4)}
+    roof["kernel"] = dom
+    roof["traffic"] = measured_traffic(dom, args.workload)
+
+    value = 100.0 * (ideal_total * 1e-3) / ms_step
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "% of MI355X roofline",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {WL_title(args.workload)}", "m": m, "n": n,
+                   "k": k, "w_dtype": L.w_dtype, "alpha": alpha, "rotating_sets": rot,
+                   "step": "quantize -> dequantize -> linear"},
+        "roofline": roof,
+        "kernels": kern,
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        import oracle as O
+        xb = WL.bf16_bits(x_host)
+        wv = (O.bf16_bits_to_f32(WL.bf16_bits(w_host)) if L.w_dtype == "bf16"
+              else w_host.numpy())
+        out["cpu_baseline"] = cpu_baseline(L, xb, wv, alpha, args.cpu_seconds, ideal_total)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def WL_title(name):
+    from w4a16_linear_amd import workloads as WL
+    return {"skinny": WL.config("skinny").title, "qkv": WL.config("qkv").title,
+            "ffn_up": "FFN up/gate: x bf16 [4096, 3840] x W 20480x3840",
+            "ffn_down": "FFN down: x bf16 [4096, 10240] x W 3840x10240",
+            "tiny": WL.config("tiny").title}[name]
+
+
+if __name__ == "__main__":
+    main()

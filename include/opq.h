@@ -1,0 +1,150 @@
+/*
+ * libopq: OPQ (Optimal Power Quantization) 4-bit weights for AMD MI355X (gfx950).
+ *
+ * The method is the one on the model card "OPQ INT4 Z-Image"
+ * (huggingpeers.co/models/dfytensor/OPQ-INT4-Z-Image):
+ *   section "OPQ 原理"            u = |w| / max|w|,  v = u^alpha,  q = round(15 v),
+ *                                  w' = sign(w) (q/15)^(1/alpha) max|w|;
+ *   section "技术细节 / 存储格式"  4-bit magnitudes eight per uint32, a 1-bit sign
+ *                                  plane thirty-two per uint32, one max per group;
+ *   section "技术细节 / 推理解码"  decode q/15 -> ^(1/alpha) -> x sign x max;
+ *   file list "opq_quantize.py (OPQLinear + replace_with_opq)": a linear layer
+ *                                  that runs on the stored form.
+ *
+ * Format used by every call (the card leaves these open):
+ *   - one max per output row n, stored as float32 scale[n];
+ *   - packed[n][k/8] (uint32): code of (n, k) in bits 4*(k%8) .. 4*(k%8)+3;
+ *   - sign[n][k/32]  (uint32): bit k%32 is 1 exactly when w[n][k] < 0;
+ *   - codes are exact: q = the integer nearest to 15 * u^alpha with
+ *     u = |w| / max|w| the IEEE binary32 quotient (round to nearest even,
+ *     subnormals kept); an exact half (only alpha = 1, u = 1/2) rounds up;
+ *   - a row whose max is 0 gets scale 0, codes 0 and signs 0;
+ *   - bfloat16 values travel as uint16 bit patterns;
+ *   - the magnitude is 4 bits and the sign a separate bit, so a weight takes
+ *     one of 31 values although the card calls the format "INT4".
+ *
+ * Conventions for every call:
+ *   - matrices are row-major and dense (row stride = number of columns);
+ *   - device pointers are memory of the current HIP device; host pointers are
+ *     marked as such;
+ *   - the caller owns every buffer; the library allocates nothing, frees
+ *     nothing, synchronises nothing and keeps no mutable global state, so
+ *     calls are reentrant; outputs must not overlap inputs;
+ *   - `stream` is a hipStream_t (NULL = the default stream); work is enqueued
+ *     on it and the call returns at once; faults inside kernels show up at the
+ *     caller's next synchronisation;
+ *   - a pointer may be NULL exactly when the array it points to has no
+ *     elements (for example packed and sign when k == 0);
+ *   - arguments are checked before anything is enqueued, in this order:
+ *     null pointers (OPQ_ERR_NULL), shapes (OPQ_ERR_SHAPE), alpha
+ *     (OPQ_ERR_ALPHA), 16-byte alignment of every array (OPQ_ERR_ALIGN),
+ *     dtype codes (OPQ_ERR_DTYPE); with an error nothing is enqueued;
+ *   - n == 0 or m == 0 is a valid empty call (OPQ_OK, nothing enqueued);
+ *   - k must be a multiple of 32 (one sign word); n, m are free;
+ *   - alpha must be finite and > 0, and every call on one set of weights must
+ *     get the same binary32 alpha (the stored form does not record it);
+ *   - weights must be finite; with NaN or Inf the codes are unspecified.
+ */
+#ifndef OPQ_H
+#define OPQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OPQ_ABI_VERSION 1
+
+typedef enum {
+  OPQ_OK = 0,
+  OPQ_ERR_NULL = 1,        /* a required pointer is NULL */
+  OPQ_ERR_SHAPE = 2,       /* negative size, or k not a multiple of 32 */
+  OPQ_ERR_ALPHA = 3,       /* alpha not finite or not > 0 */
+  OPQ_ERR_ALIGN = 4,       /* an array is not 16-byte aligned */
+  OPQ_ERR_DTYPE = 5,       /* unknown dtype code */
+  OPQ_ERR_WORKSPACE = 6,   /* workspace smaller than opq_linear_workspace_bytes() */
+  OPQ_ERR_UNSUPPORTED = 7, /* a size beyond what the kernels handle */
+  OPQ_ERR_HIP = 8          /* the HIP runtime refused a launch */
+} opq_status;
+
+typedef enum { OPQ_F32 = 0, OPQ_BF16 = 1 } opq_dtype;
+
+/* ABI version of the loaded library (OPQ_ABI_VERSION). */
+int opq_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* opq_status_str(int status);
+
+/*
+ * Decision points of the quantizer ("OPQ 原理": q = round(15 u^alpha)).
+ * Host only, no GPU needed.  out_t (host, 15 floats) receives T_k, k = 1..15:
+ * the smallest binary32 t with 15 t^alpha >= k - 1/2.  For binary32 u in
+ * [0, 1] the code is the number of k with u >= T_k.  These are the values the
+ * quantize kernel compares against.
+ * Errors: OPQ_ERR_NULL, OPQ_ERR_ALPHA.
+ */
+int opq_decision_points(float alpha, float* out_t);
+
+/*
+ * Reconstruction levels ("推理解码": (q/15)^(1/alpha)).  Host only.
+ * out_g (host, 16 doubles) receives G_q = (q/15)^(1/alpha) in double, q = 0..15;
+ * G_0 = 0 and G_15 = 1 exactly.  A row with scale m reconstructs code q as the
+ * bfloat16 nearest to G_q * m (one rounding); dequantize and linear both use it.
+ * Errors: OPQ_ERR_NULL, OPQ_ERR_ALPHA.
+ */
+int opq_levels(float alpha, double* out_g);
+
+/*
+ * Quantize ("OPQ 原理", "存储格式").
+ *   w       device, [n][k] of float32 (w_dtype OPQ_F32) or bfloat16 (OPQ_BF16)
+ *   packed  device out, [n][k/8] uint32 magnitudes
+ *   sign    device out, [n][k/32] uint32 sign plane
+ *   scale   device out, [n] float32 = max_k |w[n][k]| (exact)
+ * k <= 65536.  Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA,
+ * OPQ_ERR_ALIGN, OPQ_ERR_DTYPE, OPQ_ERR_UNSUPPORTED, OPQ_ERR_HIP.
+ */
+int opq_quantize(const void* w, int w_dtype, int64_t n, int64_t k, float alpha,
+                 uint32_t* packed, uint32_t* sign, float* scale, void* stream);
+
+/*
+ * Dequantize ("推理解码").
+ *   packed, sign, scale  device, as written by opq_quantize
+ *   w_out   device out, [n][k] bfloat16: bf16(G_q * scale[n]) with the sign
+ *           applied; code 0 gives +0.0
+ * Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN, OPQ_ERR_HIP.
+ */
+int opq_dequantize(const uint32_t* packed, const uint32_t* sign, const float* scale,
+                   int64_t n, int64_t k, float alpha, uint16_t* w_out, void* stream);
+
+/*
+ * Bytes of device workspace opq_linear needs for this shape (0 means none;
+ * the workspace pointer may then be NULL).
+ */
+size_t opq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
+
+/*
+ * W4A16 linear layer on the stored form (the card's OPQLinear):
+ *   y[m][n] = sum_k x[m][k] * W'[n][k] (+ bias[n])
+ * with W'[n][k] = the bfloat16 reconstruction that opq_dequantize writes,
+ * made on chip, and float32 accumulation.
+ *   x       device, [m][k] bfloat16 activations
+ *   packed, sign, scale  device, as written by opq_quantize for W[n][k]
+ *   bias    device, [n] float32, or NULL for none
+ *   y       device out, [m][n] float32
+ *   workspace, workspace_bytes  device scratch of at least
+ *           opq_linear_workspace_bytes(m, n, k) bytes (NULL when that is 0)
+ * Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN,
+ * OPQ_ERR_WORKSPACE, OPQ_ERR_HIP.
+ */
+int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
+               const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
+               float alpha, float* y, void* workspace, size_t workspace_bytes,
+               void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OPQ_H */

@@ -1,0 +1,136 @@
+"""CPU tests of the C-ABI library: it loads, exports every declared symbol,
+and its host-only parts (tables, argument checks, empty calls) behave as
+include/opq.h states.  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import mpmath
+import numpy as np
+import pytest
+
+import oracle as O
+from w4a16_linear_amd import opq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "opq.h")
+
+OK, NULL, SHAPE, ALPHA, ALIGN, DTYPE, WORKSPACE, UNSUPPORTED, HIP = range(9)
+FAKE = 0x7F0000000000          # an aligned, never dereferenced address
+MISALIGNED = FAKE + 4
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return opq.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(opq_\w+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) == 8
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(opq._SIGNATURES)
+
+
+def test_abi_version_and_status_text(lib):
+    assert lib.opq_abi_version() == 1
+    for s in range(9):
+        assert opq.status_str(s) and opq.status_str(s) != "unknown status"
+    assert opq.status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0, 0.5, 0.25, 2.0, 0.3, 3.7, 0.05, 10.0, 0.999])
+def test_decision_points_equal_oracle(alpha):
+    """The library's binary128 search and the oracle's mpmath search agree."""
+    got = opq.decision_points(alpha)
+    ref = O.decision_thresholds_f32(alpha)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0, 2.5])
+def test_levels(alpha):
+    g = opq.levels(alpha)
+    assert g[0] == 0.0 and g[15] == 1.0
+    a = mpmath.mpf(O.alpha_f32(alpha))
+    with mpmath.workprec(120):
+        for q in range(1, 15):
+            ex = mpmath.power(mpmath.mpf(q) / 15, 1 / a)
+            assert abs(g[q] - float(ex)) <= np.spacing(float(ex))  # rounded from binary128
+
+
+def test_table_argument_errors(lib):
+    buf = np.zeros(16, np.float64)
+    assert lib.opq_decision_points(0.73, None) == NULL
+    assert lib.opq_levels(0.73, None) == NULL
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        assert lib.opq_decision_points(bad, buf.ctypes.data) == ALPHA
+        assert lib.opq_levels(bad, buf.ctypes.data) == ALPHA
+
+
+def test_quantize_argument_checks(lib):
+    q = lib.opq_quantize
+    assert q(None, 1, 4, 64, 0.73, FAKE, FAKE, FAKE, None) == NULL
+    assert q(FAKE, 1, 4, 64, 0.73, FAKE, None, FAKE, None) == NULL
+    assert q(None, 1, 4, 63, 0.0, FAKE, FAKE, FAKE, None) == NULL      # null first
+    assert q(FAKE, 1, 4, 48, 0.73, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, 1, -1, 64, 0.73, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, 1, 4, -32, 0.73, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, 1, 4, 48, -1.0, FAKE, FAKE, FAKE, None) == SHAPE     # shape before alpha
+    for bad in (0.0, -0.5, float("nan"), float("inf")):
+        assert q(FAKE, 1, 4, 64, bad, FAKE, FAKE, FAKE, None) == ALPHA
+    assert q(FAKE, 1, 4, 64, 0.0, MISALIGNED, FAKE, FAKE, None) == ALPHA
+    assert q(MISALIGNED, 1, 4, 64, 0.73, FAKE, FAKE, FAKE, None) == ALIGN
+    assert q(FAKE, 1, 4, 64, 0.73, FAKE, MISALIGNED, FAKE, None) == ALIGN
+    assert q(FAKE, 1, 4, 64, 0.73, FAKE, FAKE, MISALIGNED, None) == ALIGN
+    assert q(FAKE, 7, 4, 64, 0.73, MISALIGNED, FAKE, FAKE, None) == ALIGN
+    assert q(FAKE, 7, 4, 64, 0.73, FAKE, FAKE, FAKE, None) == DTYPE
+    assert q(FAKE, 1, 4, 65536 + 32, 0.73, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert q(FAKE, 1, 0, 64, 0.73, FAKE, FAKE, FAKE, None) == OK         # empty: nothing enqueued
+
+
+def test_dequantize_argument_checks(lib):
+    d = lib.opq_dequantize
+    assert d(FAKE, None, FAKE, 4, 64, 0.73, FAKE, None) == NULL
+    assert d(FAKE, FAKE, FAKE, 4, 40, 0.73, FAKE, None) == SHAPE
+    assert d(FAKE, FAKE, FAKE, 4, 64, float("nan"), FAKE, None) == ALPHA
+    assert d(FAKE, FAKE, FAKE, 4, 64, 0.73, MISALIGNED, None) == ALIGN
+    assert d(FAKE, FAKE, FAKE, 0, 64, 0.73, FAKE, None) == OK
+    assert d(FAKE, FAKE, FAKE, 4, 0, 0.73, FAKE, None) == OK
+
+
+def test_linear_argument_checks(lib):
+    f = lib.opq_linear
+    args = dict(x=FAKE, p=FAKE, s=FAKE, sc=FAKE, b=None, m=8, n=16, k=64, a=0.73, y=FAKE,
+                ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["x"], a["p"], a["s"], a["sc"], a["b"], a["m"], a["n"], a["k"], a["a"], a["y"],
+                 a["ws"], a["wsb"], None)
+
+    assert call(x=None) == NULL
+    assert call(y=None) == NULL
+    assert call(k=33) == SHAPE
+    assert call(m=-1) == SHAPE
+    assert call(a=0.0) == ALPHA
+    assert call(b=MISALIGNED) == ALIGN
+    assert call(x=MISALIGNED) == ALIGN
+    assert call(ws=MISALIGNED) == ALIGN
+    assert call(m=0) == OK
+    assert call(n=0) == OK
+    assert lib.opq_linear_workspace_bytes(8, 16, 64) == opq.linear_workspace_bytes(8, 16, 64)
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        opq.quantize(torch.zeros(4, 64), 0.73)
+    with pytest.raises(ValueError):
+        opq.quantize(torch.zeros(4, 64, dtype=torch.float16), 0.73)

@@ -1,0 +1,313 @@
+"""GPU parity: libopq's HIP kernels against the CPU oracle, through the C ABI.
+
+Bars (same inputs, element by element):
+  * packed codes, sign words and scales bit-exact;
+  * dequantized bfloat16 within 1 ulp (ordered patterns, so -0 and +0 agree),
+    and +0.0 for every zero code;
+  * linear output max|y - y_ref| <= 1e-2 * rms(y_ref), y_ref the float64 product
+    over the oracle's bfloat16 reconstructions.
+
+Every output buffer is a view into a larger pattern-filled allocation; the
+margins are checked after each call to catch stray writes.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from w4a16_linear_amd import workloads as WL
+from w4a16_linear_amd.workloads import bf16_bits, to_bf16, u32
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+MARGIN = 256  # bytes of guard band on each side (keeps 16-byte alignment)
+LINEAR_TOL = 1e-2
+
+
+# ------------------------------------------------------------------ helpers
+
+class Guarded:
+    """A tensor view with pattern-filled guard bands before and after it."""
+
+    def __init__(self, shape, dtype):
+        self.shape = tuple(shape)
+        esz = torch.tensor([], dtype=dtype).element_size()
+        self.pad = MARGIN // esz
+        numel = int(np.prod(self.shape)) if self.shape else 1
+        self.base = torch.empty(numel + 2 * self.pad, dtype=torch.uint8 if esz == 1 else dtype,
+                                device=DEV)
+        self.base.view(torch.uint8).fill_(0xA5)
+        self.t = self.base[self.pad:self.pad + numel].view(self.shape)
+
+    def check(self):
+        raw = self.base.view(torch.uint8).cpu().numpy()
+        nb = self.pad * self.base.element_size()
+        assert np.all(raw[:nb] == 0xA5), "write before the buffer"
+        assert np.all(raw[len(raw) - nb:] == 0xA5), "write after the buffer"
+
+
+def quantize_guarded(opq, w_dev, alpha):
+    n, k = w_dev.shape
+    gp = Guarded((n, k // 8), torch.int32)
+    gs = Guarded((n, k // 32), torch.int32)
+    gm = Guarded((n,), torch.float32)
+    qw = opq.QuantizedWeight(gp.t, gs.t, gm.t)
+    opq.quantize(w_dev, alpha, out=qw)
+    torch.cuda.synchronize()
+    for g in (gp, gs, gm):
+        g.check()
+    return qw
+
+
+def dequantize_guarded(opq, qw, alpha):
+    n, k = qw.shape
+    g = Guarded((n, k), torch.bfloat16)
+    opq.dequantize(qw, alpha, out=g.t)
+    torch.cuda.synchronize()
+    g.check()
+    return g.t
+
+
+def ordered(bits):
+    b = bits.astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def assert_quant_equal(qw, ref, rows=None):
+    p_ref, s_ref, m_ref = ref
+    sel = slice(None) if rows is None else rows
+    p = u32(qw.packed)[sel]
+    s = u32(qw.sign)[sel]
+    m = qw.scale.cpu().numpy()[sel]
+    assert np.array_equal(m.view(np.uint32), m_ref.view(np.uint32)), "scale"
+    bad = np.argwhere(p != p_ref)
+    assert bad.size == 0, f"packed differs at {bad[:5].tolist()} of {bad.shape[0]}"
+    bad = np.argwhere(s != s_ref)
+    assert bad.size == 0, f"sign differs at {bad[:5].tolist()} of {bad.shape[0]}"
+
+
+def assert_dequant_close(d_bits, ref_bits, q_ref):
+    dist = np.abs(ordered(d_bits) - ordered(ref_bits))
+    assert dist.max(initial=0) <= 1, f"max ulp distance {dist.max()}"
+    zero = q_ref == 0
+    assert np.all(d_bits[zero] == 0), "code 0 must give +0.0"
+    return float(np.mean(dist == 0)) if dist.size else 1.0
+
+
+def assert_linear_close(y, y_ref):
+    rms = math.sqrt(float(np.mean(y_ref * y_ref))) if y_ref.size else 0.0
+    err = float(np.max(np.abs(y.astype(np.float64) - y_ref))) if y_ref.size else 0.0
+    assert err <= LINEAR_TOL * rms + 1e-30, f"max err {err:.3e} > {LINEAR_TOL} * rms {rms:.3e}"
+    return err / rms if rms else 0.0
+
+
+def weight_tensor(w32, dtype):
+    """Host float32 values -> (exact float32 values of the stored dtype, device tensor)."""
+    if dtype == "bf16":
+        t = to_bf16(w32)
+        return O.bf16_bits_to_f32(bf16_bits(t)), t.to(DEV)
+    return np.ascontiguousarray(w32, np.float32), torch.from_numpy(np.ascontiguousarray(w32)).to(DEV)
+
+
+def full_roundtrip(opq, w_vals, w_dev, alpha):
+    """Quantize + dequantize on the GPU and in the oracle; compare everything."""
+    qw = quantize_guarded(opq, w_dev, alpha)
+    ref = O.quantize(w_vals, alpha)
+    assert_quant_equal(qw, ref)
+    d = dequantize_guarded(opq, qw, alpha)
+    d_ref = O.dequantize(*ref, alpha)
+    q_ref, _ = O.unpack(ref[0], ref[1])
+    assert_dequant_close(bf16_bits(d), d_ref, q_ref)
+    return qw, ref, d_ref
+
+
+# ------------------------------------------------------------------ tiny config (whole path)
+
+def test_tiny_config_whole_path(gpu_lib):
+    opq = gpu_lib
+    cfg = WL.config("tiny")
+    L = cfg.layers[0]
+    w_vals, w_dev = weight_tensor(L.make_w(), L.w_dtype)
+    qw, ref, d_ref = full_roundtrip(opq, w_vals, w_dev, WL.ALPHA)
+    xt = to_bf16(L.make_x())
+    gy = Guarded((L.m, L.n), torch.float32)
+    opq.linear(xt.to(DEV), qw, WL.ALPHA, out=gy.t)
+    torch.cuda.synchronize()
+    gy.check()
+    y_ref = O.linear(bf16_bits(xt), d_ref)
+    assert_linear_close(gy.t.cpu().numpy(), y_ref)
+
+
+# ------------------------------------------------------------------ quantize / dequantize edge cases
+
+SHAPES = [(1, 32), (5, 96), (7, 544), (33, 3840), (3, 10240), (2, 16384), (2, 16416), (3, 20480)]
+
+
+@pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0])
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_quantize_bf16_shapes(gpu_lib, n, k, alpha):
+    w = WL.student_t(100 + n + k, (n, k))
+    w_vals, w_dev = weight_tensor(w, "bf16")
+    full_roundtrip(gpu_lib, w_vals, w_dev, alpha)
+
+
+@pytest.mark.parametrize("n,k", [(3, 256), (4, 4096), (2, 8192), (2, 8224), (3, 12288)])
+def test_quantize_fp32_shapes(gpu_lib, n, k):
+    w = WL.normal(200 + k, (n, k), 0.02)
+    w_vals, w_dev = weight_tensor(w, "f32")
+    full_roundtrip(gpu_lib, w_vals, w_dev, 0.73)
+
+
+def _special_rows(k, dtype):
+    rng = np.random.default_rng(7)
+    rows = []
+    rows.append(np.zeros(k, np.float32))                                    # all zero
+    r = np.zeros(k, np.float32); r[::3] = -0.0; rows.append(r)              # signed zeros
+    r = (rng.standard_normal(k) * 0.02).astype(np.float32); r[k // 2] = -1.5; rows.append(r)
+    rows.append((rng.standard_normal(k) * 1e-39).astype(np.float32))        # subnormal scale
+    rows.append((rng.standard_normal(k) * 1e37).astype(np.float32))         # huge scale
+    rows.append(np.full(k, -0.25, np.float32))                              # constant magnitude
+    r = np.zeros(k, np.float32); r[5] = 3.0; r[6] = -1e-30; rows.append(r)  # tiny negative
+    rows.append(np.linspace(-1, 1, k).astype(np.float32))
+    r = (rng.standard_normal(k) * 0.02).astype(np.float32); r[r < 0] = -0.0; rows.append(r)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("alpha", [0.1, 0.45, 0.73, 1.0, 2.0, 5.0])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_special_rows(gpu_lib, dtype, alpha):
+    w = _special_rows(544, dtype)
+    w_vals, w_dev = weight_tensor(w, dtype)
+    full_roundtrip(gpu_lib, w_vals, w_dev, alpha)
+
+
+@pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0])
+def test_quantize_near_decision_points(gpu_lib, alpha):
+    """Magnitudes within a few binary32 ulps of every row boundary A_k."""
+    k = 1024
+    t = O.decision_thresholds_f32(alpha)
+    rows = []
+    for m in (np.float32(0.0371), np.float32(1.0), np.float32(3.1e-3)):
+        vals = []
+        for tk in t:
+            ci = int(np.array([tk * m], np.float32).view(np.int32)[0])
+            steps = np.arange(ci - 24, ci + 25, dtype=np.int32)
+            vals.extend(steps.view(np.float32).tolist())
+        vals = np.array(vals, np.float32)
+        vals = vals[(vals >= 0) & (vals <= m)]
+        row = np.zeros(k, np.float32)
+        row[:len(vals)] = vals
+        row[len(vals)] = m
+        sgn = np.where(np.arange(k) % 2 == 1, -1.0, 1.0).astype(np.float32)
+        rows.append(row * sgn)
+    w = np.stack(rows)
+    w_vals, w_dev = weight_tensor(w, "f32")
+    full_roundtrip(gpu_lib, w_vals, w_dev, alpha)
+
+
+def test_empty_calls(gpu_lib):
+    opq = gpu_lib
+    w = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    qw = opq.quantize(w, 0.73)
+    assert qw.packed.shape == (0, 8)
+    w = torch.empty((3, 0), dtype=torch.bfloat16, device=DEV)
+    qw = opq.quantize(w, 0.73)
+    torch.cuda.synchronize()
+    assert np.all(qw.scale.cpu().numpy() == 0)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    qw = opq.quantize(to_bf16(WL.normal(1, (16, 64), 0.02)).to(DEV), 0.73)
+    y = opq.linear(x, qw, 0.73)
+    assert y.shape == (0, 16)
+    # k = 0: y = bias
+    qw0 = opq.quantize(torch.empty((16, 0), dtype=torch.bfloat16, device=DEV), 0.73)
+    bias = torch.arange(16, dtype=torch.float32, device=DEV)
+    for m in (4, 200):
+        y = opq.linear(torch.empty((m, 0), dtype=torch.bfloat16, device=DEV), qw0, 0.73, bias=bias)
+        assert torch.equal(y.cpu(), bias.cpu().expand(m, 16))
+
+
+# ------------------------------------------------------------------ linear edge cases
+
+@pytest.mark.parametrize("m", [1, 8, 16, 33, 64, 65, 128, 130, 257])
+@pytest.mark.parametrize("n,k", [(16, 32), (100, 256), (300, 544), (129, 96)])
+def test_linear_shapes(gpu_lib, m, n, k):
+    opq = gpu_lib
+    w_vals, w_dev = weight_tensor(WL.student_t(300 + n, (n, k)), "bf16")
+    qw = quantize_guarded(opq, w_dev, 0.73)
+    ref = O.quantize(w_vals, 0.73)
+    assert_quant_equal(qw, ref)
+    d_ref = O.dequantize(*ref, 0.73)
+    xt = to_bf16(WL.normal(400 + m, (m, k)))
+    bias = WL.normal(500 + n, (n,), 0.5)
+    gy = Guarded((m, n), torch.float32)
+    opq.linear(xt.to(DEV), qw, 0.73, bias=torch.from_numpy(bias).to(DEV), out=gy.t)
+    torch.cuda.synchronize()
+    gy.check()
+    y_ref = O.linear(bf16_bits(xt), d_ref, bias)
+    assert_linear_close(gy.t.cpu().numpy(), y_ref)
+
+
+def test_linear_one_hot_rows_pick_weights(gpu_lib):
+    """x = identity rows: y[:, n] is the reconstruction W'[n, :] itself."""
+    opq = gpu_lib
+    k, n = 256, 96
+    w_vals, w_dev = weight_tensor(WL.student_t(600, (n, k)), "bf16")
+    qw = opq.quantize(w_dev, 0.73)
+    d = opq.dequantize(qw, 0.73)
+    for m in (k, 64):
+        x = torch.zeros((m, k), dtype=torch.bfloat16)
+        x[torch.arange(m), torch.arange(m)] = 1.0
+        y = opq.linear(x.to(DEV), qw, 0.73).cpu()
+        assert torch.equal(y, d.cpu().float()[:, :m].T.contiguous())
+
+
+# ------------------------------------------------------------------ full-size configs
+
+def _sample_rows(n, count, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, min(count, n), replace=False)]))
+
+
+def _check_layer(opq, L, alpha, with_linear, x_rows=64, q_rows=512):
+    w32 = L.make_w()
+    w_vals, w_dev = weight_tensor(w32, L.w_dtype)
+    del w32
+    qw = opq.quantize(w_dev, alpha)
+    rows = _sample_rows(L.n, q_rows, L.n + L.k)
+    ref_rows = O.quantize(w_vals[rows], alpha)
+    torch.cuda.synchronize()
+    assert_quant_equal(qw, ref_rows, rows)
+    d = opq.dequantize(qw, alpha)
+    d_rows = bf16_bits(d[torch.from_numpy(rows).to(DEV)])
+    q_ref, _ = O.unpack(ref_rows[0], ref_rows[1])
+    assert_dequant_close(d_rows, O.dequantize(*ref_rows, alpha), q_ref)
+    del d
+    if with_linear:
+        ref = O.quantize(w_vals, alpha)
+        d_ref = O.dequantize(*ref, alpha)
+        xt = to_bf16(L.make_x())
+        y = opq.linear(xt.to(DEV), qw, alpha)
+        xr = _sample_rows(L.m, x_rows, L.m)
+        y_rows = y[torch.from_numpy(xr).to(DEV)].cpu().numpy()
+        y_ref = O.linear(bf16_bits(xt)[xr], d_ref)
+        return assert_linear_close(y_rows, y_ref)
+    return None
+
+
+@pytest.mark.parametrize("key", ["skinny", "qkv", "ffn"])
+def test_config_full_size(gpu_lib, key):
+    cfg = WL.config(key)
+    for L in cfg.layers:
+        rel = _check_layer(gpu_lib, L, WL.ALPHA, with_linear=True)
+        print(f"{key}/{L.name}: linear max err / rms = {rel:.2e}")
+
+
+@pytest.mark.parametrize("alpha", WL.ALPHAS_SWEEP)
+def test_model_layer_shapes(gpu_lib, alpha):
+    """The four block shapes of the whole-model pass, first and last block."""
+    cfg = WL.config("model")
+    for L in cfg.layers[:4] + cfg.layers[-4:]:
+        _check_layer(gpu_lib, L, alpha, with_linear=False, q_rows=128)

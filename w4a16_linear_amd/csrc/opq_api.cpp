@@ -1,0 +1,117 @@
+// The C ABI of libopq (include/opq.h): argument checks in the documented
+// order, host tables, then one launch on the caller's stream.
+#include "opq.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "opq_internal.hpp"
+
+namespace {
+
+constexpr int64_t kMaxK = 65536;
+
+// NULL (allowed for an empty array) counts as aligned.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool alpha_ok(float a) { return std::isfinite(a) && a > 0.0f; }
+
+bool shape_ok(int64_t n, int64_t k) { return n >= 0 && k >= 0 && k % 32 == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? OPQ_OK : OPQ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+int opq_abi_version(void) { return OPQ_ABI_VERSION; }
+
+const char* opq_status_str(int status) {
+  switch (status) {
+    case OPQ_OK: return "ok";
+    case OPQ_ERR_NULL: return "a required pointer is NULL";
+    case OPQ_ERR_SHAPE: return "bad shape: sizes must be >= 0 and k a multiple of 32";
+    case OPQ_ERR_ALPHA: return "alpha must be finite and > 0";
+    case OPQ_ERR_ALIGN: return "every array must be 16-byte aligned";
+    case OPQ_ERR_DTYPE: return "unknown dtype code";
+    case OPQ_ERR_WORKSPACE: return "workspace smaller than opq_linear_workspace_bytes()";
+    case OPQ_ERR_UNSUPPORTED: return "size beyond what the kernels handle";
+    case OPQ_ERR_HIP: return "the HIP runtime refused a launch";
+    default: return "unknown status";
+  }
+}
+
+int opq_decision_points(float alpha, float* out_t) {
+  if (!out_t) return OPQ_ERR_NULL;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  return opq::decision_points(alpha, out_t) ? OPQ_OK : OPQ_ERR_ALPHA;
+}
+
+int opq_levels(float alpha, double* out_g) {
+  if (!out_g) return OPQ_ERR_NULL;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  opq::levels(alpha, out_g);
+  return OPQ_OK;
+}
+
+int opq_quantize(const void* w, int w_dtype, int64_t n, int64_t k, float alpha,
+                 uint32_t* packed, uint32_t* sign, float* scale, void* stream) {
+  const bool nk = n > 0 && k > 0;
+  if ((nk && (!w || !packed || !sign)) || (n > 0 && !scale)) return OPQ_ERR_NULL;
+  if (!shape_ok(n, k)) return OPQ_ERR_SHAPE;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(sign) || !aligned16(scale))
+    return OPQ_ERR_ALIGN;
+  if (w_dtype != OPQ_F32 && w_dtype != OPQ_BF16) return OPQ_ERR_DTYPE;
+  if (k > kMaxK) return OPQ_ERR_UNSUPPORTED;
+  if (n == 0) return OPQ_OK;
+  opq::DecisionPoints dp;
+  if (!opq::decision_points(alpha, dp.t)) return OPQ_ERR_ALPHA;
+  return hip_status(opq::launch_quantize(w, w_dtype == OPQ_BF16, n, k, dp, packed, sign, scale,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int opq_dequantize(const uint32_t* packed, const uint32_t* sign, const float* scale, int64_t n,
+                   int64_t k, float alpha, uint16_t* w_out, void* stream) {
+  if (n > 0 && k > 0 && (!packed || !sign || !scale || !w_out)) return OPQ_ERR_NULL;
+  if (!shape_ok(n, k)) return OPQ_ERR_SHAPE;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  if (!aligned16(packed) || !aligned16(sign) || !aligned16(scale) || !aligned16(w_out))
+    return OPQ_ERR_ALIGN;
+  if (n == 0 || k == 0) return OPQ_OK;
+  if (k > kMaxK) return OPQ_ERR_UNSUPPORTED;
+  opq::Levels lv;
+  opq::levels(alpha, lv.g);
+  return hip_status(opq::launch_dequantize(packed, sign, scale, n, k, lv, w_out,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+size_t opq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m < 0 || n < 0 || k < 0) return 0;
+  return opq::linear_workspace_bytes(m, n, k);
+}
+
+int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign, const float* scale,
+               const float* bias, int64_t m, int64_t n, int64_t k, float alpha, float* y,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  if ((m > 0 && k > 0 && !x) || (n > 0 && k > 0 && (!packed || !sign)) || (n > 0 && !scale) ||
+      (m > 0 && n > 0 && !y))
+    return OPQ_ERR_NULL;
+  if (m < 0 || !shape_ok(n, k)) return OPQ_ERR_SHAPE;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(sign) || !aligned16(scale) ||
+      !aligned16(y) || (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)))
+    return OPQ_ERR_ALIGN;
+  const size_t need = opq::linear_workspace_bytes(m, n, k);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return OPQ_ERR_WORKSPACE;
+  if (m == 0 || n == 0) return OPQ_OK;
+  if (k > kMaxK) return OPQ_ERR_UNSUPPORTED;
+  opq::Levels lv;
+  opq::levels(alpha, lv.g);
+  return hip_status(opq::launch_linear(x, packed, sign, scale, bias, m, n, k, lv, y, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

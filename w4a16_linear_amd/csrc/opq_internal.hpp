@@ -1,0 +1,42 @@
+// Internal interface between the C ABI (opq_api.cpp), the host tables
+// (tables.cpp) and the kernel launchers (*.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace opq {
+
+constexpr int kLevels = 15;  // 4-bit magnitude codes 0..15
+
+// Decision points T_k (k = 1..15) of round(15 u^alpha), passed by value.
+struct DecisionPoints {
+  float t[kLevels];
+};
+
+// Reconstruction levels G_q = (q/15)^(1/alpha), q = 0..15, passed by value.
+struct Levels {
+  double g[kLevels + 1];
+};
+
+// tables.cpp (host only)
+bool decision_points(float alpha, float out[kLevels]);
+void levels(float alpha, double out[kLevels + 1]);
+
+// quantize.hip
+hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, int64_t k,
+                           const DecisionPoints& dp, uint32_t* packed, uint32_t* sign,
+                           float* scale, hipStream_t stream);
+
+// dequantize.hip
+hipError_t launch_dequantize(const uint32_t* packed, const uint32_t* sign, const float* scale,
+                             int64_t n, int64_t k, const Levels& lv, uint16_t* out,
+                             hipStream_t stream);
+
+// linear.hip
+size_t linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
+hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
+                         const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
+                         const Levels& lv, float* y, void* workspace, hipStream_t stream);
+
+}  // namespace opq

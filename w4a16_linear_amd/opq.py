@@ -1,0 +1,187 @@
+"""Python binding of libopq (include/opq.h): argument marshalling only.
+
+Every step of the hot path runs in the library's HIP kernels; this module
+checks tensor placement, allocates outputs with torch on the caller's device
+and passes raw pointers plus the current torch stream.  It never computes the
+method itself and fails loudly when libopq.so is missing.
+
+Packed words and sign words are carried in torch.int32 tensors holding the
+uint32 bit patterns; bfloat16 tensors are passed by their bits.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import NamedTuple, Optional
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libopq.so")
+ABI_VERSION = 1
+
+OPQ_F32 = 0
+OPQ_BF16 = 1
+
+# int opq_*(...) signatures, in header order
+_SIGNATURES = {
+    "opq_abi_version": (ctypes.c_int, []),
+    "opq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "opq_decision_points": (ctypes.c_int, [ctypes.c_float, ctypes.c_void_p]),
+    "opq_levels": (ctypes.c_int, [ctypes.c_float, ctypes.c_void_p]),
+    "opq_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                    ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]),
+    "opq_dequantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                      ctypes.c_void_p, ctypes.c_void_p]),
+    "opq_linear_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64,
+                                                     ctypes.c_int64]),
+    "opq_linear": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                  ctypes.c_void_p]),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+class OpqError(ValueError):
+    """A libopq call returned a non-zero status."""
+
+    def __init__(self, fn: str, status: int, text: str):
+        super().__init__(f"{fn}: status {status}: {text}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libopq.so once; raise if it is missing or of another ABI."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libopq.so not built at {path}: run `python -m w4a16_linear_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    ver = lib.opq_abi_version()
+    if ver != ABI_VERSION:
+        raise RuntimeError(f"libopq ABI {ver}, binding expects {ABI_VERSION}")
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return load().opq_status_str(status).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise OpqError(fn, status, status_str(status))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _need_cuda(name: str, t: torch.Tensor, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {ndim}-d tensor")
+
+
+# ------------------------------------------------------------------ host tables
+
+def decision_points(alpha: float) -> np.ndarray:
+    """The fifteen binary32 decision points the quantize kernel uses (host)."""
+    out = np.zeros(15, np.float32)
+    _check("opq_decision_points", load().opq_decision_points(alpha, out.ctypes.data))
+    return out
+
+
+def levels(alpha: float) -> np.ndarray:
+    """The sixteen reconstruction levels (q/15)^(1/alpha) in double (host)."""
+    out = np.zeros(16, np.float64)
+    _check("opq_levels", load().opq_levels(alpha, out.ctypes.data))
+    return out
+
+
+# ------------------------------------------------------------------ device calls
+
+class QuantizedWeight(NamedTuple):
+    packed: torch.Tensor  # int32 [n, k/8]: eight 4-bit codes per word
+    sign: torch.Tensor    # int32 [n, k/32]: sign plane
+    scale: torch.Tensor   # float32 [n]: per-row max |w|
+
+    @property
+    def shape(self):
+        return (self.packed.shape[0], self.packed.shape[1] * 8)
+
+
+def quantize(w: torch.Tensor, alpha: float, out: Optional[QuantizedWeight] = None) -> QuantizedWeight:
+    """Quantize a float32 or bfloat16 weight [n, k] on its device."""
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("w must be float32 or bfloat16")
+    _need_cuda("w", w, w.dtype, 2)
+    n, k = w.shape
+    if out is None:
+        out = QuantizedWeight(
+            torch.empty((n, k // 8), dtype=torch.int32, device=w.device),
+            torch.empty((n, k // 32), dtype=torch.int32, device=w.device),
+            torch.empty((n,), dtype=torch.float32, device=w.device))
+    dtype = OPQ_BF16 if w.dtype == torch.bfloat16 else OPQ_F32
+    st = load().opq_quantize(_ptr(w), dtype, n, k, alpha, _ptr(out.packed), _ptr(out.sign),
+                             _ptr(out.scale), _stream(w.device))
+    _check("opq_quantize", st)
+    return out
+
+
+def dequantize(qw: QuantizedWeight, alpha: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bfloat16 reconstruction [n, k] of a quantized weight."""
+    n, k = qw.shape
+    for name, t, dt in (("packed", qw.packed, torch.int32), ("sign", qw.sign, torch.int32)):
+        _need_cuda(name, t, dt, 2)
+    _need_cuda("scale", qw.scale, torch.float32, 1)
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.bfloat16, device=qw.packed.device)
+    st = load().opq_dequantize(_ptr(qw.packed), _ptr(qw.sign), _ptr(qw.scale), n, k, alpha,
+                               _ptr(out), _stream(qw.packed.device))
+    _check("opq_dequantize", st)
+    return out
+
+
+def linear_workspace_bytes(m: int, n: int, k: int) -> int:
+    return int(load().opq_linear_workspace_bytes(m, n, k))
+
+
+def linear(x: torch.Tensor, qw: QuantizedWeight, alpha: float, bias: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y[m, n] = x[m, k] W'^T (+ bias) in float32, W' made on chip from qw."""
+    _need_cuda("x", x, torch.bfloat16, 2)
+    m, k = x.shape
+    n, kw = qw.shape
+    if kw != k:
+        raise ValueError(f"x has k={k}, weight has k={kw}")
+    if bias is not None:
+        _need_cuda("bias", bias, torch.float32, 1)
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    need = linear_workspace_bytes(m, n, k)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = load().opq_linear(_ptr(x), _ptr(qw.packed), _ptr(qw.sign), _ptr(qw.scale), _ptr(bias),
+                           m, n, k, alpha, _ptr(out), _ptr(workspace), ws_bytes,
+                           _stream(x.device))
+    _check("opq_linear", st)
+    return out
