@@ -28,8 +28,9 @@
  *   - device pointers are memory of the current HIP device; host pointers are
  *     marked as such;
  *   - the caller owns every buffer; the library allocates nothing, frees
- *     nothing, synchronises nothing and keeps no mutable global state, so
- *     calls are reentrant; outputs must not overlap inputs;
+ *     nothing and synchronises nothing; its only global state is a
+ *     mutex-guarded memo of the per-alpha host tables, so calls are reentrant
+ *     and thread-safe; outputs must not overlap inputs;
  *   - `stream` is a hipStream_t (NULL = the default stream); work is enqueued
  *     on it and the call returns at once; faults inside kernels show up at the
  *     caller's next synchronisation;

@@ -13,8 +13,8 @@
 //    rows and all of k; its waves split k and reduce through LDS.  W' is the
 //    A operand of v_mfma_f32_16x16x32_bf16 (one packed word = a lane's eight
 //    k values), x^T the B operand.
-//  * otherwise: 128x128 output tiles, k steps of 64, x and dequantized W'
-//    staged through LDS, 2x2 waves each on 64x64 with v_mfma_f32_32x32x16_bf16.
+//  * otherwise: 256x256 output tiles with v_mfma_f32_32x32x16_bf16; weights
+//    dequantized in registers, x staged through LDS (details below).
 #include "device_common.hpp"
 
 namespace opq {
@@ -107,112 +107,274 @@ __global__ __launch_bounds__(kSkWaves * kWave) void linear_skinny(
 }
 
 // ---------------------------------------------------------------- tiled MFMA path
+//
+// Block tile 256 (x rows) x 256 (weight rows), k steps of 64, four waves.
+// Wave w owns weight rows [64w, 64w + 64) of the tile and all 256 x rows:
+// 8 x 2 accumulators of 32x32 (256 fp32 per lane, held in AGPRs).
+//
+// Weights never pass through LDS: each lane loads the packed words of its two
+// weight rows straight into VGPRs, in the layout of the MFMA B operand (one
+// packed word = the eight k values a lane supplies), and dequantizes them with
+// its rows' tables held as byte planes in registers (v_perm lookups).  Lanes
+// 0..31 take words 0..3 of the 8-word k step and lanes 32..63 words 4..7, so
+// sub-step s contracts k-blocks {s, 4 + s}; the x fragments read from LDS use
+// the same k-blocks.  Within a k-block the dequantizer emits bf16 pairs in the
+// order (k0,k2) (k4,k6) (k1,k3) (k5,k7); x is stored to LDS in that order too.
+// Only x is staged in LDS (two stages, rows XOR-swizzled by 16-byte chunk).
 
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kTiledThreads = 256;
-constexpr int kLd = kBK + 8;  // padded LDS row stride (bf16 elements)
+constexpr int kTM = 256, kTN = 256, kTK = 64;
+constexpr int kMfmaThreads = 256;
+constexpr int kAChunks = kTK / 8;                  // 16-byte chunks per LDS row
+constexpr int kAStage = kTM * kTK;                 // bf16 per stage
 
-__global__ __launch_bounds__(kTiledThreads) void linear_tiled(
+// Byte planes of a row's sixteen bf16 table entries: lo[i] holds the low bytes
+// of entries 4i..4i+3, hi[i] the high bytes.
+struct RowLut {
+  uint32_t lo[4];
+  uint32_t hi[4];
+};
+
+__device__ __forceinline__ RowLut make_row_lut(const Levels& lv, float m) {
+  RowLut t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) t.lo[i] = t.hi[i] = 0u;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const uint32_t e = lut_entry(lv, q, m);
+    t.lo[q >> 2] |= (e & 0xFFu) << (8 * (q & 3));
+    t.hi[q >> 2] |= (e >> 8) << (8 * (q & 3));
+  }
+  return t;
+}
+
+// One plane looked up for four codes (one per byte of `sel7`, bit 3 stripped);
+// `mask` has 0xFF in the bytes whose code is >= 8.
+__device__ __forceinline__ uint32_t plane4(const uint32_t (&p)[4], uint32_t sel7, uint32_t mask) {
+  const uint32_t a = __builtin_amdgcn_perm(p[1], p[0], sel7);
+  const uint32_t b = __builtin_amdgcn_perm(p[3], p[2], sel7);
+  return (b & mask) | (a & ~mask);
+}
+
+// Dequantize one packed word (codes k0..k7) with its sign byte into four bf16
+// pairs: out = {(k0,k2), (k4,k6), (k1,k3), (k5,k7)}.  `sb` holds the sign byte
+// in bits 0..7 (higher bits are ignored).
+__device__ __forceinline__ void dequant_word(uint32_t w, uint32_t sb, const RowLut& t,
+                                             uint32_t (&out)[4]) {
+  const uint32_t se7 = w & 0x07070707u;          // codes k0 k2 k4 k6, bit 3 stripped
+  const uint32_t so7 = (w >> 4) & 0x07070707u;   // codes k1 k3 k5 k7, bit 3 stripped
+  // 0xFF bytes where the code is >= 8: replicate bit 3 of each code via the
+  // sign-copy selectors of v_perm (8 -> bit 15, 9 -> bit 31, 10 -> bit 47, 11 -> bit 63).
+  const uint32_t w4 = w << 4;
+  const uint32_t me = __builtin_amdgcn_perm(w4 << 8, w4, 0x090B080Au);
+  const uint32_t mo = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
+  const uint32_t lo_e = plane4(t.lo, se7, me), hi_e = plane4(t.hi, se7, me);
+  const uint32_t lo_o = plane4(t.lo, so7, mo), hi_o = plane4(t.hi, so7, mo);
+  // sign bits into bit 7 of each high byte: spread bits 0,2,4,6 (even) or
+  // 1,3,5,7 (odd) of the byte to 7, 15, 23, 31 with one 24-bit multiply.
+  const uint32_t sge = __umul24((sb << 7) & 0x2A80u, 0x41041u);
+  const uint32_t sgo = __umul24((sb << 6) & 0x2A80u, 0x41041u);
+  const uint32_t hs_e = hi_e | (sge & 0x80808080u);
+  const uint32_t hs_o = hi_o | (sgo & 0x80808080u);
+  out[0] = __builtin_amdgcn_perm(hs_e, lo_e, 0x05010400u);
+  out[1] = __builtin_amdgcn_perm(hs_e, lo_e, 0x07030602u);
+  out[2] = __builtin_amdgcn_perm(hs_o, lo_o, 0x05010400u);
+  out[3] = __builtin_amdgcn_perm(hs_o, lo_o, 0x07030602u);
+}
+
+// x chunk (8 bf16, natural k order) -> the dequantizer's pair order.
+__device__ __forceinline__ uint4 sigma_order(uint4 v) {
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (k0, k2)
+  r.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // (k4, k6)
+  r.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (k1, k3)
+  r.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // (k5, k7)
+  return r;
+}
+
+// LDS element offset of 16-byte chunk c of tile row r.  A row is 128 bytes
+// (32 banks), so rows alternate bank halves; XOR-ing the chunk with bits 1..3
+// of the row spreads any 16 consecutive rows over all 64 banks, which keeps the
+// 16-lane passes of ds_read_b128 conflict-free.
+__device__ __forceinline__ int a_off(int r, int c) { return r * kTK + ((c ^ ((r >> 1) & 7)) << 3); }
+
+__global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
-    const float* __restrict__ bias, int m, int n, int k, Levels lv, float* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[kBM * kLd];
-  __shared__ __attribute__((aligned(16))) uint16_t s_b[kBN * kLd];
-  __shared__ uint16_t s_lut[kBN * 16];
+    const float* __restrict__ bias, int m, int n, int k, int tiles_m, Levels lv,
+    float* __restrict__ y) {
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kAStage];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * kBM, n0 = blockIdx.x * kBN;
+  // consecutive blocks share a weight tile and walk the x tiles
+  const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
+  const int m0 = tile_m * kTM;
+  const int nw = tile_n * kTN + wave * 64;       // first weight row of this wave
+  const int g = lane >> 5;                        // which half of the k step
   const int kwords = k / 8, swords = k / 32;
+  const int nsteps = (k + kTK - 1) / kTK;
 
-  for (int i = tid; i < kBN * 16; i += kTiledThreads) {
-    const int gn = n0 + (i >> 4);
-    s_lut[i] = (uint16_t)lut_entry(lv, i & 15, gn < n ? scale[gn] : 0.0f);
+  // This lane's two weight rows (B fragments f = 0, 1).  Rows past n are
+  // clamped to row n - 1: their columns are computed and never stored.
+  int brow[2];
+  RowLut lut[2];
+  uint32_t pw_off[2], sw_off[2];  // byte offsets from the wave's first row
+  const int nw_c = min(nw, n - 1);
+  const char* pbase = reinterpret_cast<const char*>(packed + (int64_t)nw_c * kwords);
+  const char* sbase = reinterpret_cast<const char*>(sign + (int64_t)nw_c * swords);
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    brow[f] = nw + 32 * f + (lane & 31);
+    const int rc = min(brow[f], n - 1);
+    lut[f] = make_row_lut(lv, scale[rc]);
+    pw_off[f] = (uint32_t)(rc - nw_c) * (uint32_t)kwords * 4u;
+    sw_off[f] = (uint32_t)(rc - nw_c) * (uint32_t)swords * 4u;
   }
 
-  floatx16_t acc[2][2];
+  // Weights of step kt: words 4g..4g+3 and sign word g of the step.  In a final
+  // half step (k % 64 == 32) lanes g = 1 read the first half again and zero it.
+  auto load_b = [&](int kt, uint4 (&pw)[2], uint32_t (&sw)[2]) {
+    const int kk = kt * kTK + 32 * g;
+    const int kc = min(kk, k - 32);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // weight staging: thread -> row tid/2, 32 k values (four packed words)
-  const int br = tid >> 1, bh = tid & 1;
-  const int bgn = n0 + br;
-
-  for (int k0 = 0; k0 < k; k0 += kBK) {
-    __syncthreads();  // previous tile consumed; tables ready on the first pass
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + kTiledThreads * i;
-      const int r = c >> 3, cc = c & 7;
-      const int gm = m0 + r, gk = k0 + cc * 8;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (gm < m && gk < k) v = *reinterpret_cast<const uint4*>(x + (int64_t)gm * k + gk);
-      *reinterpret_cast<uint4*>(s_a + r * kLd + cc * 8) = v;
+    for (int f = 0; f < 2; ++f) {
+      pw[f] = *reinterpret_cast<const uint4*>(pbase + pw_off[f] + (uint32_t)kc / 2u);
+      sw[f] = *reinterpret_cast<const uint32_t*>(sbase + sw_off[f] + (uint32_t)kc / 8u);
     }
-    {
-      const int gk = k0 + 32 * bh;
-      uint4 pw = make_uint4(0u, 0u, 0u, 0u);
-      uint32_t sw = 0u;
-      if (bgn < n && gk < k) {
-        pw = *reinterpret_cast<const uint4*>(packed + (int64_t)bgn * kwords + gk / 8);
-        sw = sign[(int64_t)bgn * swords + gk / 32];
+    if ((k & (kTK - 1)) && kt == nsteps - 1 && kk >= k) {
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        pw[f] = make_uint4(0u, 0u, 0u, 0u);
+        sw[f] = 0u;
       }
-      const uint16_t* lut = s_lut + br * 16;
-      const uint32_t pws[4] = {pw.x, pw.y, pw.z, pw.w};
-      uint32_t o[16];
+    }
+  };
+  // x of step kt: thread tid moves chunks tid + 256 i (row c/8, chunk c%8).
+  // Rows past m read row m - 1 (never stored); chunks past k read the last
+  // chunk, which only meets zero weights.
+  const char* xbase = reinterpret_cast<const char*>(x + (int64_t)m0 * k);
+  uint32_t x_off[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + kMfmaThreads * i;
+    const int r = min(m0 + (c >> 3), m - 1) - m0;
+    x_off[i] = ((uint32_t)r * (uint32_t)k + 8u * (uint32_t)(c & 7)) * 2u;
+  }
+  auto load_a = [&](int kt, uint4 (&xa)[8]) {
+    const bool tail = kt * kTK + kTK > k;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          uint32_t h = lut[(pws[j] >> (4 * i)) & 15u];
-          h |= ((sw >> (8 * j + i)) & 1u) << 15;
-          if (i & 1) o[4 * j + (i >> 1)] |= h << 16;
-          else o[4 * j + (i >> 1)] = h;
-        }
-      uint4* dst = reinterpret_cast<uint4*>(s_b + br * kLd + 32 * bh);
+    for (int i = 0; i < 8; ++i) {
+      uint32_t off = x_off[i] + (uint32_t)(kt * kTK) * 2u;
+      if (tail) {
+        const int c = tid + kMfmaThreads * i;
+        if (kt * kTK + 8 * (c & 7) >= k) off -= 64u;  // step back into the row
+      }
+      xa[i] = *reinterpret_cast<const uint4*>(xbase + off);
+    }
+  };
+  auto store_a = [&](int stage, const uint4 (&xa)[8]) {
+    uint16_t* base = s_a + stage * kAStage;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[j] = make_uint4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + kMfmaThreads * i;
+      *reinterpret_cast<uint4*>(base + a_off(c >> 3, c & 7)) = sigma_order(xa[i]);
+    }
+  };
+
+  floatx16_t acc[8][2];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][f][e] = 0.0f;
+
+  // Sub-step s of a k step: dequantize word s of both B fragments, read the
+  // eight x fragments of k-blocks {s, 4 + s}.
+  auto dequant_b = [&](int s, const uint4 (&pwv)[2], const uint32_t (&swv)[2], bf16x8_t (&b)[2]) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      const uint32_t words[4] = {pwv[f].x, pwv[f].y, pwv[f].z, pwv[f].w};
+      uint32_t o[4];
+      dequant_word(words[s], swv[f] >> (8 * s), lut[f], o);
+      b[f] = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+    }
+  };
+  auto read_a = [&](const uint16_t* sa, int s, bf16x8_t (&a)[8]) {
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+      a[mi] = *reinterpret_cast<const bf16x8_t*>(sa + a_off(mi * 32 + (lane & 31), 4 * g + s));
+  };
+
+  // Pipeline per k step kt (x in LDS stage kt & 1):
+  //   issue the weights of step kt + 1;
+  //   sub-step 0;
+  //   store x of step kt + 1 (loaded during step kt - 1) into the other stage,
+  //   then issue the x loads of step kt + 2 into the freed registers;
+  //   sub-steps 1..3;  barrier.
+  // The other stage was last read in step kt - 1, before the barrier that
+  // ended it, so the mid-step store is safe; x loads get a full step in flight.
+  uint4 pw[2], pw_next[2];
+  uint32_t sw[2], sw_next[2];
+  uint4 xa[8];
+  if (nsteps > 0) {
+    load_a(0, xa);
+    load_b(0, pw, sw);
+    store_a(0, xa);
+  }
+  if (nsteps > 1) load_a(1, xa);
+  __syncthreads();
+
+  bf16x8_t a_buf[2][8], b_buf[2][2];
+  for (int kt = 0; kt < nsteps; ++kt) {
+    const int stage = kt & 1;
+    if (kt + 1 < nsteps) load_b(kt + 1, pw_next, sw_next);
+    const uint16_t* sa = s_a + stage * kAStage;
+    read_a(sa, 0, a_buf[0]);
+    dequant_b(0, pw, sw, b_buf[0]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int cur = s & 1, nxt = cur ^ 1;
+      if (s < 3) {
+        read_a(sa, s + 1, a_buf[nxt]);
+        // the next fragments' LDS reads stay ahead of this sub-step's MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        dequant_b(s + 1, pw, sw, b_buf[nxt]);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+        for (int f = 0; f < 2; ++f)
+          acc[mi][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_buf[cur][mi], b_buf[cur][f],
+                                                               acc[mi][f], 0, 0, 0);
+      if (s == 0 && kt + 1 < nsteps) {
+        store_a(stage ^ 1, xa);
+        if (kt + 2 < nsteps) load_a(kt + 2, xa);
+      }
+    }
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+      pw[f] = pw_next[f];
+      sw[f] = sw_next[f];
     }
     __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      bf16x8_t a[2], b[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(s_a + (wm * 64 + i * 32 + (lane & 31)) * kLd + kk +
-                                                  8 * (lane >> 5));
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(s_b + (wn * 64 + j * 32 + (lane & 31)) * kLd + kk +
-                                                  8 * (lane >> 5));
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
   }
 
   // 32x32 accumulator layout: register e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32.
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int f = 0; f < 2; ++f) {
+    const int col = brow[f];
+    const float bv = (bias && col < n) ? bias[col] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = n0 + wn * 64 + j * 32 + (lane & 31);
-      const float bv = (bias && col < n) ? bias[col] : 0.0f;
+    for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (row < m && col < n) y[(int64_t)row * n + col] = acc[i][j][e] + bv;
+        const int row = m0 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (row < m && col < n) y[(int64_t)row * n + col] = acc[mi][f][e] + bv;
       }
-    }
+  }
 }
 
 }  // namespace
@@ -227,9 +389,10 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32
     hipLaunchKernelGGL(linear_skinny, dim3((unsigned)blocks), dim3(kSkWaves * kWave), 0, stream, x,
                        packed, sign, scale, bias, (int)m, (int)n, (int)k, lv, y);
   } else {
-    const dim3 grid((unsigned)((n + kBN - 1) / kBN), (unsigned)((m + kBM - 1) / kBM));
-    hipLaunchKernelGGL(linear_tiled, grid, dim3(kTiledThreads), 0, stream, x, packed, sign, scale,
-                       bias, (int)m, (int)n, (int)k, lv, y);
+    const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
+    hipLaunchKernelGGL(linear_mfma, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMfmaThreads), 0,
+                       stream, x, packed, sign, scale, bias, (int)m, (int)n, (int)k, (int)tiles_m,
+                       lv, y);
   }
   return hipGetLastError();
 }
