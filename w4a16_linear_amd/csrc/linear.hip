@@ -21,17 +21,32 @@ namespace opq {
 namespace {
 
 // ---------------------------------------------------------------- skinny path
+//
+// m <= 64: the product is bound by streaming the packed weights.  A block owns
+// 16 weight rows and all of k; k is cut into 128-wide blocks dealt round-robin
+// to the block's 8 waves.  W' is the A operand of v_mfma_f32_16x16x32_bf16 and
+// x^T the B operand.  For one 128-wide k block, lane l (row r = l%16, group
+// g = l/16) loads packed words 4g..4g+3 of row r (16 bytes, so four lanes read
+// 64 contiguous bytes of the row), sign word g, and x[.][32g .. 32g + 31] for
+// its x rows; sub-step t then contracts the k-blocks {t, 4 + t, 8 + t, 12 + t}
+// (units of 8), lane g supplying word t of its four.  A wave issues the loads
+// of up to CH of its k blocks at once, one batch ahead of use.  Codes are
+// looked up in the block's 16 x 16 bf16 table in LDS; the waves' partial sums
+// meet in LDS at the end.
 
 constexpr int kSkinnyMaxM = 64;
 constexpr int kSkRows = 16;    // weight rows per block
 constexpr int kSkWaves = 8;    // waves splitting k
+constexpr int kSkBlockK = 128; // k per block step
 
+template <int NMB>             // 16-row blocks of x: 1, 2 or 4
 __global__ __launch_bounds__(kSkWaves * kWave) void linear_skinny(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
     const float* __restrict__ bias, int m, int n, int k, Levels lv, float* __restrict__ y) {
+  constexpr int CH = NMB == 4 ? 1 : (NMB == 2 ? 2 : 3);   // k blocks per load batch
   __shared__ uint16_t s_lut[kSkRows * 16];
-  __shared__ float s_red[kSkWaves][4][4][kWave];  // wave, m-block, acc reg, lane
+  __shared__ float s_red[kSkWaves][NMB][4][kWave];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -39,61 +54,100 @@ __global__ __launch_bounds__(kSkWaves * kWave) void linear_skinny(
   const int n0 = blockIdx.x * kSkRows;
 
   if (tid < kSkRows * 16) {
-    const int r = tid >> 4, q = tid & 15;
-    const int gn = n0 + r;
-    s_lut[tid] = (uint16_t)lut_entry(lv, q, gn < n ? scale[gn] : 0.0f);
+    const int gn = min(n0 + (tid >> 4), n - 1);
+    s_lut[tid] = (uint16_t)lut_entry(lv, tid & 15, scale[gn]);
   }
   __syncthreads();
 
-  const int nmb = (m + 15) / 16;  // 16-row blocks of x, at most 4
   const int r = lane & 15;        // weight row of this lane's A fragment
-  const int g = lane >> 4;        // which eight k of the 32-wide step
-  const int gn = n0 + r;
+  const int g = lane >> 4;        // 32-wide k group within a 128-wide block
   const int kwords = k / 8, swords = k / 32;
+  const int rc = min(n0 + r, n - 1);
+  const uint32_t* prow = packed + (int64_t)rc * kwords + 4 * g;
+  const uint32_t* srow = sign + (int64_t)rc * swords + g;
   const uint16_t* lut = s_lut + r * 16;
+  const uint16_t* xrow[NMB];
+#pragma unroll
+  for (int b = 0; b < NMB; ++b) xrow[b] = x + (int64_t)min(b * 16 + r, m - 1) * k + 32 * g;
 
-  floatx4_t acc[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  // k blocks of this wave: wave, wave + 8, ...; a half block (k % 128 == 64 or
+  // 32) lets lanes whose group starts past k read group 0 again and drop it.
+  const int nblk = (k + kSkBlockK - 1) / kSkBlockK;
+  const int mine = nblk > wave ? (nblk - 1 - wave) / kSkWaves + 1 : 0;
 
-  for (int s = wave; s < swords; s += kSkWaves) {
-    const int kb = s * 32 + 8 * g;
-    uint32_t wd = 0u, sw = 0u;
-    if (gn < n) {
-      wd = packed[(int64_t)gn * kwords + kb / 8];
-      sw = sign[(int64_t)gn * swords + s];
-    }
-    const uint32_t sbyte = (sw >> (8 * g)) & 0xFFu;
-    uint32_t w4[4];
+  floatx4_t acc[NMB];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t h = lut[(wd >> (4 * i)) & 15u];
-      h |= ((sbyte >> i) & 1u) << 15;
-      if (i & 1) w4[i >> 1] |= h << 16;
-      else w4[i >> 1] = h;
-    }
-    const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+  for (int b = 0; b < NMB; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  uint4 wd[2][CH];
+  uint32_t sw[2][CH];
+  uint4 xv[2][CH][NMB][4];
+  // batch i holds this wave's k blocks i*CH .. i*CH + CH - 1 (clamped to the last)
+  auto load_batch = [&](int bi, int buf) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      if (b < nmb) {
-        const int mm = b * 16 + r;
-        uint4 xv = make_uint4(0u, 0u, 0u, 0u);
-        if (mm < m) xv = *reinterpret_cast<const uint4*>(x + (int64_t)mm * k + kb);
-        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8_t, xv),
-                                                         acc[b], 0, 0, 0);
+    for (int j = 0; j < CH; ++j) {
+      const int blk = wave + kSkWaves * min(bi * CH + j, mine - 1);
+      const int kk = blk * kSkBlockK + 32 * g;
+      const int kc = kk < k ? blk * kSkBlockK : blk * kSkBlockK - 32 * g;  // stay in the row
+      wd[buf][j] = *reinterpret_cast<const uint4*>(prow + kc / 8);
+      sw[buf][j] = srow[kc / 32];
+#pragma unroll
+      for (int b = 0; b < NMB; ++b)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          xv[buf][j][b][t] = *reinterpret_cast<const uint4*>(xrow[b] + kc + 8 * t);
+    }
+  };
+  auto compute_batch = [&](int bi, int buf) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int idx = bi * CH + j;
+      if (idx < mine) {
+        const int blk = wave + kSkWaves * idx;
+        const bool live = blk * kSkBlockK + 32 * g < k;
+        const uint32_t words[4] = {wd[buf][j].x, wd[buf][j].y, wd[buf][j].z, wd[buf][j].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t w = words[t];
+          const uint32_t sb = sw[buf][j] >> (8 * t);
+          uint32_t o[4];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t h = lut[(w >> (4 * i)) & 15u] | (((sb >> i) & 1u) << 15);
+            if (i & 1) o[i >> 1] |= h << 16;
+            else o[i >> 1] = h;
+          }
+          if (!live) o[0] = o[1] = o[2] = o[3] = 0u;
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+#pragma unroll
+          for (int b = 0; b < NMB; ++b)
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a, __builtin_bit_cast(bf16x8_t, xv[buf][j][b][t]), acc[b], 0, 0, 0);
+        }
       }
+    }
+  };
+
+  const int nbatch = (mine + CH - 1) / CH;
+  if (nbatch > 0) load_batch(0, 0);
+  for (int bi = 0; bi < nbatch; bi += 2) {
+    if (bi + 1 < nbatch) load_batch(bi + 1, 1);
+    compute_batch(bi, 0);
+    if (bi + 1 < nbatch) {
+      if (bi + 2 < nbatch) load_batch(bi + 2, 0);
+      compute_batch(bi + 1, 1);
     }
   }
 
 #pragma unroll
-  for (int b = 0; b < 4; ++b)
+  for (int b = 0; b < NMB; ++b)
 #pragma unroll
     for (int j = 0; j < 4; ++j) s_red[wave][b][j][lane] = acc[b][j];
   __syncthreads();
 
   // Output (mm, row i of the block): fragment element D[i][mm % 16] of block
   // mm / 16 sits in lane 16 * (i / 4) + mm % 16, register i % 4.
-  for (int o = tid; o < kSkRows * nmb * 16; o += kSkWaves * kWave) {
+  for (int o = tid; o < kSkRows * NMB * 16; o += kSkWaves * kWave) {
     const int i = o % kSkRows;
     const int mm = o / kSkRows;
     const int b = mm / 16;
@@ -197,6 +251,7 @@ __device__ __forceinline__ uint4 sigma_order(uint4 v) {
 // 16-lane passes of ds_read_b128 conflict-free.
 __device__ __forceinline__ int a_off(int r, int c) { return r * kTK + ((c ^ ((r >> 1) & 7)) << 3); }
 
+template <bool kHalfTail>
 __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
@@ -232,22 +287,16 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
     sw_off[f] = (uint32_t)(rc - nw_c) * (uint32_t)swords * 4u;
   }
 
-  // Weights of step kt: words 4g..4g+3 and sign word g of the step.  In a final
-  // half step (k % 64 == 32) lanes g = 1 read the first half again and zero it.
+  // Weights of step kt: words 4g..4g+3 and sign word g of the step.  Steps past
+  // the end re-read the last one (every prefetch is issued unconditionally, so
+  // the wait counts stay static); in a final half step (k % 64 == 32) lanes
+  // g = 1 re-read the first half and the dequantizer zeroes their fragments.
   auto load_b = [&](int kt, uint4 (&pw)[2], uint32_t (&sw)[2]) {
-    const int kk = kt * kTK + 32 * g;
-    const int kc = min(kk, k - 32);
+    const int kc = min(min(kt, nsteps - 1) * kTK + 32 * g, k - 32);
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       pw[f] = *reinterpret_cast<const uint4*>(pbase + pw_off[f] + (uint32_t)kc / 2u);
       sw[f] = *reinterpret_cast<const uint32_t*>(sbase + sw_off[f] + (uint32_t)kc / 8u);
-    }
-    if ((k & (kTK - 1)) && kt == nsteps - 1 && kk >= k) {
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        pw[f] = make_uint4(0u, 0u, 0u, 0u);
-        sw[f] = 0u;
-      }
     }
   };
   // x of step kt: thread tid moves chunks tid + 256 i (row c/8, chunk c%8).
@@ -262,13 +311,13 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
     x_off[i] = ((uint32_t)r * (uint32_t)k + 8u * (uint32_t)(c & 7)) * 2u;
   }
   auto load_a = [&](int kt, uint4 (&xa)[8]) {
-    const bool tail = kt * kTK + kTK > k;
+    const int kc = min(kt, nsteps - 1) * kTK;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      uint32_t off = x_off[i] + (uint32_t)(kt * kTK) * 2u;
-      if (tail) {
+      uint32_t off = x_off[i] + (uint32_t)kc * 2u;
+      if constexpr (kHalfTail) {
         const int c = tid + kMfmaThreads * i;
-        if (kt * kTK + 8 * (c & 7) >= k) off -= 64u;  // step back into the row
+        if (kc + 8 * (c & 7) >= k) off -= 64u;  // step back into the row
       }
       xa[i] = *reinterpret_cast<const uint4*>(xbase + off);
     }
@@ -292,12 +341,16 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
 
   // Sub-step s of a k step: dequantize word s of both B fragments, read the
   // eight x fragments of k-blocks {s, 4 + s}.
-  auto dequant_b = [&](int s, const uint4 (&pwv)[2], const uint32_t (&swv)[2], bf16x8_t (&b)[2]) {
+  auto dequant_b = [&](int kt, int s, const uint4 (&pwv)[2], const uint32_t (&swv)[2],
+                       bf16x8_t (&b)[2]) {
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
       const uint32_t words[4] = {pwv[f].x, pwv[f].y, pwv[f].z, pwv[f].w};
       uint32_t o[4];
       dequant_word(words[s], swv[f] >> (8 * s), lut[f], o);
+      if constexpr (kHalfTail) {
+        if (kt == nsteps - 1 && g == 1) o[0] = o[1] = o[2] = o[3] = 0u;
+      }
       b[f] = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
     }
   };
@@ -323,16 +376,16 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
     load_b(0, pw, sw);
     store_a(0, xa);
   }
-  if (nsteps > 1) load_a(1, xa);
+  if (nsteps > 0) load_a(1, xa);
   __syncthreads();
 
   bf16x8_t a_buf[2][8], b_buf[2][2];
   for (int kt = 0; kt < nsteps; ++kt) {
     const int stage = kt & 1;
-    if (kt + 1 < nsteps) load_b(kt + 1, pw_next, sw_next);
+    load_b(kt + 1, pw_next, sw_next);
     const uint16_t* sa = s_a + stage * kAStage;
     read_a(sa, 0, a_buf[0]);
-    dequant_b(0, pw, sw, b_buf[0]);
+    dequant_b(kt, 0, pw, sw, b_buf[0]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
@@ -340,7 +393,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
         read_a(sa, s + 1, a_buf[nxt]);
         // the next fragments' LDS reads stay ahead of this sub-step's MFMAs
         __builtin_amdgcn_sched_barrier(0);
-        dequant_b(s + 1, pw, sw, b_buf[nxt]);
+        dequant_b(kt, s + 1, pw, sw, b_buf[nxt]);
       }
 #pragma unroll
       for (int mi = 0; mi < 8; ++mi)
@@ -348,9 +401,9 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
         for (int f = 0; f < 2; ++f)
           acc[mi][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_buf[cur][mi], b_buf[cur][f],
                                                                acc[mi][f], 0, 0, 0);
-      if (s == 0 && kt + 1 < nsteps) {
+      if (s == 0) {
         store_a(stage ^ 1, xa);
-        if (kt + 2 < nsteps) load_a(kt + 2, xa);
+        load_a(kt + 2, xa);
       }
     }
 #pragma unroll
@@ -386,13 +439,14 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32
                          const Levels& lv, float* y, void*, hipStream_t stream) {
   if (m <= kSkinnyMaxM) {
     const int64_t blocks = (n + kSkRows - 1) / kSkRows;
-    hipLaunchKernelGGL(linear_skinny, dim3((unsigned)blocks), dim3(kSkWaves * kWave), 0, stream, x,
-                       packed, sign, scale, bias, (int)m, (int)n, (int)k, lv, y);
+    auto kernel = m <= 16 ? linear_skinny<1> : (m <= 32 ? linear_skinny<2> : linear_skinny<4>);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kSkWaves * kWave), 0, stream, x, packed,
+                       sign, scale, bias, (int)m, (int)n, (int)k, lv, y);
   } else {
     const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
-    hipLaunchKernelGGL(linear_mfma, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMfmaThreads), 0,
-                       stream, x, packed, sign, scale, bias, (int)m, (int)n, (int)k, (int)tiles_m,
-                       lv, y);
+    auto kernel = (k % kTK) ? linear_mfma<true> : linear_mfma<false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMfmaThreads), 0, stream,
+                       x, packed, sign, scale, bias, (int)m, (int)n, (int)k, (int)tiles_m, lv, y);
   }
   return hipGetLastError();
 }
