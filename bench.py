@@ -9,9 +9,12 @@ x bf16 [32, 3840], alpha 0.73) unless --workload names another.
 Prints ONE JSON line.  `value` is the step's fraction of the MI355X roofline
 in percent: the sum of each kernel's ideal time (algorithmic bytes / 8 TB/s,
 or flops / 2.5 PFLOP/s for MFMA-bound shapes) over the measured step time.
-Per-kernel absolute GB/s and TFLOP/s are under "kernels".  Inputs are
-resident in HBM before timing starts; every step rotates to another set of
-input/output buffers so that the 256 MB Infinity Cache cannot serve repeats.
+The timed region is exactly --steps steps between two HIP events.  Per-kernel
+durations (under "kernels", with absolute GB/s and TFLOP/s) come from a
+second pass: 7 batches of --steps back-to-back launches of one kernel, median
+batch; the "roofline" object is the slowest kernel's.  Inputs are resident in
+HBM before timing starts; every launch rotates to another set of input/output
+buffers so that the 256 MB Infinity Cache cannot serve repeats.
 """
 from __future__ import annotations
 
@@ -46,6 +49,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for > 768 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after timing, 5 plain device copies of this many MiB (counter scaling)")
     return ap.parse_args()
 
 
@@ -194,42 +199,54 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
 
-    def step(i, ev=None):
+    def launch(kind, i):
         w, qw, d, x, y = sets[i % rot]
-        if ev is not None:
-            ev[0].record(stream)
-        opq.quantize(w, alpha, out=qw)
-        if ev is not None:
-            ev[1].record(stream)
-        opq.dequantize(qw, alpha, out=d)
-        if ev is not None:
-            ev[2].record(stream)
-        opq.linear(x, qw, alpha, out=y)
-        if ev is not None:
-            ev[3].record(stream)
+        if kind == "quantize":
+            opq.quantize(w, alpha, out=qw)
+        elif kind == "dequantize":
+            opq.dequantize(qw, alpha, out=d)
+        else:
+            opq.linear(x, qw, alpha, out=y)
+
+    kinds = ["quantize", "dequantize", "linear"]
+
+    def step(i):
+        for kind in kinds:
+            launch(kind, i)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # Timed region: exactly K steps, events only at its two ends.
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i, events[i])
+        step(args.warmup + i)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(stop) / args.steps
 
-    kinds = ["quantize", "dequantize", "linear"]
+    # Per-kernel duration: batches of K back-to-back launches of one kernel
+    # (same rotation of buffers), median over 7 batches.
     kern = {}
     ideal_total = 0.0
-    for j, kind in enumerate(kinds):
-        us = float(np.mean([ev[j].elapsed_time(ev[j + 1]) for ev in events])) * 1e3
+    for kind in kinds:
+        per = []
+        for b in range(7):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(args.steps):
+                launch(kind, b * args.steps + i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / args.steps * 1e3)
+        us = float(np.median(per))
         ideal, bound = ideal_us(kind, alg[kind], m)
         ideal_total += ideal
         a = alg[kind]
@@ -240,6 +257,15 @@ def main():
         if a["flops"]:
             rec["TFLOPs"] = round(a["flops"] / (us * 1e-6) / 1e12, 2)
         kern[kind] = rec
+
+    if args.copy_mib:
+        # A plain device copy of known size, for scaling the HBM byte counters.
+        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     dom = max(kinds, key=lambda kk: kern[kk]["us"])
     dk = kern[dom]
@@ -272,6 +298,7 @@ def main():
                    "step": "quantize -> dequantize -> linear"},
         "roofline": roof,
         "kernels": kern,
+        "kernels_sum_us": round(sum(kk["us"] for kk in kern.values()), 3),
         "wall_s": round(wall, 3),
     }
     if not args.no_cpu_baseline:

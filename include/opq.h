@@ -27,10 +27,11 @@
  *   - matrices are row-major and dense (row stride = number of columns);
  *   - device pointers are memory of the current HIP device; host pointers are
  *     marked as such;
- *   - the caller owns every buffer; the library allocates nothing, frees
- *     nothing and synchronises nothing; its only global state is a
- *     mutex-guarded memo of the per-alpha host tables, so calls are reentrant
- *     and thread-safe; outputs must not overlap inputs;
+ *   - the caller owns every buffer (scratch comes in as a workspace argument);
+ *     the library allocates nothing, frees nothing and synchronises nothing;
+ *     its only global state is a mutex-guarded memo of the per-alpha host
+ *     tables, so calls are reentrant and thread-safe; outputs must not
+ *     overlap inputs;
  *   - `stream` is a hipStream_t (NULL = the default stream); work is enqueued
  *     on it and the call returns at once; faults inside kernels show up at the
  *     caller's next synchronisation;
@@ -39,7 +40,8 @@
  *   - arguments are checked before anything is enqueued, in this order:
  *     null pointers (OPQ_ERR_NULL), shapes (OPQ_ERR_SHAPE), alpha
  *     (OPQ_ERR_ALPHA), 16-byte alignment of every array (OPQ_ERR_ALIGN),
- *     dtype codes (OPQ_ERR_DTYPE); with an error nothing is enqueued;
+ *     dtype codes (OPQ_ERR_DTYPE), workspace size (OPQ_ERR_WORKSPACE);
+ *     with an error nothing is enqueued;
  *   - n == 0 or m == 0 is a valid empty call (OPQ_OK, nothing enqueued);
  *   - k must be a multiple of 32 (one sign word); n, m are free;
  *   - alpha must be finite and > 0, and every call on one set of weights must
@@ -56,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OPQ_ABI_VERSION 1
+#define OPQ_ABI_VERSION 2
 
 typedef enum {
   OPQ_OK = 0,
@@ -114,14 +116,17 @@ int opq_quantize(const void* w, int w_dtype, int64_t n, int64_t k, float alpha,
  *   packed, sign, scale  device, as written by opq_quantize
  *   w_out   device out, [n][k] bfloat16: bf16(G_q * scale[n]) with the sign
  *           applied; code 0 gives +0.0
- * Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN, OPQ_ERR_HIP.
+ * k <= 65536.  Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN,
+ * OPQ_ERR_UNSUPPORTED, OPQ_ERR_HIP.
  */
 int opq_dequantize(const uint32_t* packed, const uint32_t* sign, const float* scale,
                    int64_t n, int64_t k, float alpha, uint16_t* w_out, void* stream);
 
 /*
  * Bytes of device workspace opq_linear needs for this shape (0 means none;
- * the workspace pointer may then be NULL).
+ * the workspace pointer may then be NULL).  The present kernels reduce every
+ * sum inside one block and return 0 for every shape; callers that size the
+ * workspace with this function keep working if a shape ever needs one.
  */
 size_t opq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
@@ -133,15 +138,23 @@ size_t opq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *   x       device, [m][k] bfloat16 activations
  *   packed, sign, scale  device, as written by opq_quantize for W[n][k]
  *   bias    device, [n] float32, or NULL for none
- *   y       device out, [m][n] float32
+ *   y       device out, [m][n] of float32 (y_dtype OPQ_F32) or bfloat16
+ *           (OPQ_BF16: the float32 result rounded to nearest even)
  *   workspace, workspace_bytes  device scratch of at least
- *           opq_linear_workspace_bytes(m, n, k) bytes (NULL when that is 0)
+ *           opq_linear_workspace_bytes(m, n, k) bytes (NULL when that is 0).
+ *           It must be zero-filled before its first use.  A call puts back
+ *           to zero, before its work ends, every part that has to start at
+ *           zero, so one buffer serves any number of calls (of any shape) in
+ *           one stream.  Calls that may run at the same time (other streams)
+ *           need buffers of their own.
+ * The sum order is fixed for a given shape, so results are reproducible bit
+ * for bit.  k <= 65536.
  * Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN,
- * OPQ_ERR_WORKSPACE, OPQ_ERR_HIP.
+ * OPQ_ERR_DTYPE, OPQ_ERR_WORKSPACE, OPQ_ERR_UNSUPPORTED, OPQ_ERR_HIP.
  */
 int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
-               float alpha, float* y, void* workspace, size_t workspace_bytes,
+               float alpha, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
                void* stream);
 
 #ifdef __cplusplus

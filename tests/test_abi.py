@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.opq_abi_version() == 1
+    assert lib.opq_abi_version() == opq.ABI_VERSION == 2
     for s in range(9):
         assert opq.status_str(s) and opq.status_str(s) != "unknown status"
     assert opq.status_str(99) == "unknown status"
@@ -108,12 +108,12 @@ def test_dequantize_argument_checks(lib):
 def test_linear_argument_checks(lib):
     f = lib.opq_linear
     args = dict(x=FAKE, p=FAKE, s=FAKE, sc=FAKE, b=None, m=8, n=16, k=64, a=0.73, y=FAKE,
-                ws=None, wsb=0)
+                yd=0, ws=None, wsb=0)
 
     def call(**kw):
         a = dict(args, **kw)
         return f(a["x"], a["p"], a["s"], a["sc"], a["b"], a["m"], a["n"], a["k"], a["a"], a["y"],
-                 a["ws"], a["wsb"], None)
+                 a["yd"], a["ws"], a["wsb"], None)
 
     assert call(x=None) == NULL
     assert call(y=None) == NULL
@@ -123,9 +123,20 @@ def test_linear_argument_checks(lib):
     assert call(b=MISALIGNED) == ALIGN
     assert call(x=MISALIGNED) == ALIGN
     assert call(ws=MISALIGNED) == ALIGN
+    assert call(yd=7) == DTYPE
+    assert call(yd=7, y=MISALIGNED) == ALIGN          # alignment is checked before dtype
     assert call(m=0) == OK
     assert call(n=0) == OK
+    assert call(m=0, yd=1) == OK
     assert lib.opq_linear_workspace_bytes(8, 16, 64) == opq.linear_workspace_bytes(8, 16, 64)
+
+
+def test_linear_workspace_sizes(lib):
+    # every shape is reduced inside its blocks: no workspace
+    ws = lib.opq_linear_workspace_bytes
+    for m, n, k in [(1, 3840, 3840), (32, 3840, 3840), (64, 3840, 10240), (65, 3840, 3840),
+                    (4096, 11520, 3840), (0, 3840, 3840), (32, 0, 3840), (-1, 3840, 3840)]:
+        assert ws(m, n, k) == 0
 
 
 def test_binding_refuses_host_tensors():

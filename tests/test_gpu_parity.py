@@ -264,6 +264,55 @@ def test_linear_one_hot_rows_pick_weights(gpu_lib):
         assert torch.equal(y, d.cpu().float()[:, :m].T.contiguous())
 
 
+@pytest.mark.parametrize("m,n,k", [(1, 200, 4096), (17, 64, 8192), (32, 130, 2080),
+                                   (48, 1000, 1024), (64, 64, 65536), (64, 4000, 96)])
+def test_linear_skinny_long_k(gpu_lib, m, n, k):
+    """Skinny shapes with many k blocks per wave, ragged n and m, k up to the limit."""
+    opq = gpu_lib
+    w_vals, w_dev = weight_tensor(WL.student_t(700 + n, (n, k)), "bf16")
+    qw = opq.quantize(w_dev, 0.73)
+    ref = O.quantize(w_vals, 0.73)
+    torch.cuda.synchronize()
+    assert_quant_equal(qw, ref)
+    xt = to_bf16(WL.normal(800 + m, (m, k)))
+    gy = Guarded((m, n), torch.float32)
+    opq.linear(xt.to(DEV), qw, 0.73, out=gy.t)
+    torch.cuda.synchronize()
+    gy.check()
+    y_ref = O.linear(bf16_bits(xt), O.dequantize(*ref, 0.73))
+    assert_linear_close(gy.t.cpu().numpy(), y_ref)
+
+
+def _bf16_rne_bits(y32):
+    b = y32.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("m,n,k", [(8, 300, 544), (32, 3840, 3840), (200, 300, 544)])
+def test_linear_repeatable_and_bf16_out(gpu_lib, m, n, k):
+    """Same call twice gives the same bits (fixed sum order; a workspace passed
+    in stays reusable), and bfloat16 output is the float32 output rounded to
+    nearest even."""
+    opq = gpu_lib
+    _, w_dev = weight_tensor(WL.student_t(900 + n, (n, k)), "bf16")
+    qw = opq.quantize(w_dev, 0.73)
+    x = to_bf16(WL.normal(901 + m, (m, k))).to(DEV)
+    bias = torch.from_numpy(WL.normal(902, (n,), 0.5)).to(DEV)
+    need = max(opq.linear_workspace_bytes(m, n, k), opq.linear_workspace_bytes(5, n, k), 16)
+    ws = torch.zeros(need, dtype=torch.uint8, device=DEV)
+    y1 = opq.linear(x, qw, 0.73, bias=bias, workspace=ws).cpu().numpy()
+    # another shape through the same workspace in between
+    x_small = to_bf16(WL.normal(903, (5, k))).to(DEV)
+    opq.linear(x_small, qw, 0.73, workspace=ws)
+    y2 = opq.linear(x, qw, 0.73, bias=bias, workspace=ws).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    gb = Guarded((m, n), torch.bfloat16)
+    opq.linear(x, qw, 0.73, bias=bias, out=gb.t, workspace=ws)
+    torch.cuda.synchronize()
+    gb.check()
+    assert np.array_equal(bf16_bits(gb.t.cpu()), _bf16_rne_bits(y1))
+
+
 # ------------------------------------------------------------------ full-size configs
 
 def _sample_rows(n, count, seed):

@@ -3,183 +3,23 @@
 // OPQLinear layer of the file list, decoded as in "技术细节 / 推理解码").
 //
 // W' is never written to HBM.  Each block builds the sixteen-entry table
-// L_n[q] = bf16(G_q * m_n) for its weight rows in LDS, turns packed codes and
-// sign bits into bfloat16 on chip, and feeds bf16 MFMA with fp32 accumulation.
-// The table holds the same values opq_dequantize writes; the scale is never
-// applied after the product.
+// L_n[q] = bf16(G_q * m_n) of its weight rows, turns packed codes and sign
+// bits into bfloat16 in registers (byte-plane lookups with v_perm), and feeds
+// bf16 MFMA with fp32 accumulation.  The table holds the same values
+// opq_dequantize writes; the scale is never applied after the product.
 //
 // Two paths:
-//  * m <= kSkinnyMaxM: weight-streaming (HBM-bound).  A block owns 16 weight
-//    rows and all of k; its waves split k and reduce through LDS.  W' is the
-//    A operand of v_mfma_f32_16x16x32_bf16 (one packed word = a lane's eight
-//    k values), x^T the B operand.
-//  * otherwise: 256x256 output tiles with v_mfma_f32_32x32x16_bf16; weights
-//    dequantized in registers, x staged through LDS (details below).
+//  * m <= kSkinnyMaxM: weight streaming, bound by HBM.  Blocks of 64 weight
+//    rows x one k slice; slices of a row group are summed by the block that
+//    finishes last (details below).
+//  * otherwise: 256x256 output tiles with v_mfma_f32_32x32x16_bf16; x staged
+//    through LDS (details below).
 #include "device_common.hpp"
 
 namespace opq {
 namespace {
 
-// ---------------------------------------------------------------- skinny path
-//
-// m <= 64: the product is bound by streaming the packed weights.  A block owns
-// 16 weight rows and all of k; k is cut into 128-wide blocks dealt round-robin
-// to the block's 8 waves.  W' is the A operand of v_mfma_f32_16x16x32_bf16 and
-// x^T the B operand.  For one 128-wide k block, lane l (row r = l%16, group
-// g = l/16) loads packed words 4g..4g+3 of row r (16 bytes, so four lanes read
-// 64 contiguous bytes of the row), sign word g, and x[.][32g .. 32g + 31] for
-// its x rows; sub-step t then contracts the k-blocks {t, 4 + t, 8 + t, 12 + t}
-// (units of 8), lane g supplying word t of its four.  A wave issues the loads
-// of up to CH of its k blocks at once, one batch ahead of use.  Codes are
-// looked up in the block's 16 x 16 bf16 table in LDS; the waves' partial sums
-// meet in LDS at the end.
-
-constexpr int kSkinnyMaxM = 64;
-constexpr int kSkRows = 16;    // weight rows per block
-constexpr int kSkWaves = 8;    // waves splitting k
-constexpr int kSkBlockK = 128; // k per block step
-
-template <int NMB>             // 16-row blocks of x: 1, 2 or 4
-__global__ __launch_bounds__(kSkWaves * kWave) void linear_skinny(
-    const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
-    const uint32_t* __restrict__ sign, const float* __restrict__ scale,
-    const float* __restrict__ bias, int m, int n, int k, Levels lv, float* __restrict__ y) {
-  constexpr int CH = NMB == 4 ? 1 : (NMB == 2 ? 2 : 3);   // k blocks per load batch
-  __shared__ uint16_t s_lut[kSkRows * 16];
-  __shared__ float s_red[kSkWaves][NMB][4][kWave];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  const int n0 = blockIdx.x * kSkRows;
-
-  if (tid < kSkRows * 16) {
-    const int gn = min(n0 + (tid >> 4), n - 1);
-    s_lut[tid] = (uint16_t)lut_entry(lv, tid & 15, scale[gn]);
-  }
-  __syncthreads();
-
-  const int r = lane & 15;        // weight row of this lane's A fragment
-  const int g = lane >> 4;        // 32-wide k group within a 128-wide block
-  const int kwords = k / 8, swords = k / 32;
-  const int rc = min(n0 + r, n - 1);
-  const uint32_t* prow = packed + (int64_t)rc * kwords + 4 * g;
-  const uint32_t* srow = sign + (int64_t)rc * swords + g;
-  const uint16_t* lut = s_lut + r * 16;
-  const uint16_t* xrow[NMB];
-#pragma unroll
-  for (int b = 0; b < NMB; ++b) xrow[b] = x + (int64_t)min(b * 16 + r, m - 1) * k + 32 * g;
-
-  // k blocks of this wave: wave, wave + 8, ...; a half block (k % 128 == 64 or
-  // 32) lets lanes whose group starts past k read group 0 again and drop it.
-  const int nblk = (k + kSkBlockK - 1) / kSkBlockK;
-  const int mine = nblk > wave ? (nblk - 1 - wave) / kSkWaves + 1 : 0;
-
-  floatx4_t acc[NMB];
-#pragma unroll
-  for (int b = 0; b < NMB; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 wd[2][CH];
-  uint32_t sw[2][CH];
-  uint4 xv[2][CH][NMB][4];
-  // batch i holds this wave's k blocks i*CH .. i*CH + CH - 1 (clamped to the last)
-  auto load_batch = [&](int bi, int buf) {
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int blk = wave + kSkWaves * min(bi * CH + j, mine - 1);
-      const int kk = blk * kSkBlockK + 32 * g;
-      const int kc = kk < k ? blk * kSkBlockK : blk * kSkBlockK - 32 * g;  // stay in the row
-      wd[buf][j] = *reinterpret_cast<const uint4*>(prow + kc / 8);
-      sw[buf][j] = srow[kc / 32];
-#pragma unroll
-      for (int b = 0; b < NMB; ++b)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          xv[buf][j][b][t] = *reinterpret_cast<const uint4*>(xrow[b] + kc + 8 * t);
-    }
-  };
-  auto compute_batch = [&](int bi, int buf) {
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int idx = bi * CH + j;
-      if (idx < mine) {
-        const int blk = wave + kSkWaves * idx;
-        const bool live = blk * kSkBlockK + 32 * g < k;
-        const uint32_t words[4] = {wd[buf][j].x, wd[buf][j].y, wd[buf][j].z, wd[buf][j].w};
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint32_t w = words[t];
-          const uint32_t sb = sw[buf][j] >> (8 * t);
-          uint32_t o[4];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t h = lut[(w >> (4 * i)) & 15u] | (((sb >> i) & 1u) << 15);
-            if (i & 1) o[i >> 1] |= h << 16;
-            else o[i >> 1] = h;
-          }
-          if (!live) o[0] = o[1] = o[2] = o[3] = 0u;
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-#pragma unroll
-          for (int b = 0; b < NMB; ++b)
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                a, __builtin_bit_cast(bf16x8_t, xv[buf][j][b][t]), acc[b], 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  const int nbatch = (mine + CH - 1) / CH;
-  if (nbatch > 0) load_batch(0, 0);
-  for (int bi = 0; bi < nbatch; bi += 2) {
-    if (bi + 1 < nbatch) load_batch(bi + 1, 1);
-    compute_batch(bi, 0);
-    if (bi + 1 < nbatch) {
-      if (bi + 2 < nbatch) load_batch(bi + 2, 0);
-      compute_batch(bi + 1, 1);
-    }
-  }
-
-#pragma unroll
-  for (int b = 0; b < NMB; ++b)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s_red[wave][b][j][lane] = acc[b][j];
-  __syncthreads();
-
-  // Output (mm, row i of the block): fragment element D[i][mm % 16] of block
-  // mm / 16 sits in lane 16 * (i / 4) + mm % 16, register i % 4.
-  for (int o = tid; o < kSkRows * NMB * 16; o += kSkWaves * kWave) {
-    const int i = o % kSkRows;
-    const int mm = o / kSkRows;
-    const int b = mm / 16;
-    const int ln = 16 * (i / 4) + (mm % 16);
-    float sum = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kSkWaves; ++w) sum += s_red[w][b][i % 4][ln];
-    const int gcol = n0 + i;
-    if (mm < m && gcol < n) y[(int64_t)mm * n + gcol] = sum + (bias ? bias[gcol] : 0.0f);
-  }
-}
-
-// ---------------------------------------------------------------- tiled MFMA path
-//
-// Block tile 256 (x rows) x 256 (weight rows), k steps of 64, four waves.
-// Wave w owns weight rows [64w, 64w + 64) of the tile and all 256 x rows:
-// 8 x 2 accumulators of 32x32 (256 fp32 per lane, held in AGPRs).
-//
-// Weights never pass through LDS: each lane loads the packed words of its two
-// weight rows straight into VGPRs, in the layout of the MFMA B operand (one
-// packed word = the eight k values a lane supplies), and dequantizes them with
-// its rows' tables held as byte planes in registers (v_perm lookups).  Lanes
-// 0..31 take words 0..3 of the 8-word k step and lanes 32..63 words 4..7, so
-// sub-step s contracts k-blocks {s, 4 + s}; the x fragments read from LDS use
-// the same k-blocks.  Within a k-block the dequantizer emits bf16 pairs in the
-// order (k0,k2) (k4,k6) (k1,k3) (k5,k7); x is stored to LDS in that order too.
-// Only x is staged in LDS (two stages, rows XOR-swizzled by 16-byte chunk).
-
-constexpr int kTM = 256, kTN = 256, kTK = 64;
-constexpr int kMfmaThreads = 256;
-constexpr int kAChunks = kTK / 8;                  // 16-byte chunks per LDS row
-constexpr int kAStage = kTM * kTK;                 // bf16 per stage
+// ---------------------------------------------------------------- dequantizer
 
 // Byte planes of a row's sixteen bf16 table entries: lo[i] holds the low bytes
 // of entries 4i..4i+3, hi[i] the high bytes.
@@ -245,6 +85,219 @@ __device__ __forceinline__ uint4 sigma_order(uint4 v) {
   return r;
 }
 
+// Output element (row i of a 16-row weight fragment, column c of a 16-column x
+// fragment) of v_mfma_f32_16x16x32_bf16 sits in lane 16 * (i / 4) + c,
+// register i % 4.
+__device__ __forceinline__ void store_y(void* y, bool y_bf16, int64_t at, float v) {
+  if (y_bf16) static_cast<uint16_t*>(y)[at] = (uint16_t)bf16_rne(v);
+  else static_cast<float*>(y)[at] = v;
+}
+
+// ---------------------------------------------------------------- skinny path
+//
+// m <= 64: the product is bound by streaming the packed weights (0.625 bytes
+// per weight against 2 m flops).  A block owns 16 weight rows (one fragment of
+// v_mfma_f32_16x16x32_bf16, W' the A operand, x^T the B operand) and all of k;
+// its eight waves take the 128-wide k blocks in turn and meet in LDS at the
+// end, so no partial sums leave the block.
+//
+// For one 128-wide k block, lane l (row r = l % 16, group g = l / 16) loads
+// packed words 4g..4g+3 of its row (four groups read 64 contiguous bytes of
+// the row), sign word g, and x[.][32g .. 32g+31] of its x rows.  Sub-step t
+// contracts the 8-wide k chunks {t, 4+t, 8+t, 12+t}, group g supplying word t
+// of its four; x chunks are put in the dequantizer's pair order so both
+// operands list k the same way.
+
+constexpr int kSkinnyMaxM = 64;
+constexpr int kSkRows = 16;                     // weight rows per block
+constexpr int kSkFrags = kSkRows / 16;          // 16-row MFMA fragments per block
+constexpr int kSkWaves = 8;
+constexpr int kSkThreads = kSkWaves * kWave;
+constexpr int kSkBlockK = 128;                  // k per wave step
+
+template <int NMB>
+__global__ __launch_bounds__(kSkThreads) void linear_skinny(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
+    const uint32_t* __restrict__ sign, const float* __restrict__ scale,
+    const float* __restrict__ bias, int m, int n, int k, Levels lv, void* __restrict__ y,
+    int y_bf16) {
+  constexpr int CH = NMB == 4 ? 1 : 2;                  // k blocks per load batch
+  constexpr int kOut = kSkFrags * NMB * 4 * kWave;      // block outputs, accumulator order
+  __shared__ uint32_t s_lut[kSkRows][8];
+  __shared__ float s_red[kSkWaves][kOut];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int n0 = blockIdx.x * kSkRows;
+  const int r = lane & 15, g = lane >> 4;
+  const int kwords = k / 8, swords = k / 32;
+
+  // This wave's k blocks: wave, wave + kSkWaves, ...
+  const int nkb = (k + kSkBlockK - 1) / kSkBlockK;
+  const int mine = nkb > wave ? (nkb - 1 - wave) / kSkWaves + 1 : 0;
+
+  // Byte offsets from uniform bases.  Weight rows past n read row n - 1 and x
+  // rows past m read row m - 1; neither is stored.
+  const int n0c = min(n0, n - 1);
+  const char* pbase = reinterpret_cast<const char*>(packed + (int64_t)n0c * kwords);
+  const char* sbase = reinterpret_cast<const char*>(sign + (int64_t)n0c * swords);
+  uint32_t p_off[kSkFrags], s_off[kSkFrags];
+#pragma unroll
+  for (int f = 0; f < kSkFrags; ++f) {
+    const uint32_t rel = (uint32_t)(min(n0 + 16 * f + r, n - 1) - n0c);
+    p_off[f] = rel * (uint32_t)kwords * 4u;
+    s_off[f] = rel * (uint32_t)swords * 4u;
+  }
+  const char* xbase = reinterpret_cast<const char*>(x);
+  uint32_t x_off[NMB];
+#pragma unroll
+  for (int b = 0; b < NMB; ++b) x_off[b] = (uint32_t)min(b * 16 + r, m - 1) * (uint32_t)k * 2u;
+
+  uint4 wd[2][CH][kSkFrags];
+  uint32_t sw[2][CH][kSkFrags];
+  uint4 xv[2][CH][NMB][4];
+  // Batch bi holds this wave's k blocks bi*CH .. bi*CH + CH - 1 (clamped to the
+  // last).  In a final part block (k % 128 != 0) groups past k re-read group 0
+  // of the block and the dequantizer zeroes their fragments.
+  auto load_batch = [&](int bi, int buf) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int blk = wave + kSkWaves * min(bi * CH + j, mine - 1);
+      const int kk = blk * kSkBlockK + 32 * g;
+      const uint32_t ke = (uint32_t)(kk < k ? kk : blk * kSkBlockK);
+#pragma unroll
+      for (int f = 0; f < kSkFrags; ++f) {
+        wd[buf][j][f] = *reinterpret_cast<const uint4*>(pbase + p_off[f] + ke / 2u);
+        sw[buf][j][f] = *reinterpret_cast<const uint32_t*>(sbase + s_off[f] + ke / 8u);
+      }
+#pragma unroll
+      for (int b = 0; b < NMB; ++b)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          xv[buf][j][b][t] = *reinterpret_cast<const uint4*>(xbase + x_off[b] + (ke + 8u * t) * 2u);
+    }
+  };
+
+  const int nbatch = (mine + CH - 1) / CH;
+  if (nbatch > 0) load_batch(0, 0);
+  if (nbatch > 1) load_batch(1, 1);
+
+  // Byte planes of the block's 64 row tables, four entries per thread: thread
+  // t makes entries 4(t%4) .. 4(t%4)+3 of row t/4.
+  if (tid < kSkRows * 4) {
+    const int row = tid >> 2, j = tid & 3;
+    const float mr = scale[min(n0 + row, n - 1)];
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t e = lut_entry(lv, 4 * j + i, mr);
+      lo |= (e & 0xFFu) << (8 * i);
+      hi |= (e >> 8) << (8 * i);
+    }
+    s_lut[row][j] = lo;
+    s_lut[row][4 + j] = hi;
+  }
+  __syncthreads();
+  RowLut lut[kSkFrags];
+#pragma unroll
+  for (int f = 0; f < kSkFrags; ++f) {
+    const uint4 lo = *reinterpret_cast<const uint4*>(&s_lut[16 * f + r][0]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(&s_lut[16 * f + r][4]);
+    lut[f].lo[0] = lo.x; lut[f].lo[1] = lo.y; lut[f].lo[2] = lo.z; lut[f].lo[3] = lo.w;
+    lut[f].hi[0] = hi.x; lut[f].hi[1] = hi.y; lut[f].hi[2] = hi.z; lut[f].hi[3] = hi.w;
+  }
+
+  floatx4_t acc[kSkFrags][NMB];
+#pragma unroll
+  for (int f = 0; f < kSkFrags; ++f)
+#pragma unroll
+    for (int b = 0; b < NMB; ++b) acc[f][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  auto compute_batch = [&](int bi, int buf) {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int idx = bi * CH + j;
+      if (idx < mine) {
+        const int blk = wave + kSkWaves * idx;
+        const bool live = blk * kSkBlockK + 32 * g < k;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          bf16x8_t xs[NMB];
+#pragma unroll
+          for (int b = 0; b < NMB; ++b)
+            xs[b] = __builtin_bit_cast(bf16x8_t, sigma_order(xv[buf][j][b][t]));
+#pragma unroll
+          for (int f = 0; f < kSkFrags; ++f) {
+            const uint4 wv = wd[buf][j][f];
+            const uint32_t word = t == 0 ? wv.x : (t == 1 ? wv.y : (t == 2 ? wv.z : wv.w));
+            uint32_t o[4];
+            dequant_word(word, sw[buf][j][f] >> (8 * t), lut[f], o);
+            if (!live) o[0] = o[1] = o[2] = o[3] = 0u;
+            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+#pragma unroll
+            for (int b = 0; b < NMB; ++b)
+              acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xs[b], acc[f][b], 0, 0, 0);
+          }
+        }
+      }
+    }
+  };
+
+  for (int bi = 0; bi < nbatch; bi += 2) {
+    compute_batch(bi, 0);
+    if (bi + 2 < nbatch) load_batch(bi + 2, 0);
+    if (bi + 1 < nbatch) {
+      compute_batch(bi + 1, 1);
+      if (bi + 3 < nbatch) load_batch(bi + 3, 1);
+    }
+  }
+
+  // Waves meet in LDS; element o = ((f * NMB + b) * 4 + e) * 64 + lane.
+#pragma unroll
+  for (int f = 0; f < kSkFrags; ++f)
+#pragma unroll
+    for (int b = 0; b < NMB; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_red[wave][((f * NMB + b) * 4 + e) * kWave + lane] = acc[f][b][e];
+  __syncthreads();
+  // Output (x row mm, weight row i): fragment f = i / 16, register (i % 16) % 4
+  // of lane 16 * ((i % 16) / 4) + mm % 16; waves summed in a fixed order.
+  for (int o = tid; o < kSkRows * NMB * 16; o += kSkThreads) {
+    const int i = o % kSkRows, mm = o / kSkRows;
+    const int gcol = n0 + i;
+    if (mm < m && gcol < n) {
+      const int f = i / 16, ii = i % 16, b = mm / 16;
+      const int src = ((f * NMB + b) * 4 + (ii & 3)) * kWave + 16 * (ii >> 2) + (mm & 15);
+      float val = s_red[0][src];
+#pragma unroll
+      for (int w = 1; w < kSkWaves; ++w) val += s_red[w][src];
+      store_y(y, y_bf16, (int64_t)mm * n + gcol, val + (bias ? bias[gcol] : 0.0f));
+    }
+  }
+}
+
+// ---------------------------------------------------------------- tiled MFMA path
+//
+// Block tile 256 (x rows) x 256 (weight rows), k steps of 64, four waves.
+// Wave w owns weight rows [64w, 64w + 64) of the tile and all 256 x rows:
+// 8 x 2 accumulators of 32x32 (256 fp32 per lane, held in AGPRs).
+//
+// Weights never pass through LDS: each lane loads the packed words of its two
+// weight rows straight into VGPRs, in the layout of the MFMA B operand (one
+// packed word = the eight k values a lane supplies), and dequantizes them with
+// its rows' tables held as byte planes in registers (v_perm lookups).  Lanes
+// 0..31 take words 0..3 of the 8-word k step and lanes 32..63 words 4..7, so
+// sub-step s contracts k-blocks {s, 4 + s}; the x fragments read from LDS use
+// the same k-blocks.  Within a k-block the dequantizer emits bf16 pairs in the
+// order (k0,k2) (k4,k6) (k1,k3) (k5,k7); x is stored to LDS in that order too.
+// Only x is staged in LDS (two stages, rows XOR-swizzled by 16-byte chunk).
+
+constexpr int kTM = 256, kTN = 256, kTK = 64;
+constexpr int kMfmaThreads = 256;
+constexpr int kAChunks = kTK / 8;                  // 16-byte chunks per LDS row
+constexpr int kAStage = kTM * kTK;                 // bf16 per stage
+
 // LDS element offset of 16-byte chunk c of tile row r.  A row is 128 bytes
 // (32 banks), so rows alternate bank halves; XOR-ing the chunk with bits 1..3
 // of the row spreads any 16 consecutive rows over all 64 banks, which keeps the
@@ -256,7 +309,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
     const float* __restrict__ bias, int m, int n, int k, int tiles_m, Levels lv,
-    float* __restrict__ y) {
+    void* __restrict__ y, int y_bf16) {
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kAStage];
 
   const int tid = threadIdx.x;
@@ -425,7 +478,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-        if (row < m && col < n) y[(int64_t)row * n + col] = acc[mi][f][e] + bv;
+        if (row < m && col < n) store_y(y, y_bf16, (int64_t)row * n + col, acc[mi][f][e] + bv);
       }
   }
 }
@@ -436,17 +489,18 @@ size_t linear_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
 hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                          const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
-                         const Levels& lv, float* y, void*, hipStream_t stream) {
+                         const Levels& lv, void* y, bool y_bf16, void*, hipStream_t stream) {
   if (m <= kSkinnyMaxM) {
     const int64_t blocks = (n + kSkRows - 1) / kSkRows;
     auto kernel = m <= 16 ? linear_skinny<1> : (m <= 32 ? linear_skinny<2> : linear_skinny<4>);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kSkWaves * kWave), 0, stream, x, packed,
-                       sign, scale, bias, (int)m, (int)n, (int)k, lv, y);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kSkThreads), 0, stream, x, packed,
+                       sign, scale, bias, (int)m, (int)n, (int)k, lv, y, (int)y_bf16);
   } else {
     const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
     auto kernel = (k % kTK) ? linear_mfma<true> : linear_mfma<false>;
     hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMfmaThreads), 0, stream,
-                       x, packed, sign, scale, bias, (int)m, (int)n, (int)k, (int)tiles_m, lv, y);
+                       x, packed, sign, scale, bias, (int)m, (int)n, (int)k, (int)tiles_m, lv, y,
+                       (int)y_bf16);
   }
   return hipGetLastError();
 }

@@ -94,8 +94,8 @@ size_t opq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
 }
 
 int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign, const float* scale,
-               const float* bias, int64_t m, int64_t n, int64_t k, float alpha, float* y,
-               void* workspace, size_t workspace_bytes, void* stream) {
+               const float* bias, int64_t m, int64_t n, int64_t k, float alpha, void* y,
+               int y_dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if ((m > 0 && k > 0 && !x) || (n > 0 && k > 0 && (!packed || !sign)) || (n > 0 && !scale) ||
       (m > 0 && n > 0 && !y))
     return OPQ_ERR_NULL;
@@ -104,13 +104,15 @@ int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign, 
   if (!aligned16(x) || !aligned16(packed) || !aligned16(sign) || !aligned16(scale) ||
       !aligned16(y) || (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)))
     return OPQ_ERR_ALIGN;
+  if (y_dtype != OPQ_F32 && y_dtype != OPQ_BF16) return OPQ_ERR_DTYPE;
   const size_t need = opq::linear_workspace_bytes(m, n, k);
   if (workspace_bytes < need || (need > 0 && !workspace)) return OPQ_ERR_WORKSPACE;
   if (m == 0 || n == 0) return OPQ_OK;
   if (k > kMaxK) return OPQ_ERR_UNSUPPORTED;
   opq::Levels lv;
   opq::levels(alpha, lv.g);
-  return hip_status(opq::launch_linear(x, packed, sign, scale, bias, m, n, k, lv, y, workspace,
+  return hip_status(opq::launch_linear(x, packed, sign, scale, bias, m, n, k, lv, y,
+                                       y_dtype == OPQ_BF16, workspace,
                                        static_cast<hipStream_t>(stream)));
 }
 

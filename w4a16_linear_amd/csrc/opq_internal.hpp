@@ -37,6 +37,7 @@ hipError_t launch_dequantize(const uint32_t* packed, const uint32_t* sign, const
 size_t linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
 hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                          const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
-                         const Levels& lv, float* y, void* workspace, hipStream_t stream);
+                         const Levels& lv, void* y, bool y_bf16, void* workspace,
+                         hipStream_t stream);
 
 }  // namespace opq

@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libopq.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 OPQ_F32 = 0
 OPQ_BF16 = 1
@@ -40,8 +40,8 @@ _SIGNATURES = {
     "opq_linear": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
-                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
-                                  ctypes.c_void_p]),
+                                  ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -164,9 +164,35 @@ def linear_workspace_bytes(m: int, n: int, k: int) -> int:
     return int(load().opq_linear_workspace_bytes(m, n, k))
 
 
+# One zero-filled workspace per device, grown on demand.  opq_linear puts the
+# parts that must start at zero back to zero, so calls in one stream can share
+# it; calls that may overlap (other streams) must pass workspaces of their own.
+_workspaces: dict = {}
+
+
+def shared_workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
+    """The per-device zero-filled workspace, at least `nbytes` long (None for 0)."""
+    if nbytes <= 0:
+        return None
+    key = torch.device(device).index if torch.device(device).index is not None \
+        else torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=torch.device("cuda", key))
+        _workspaces[key] = ws
+    return ws
+
+
 def linear(x: torch.Tensor, qw: QuantizedWeight, alpha: float, bias: Optional[torch.Tensor] = None,
-           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y[m, n] = x[m, k] W'^T (+ bias) in float32, W' made on chip from qw."""
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """y[m, n] = x[m, k] W'^T (+ bias), W' made on chip from qw.
+
+    out_dtype is torch.float32 or torch.bfloat16 (the float32 result rounded
+    to nearest even).  `workspace`, when given, must be a zero-filled uint8
+    device tensor of at least linear_workspace_bytes(m, n, k) bytes; by default
+    the per-device shared one is used.
+    """
     _need_cuda("x", x, torch.bfloat16, 2)
     m, k = x.shape
     n, kw = qw.shape
@@ -175,13 +201,24 @@ def linear(x: torch.Tensor, qw: QuantizedWeight, alpha: float, bias: Optional[to
     if bias is not None:
         _need_cuda("bias", bias, torch.float32, 1)
     if out is None:
-        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    if out.dtype == torch.float32:
+        y_dtype = OPQ_F32
+    elif out.dtype == torch.bfloat16:
+        y_dtype = OPQ_BF16
+    else:
+        raise ValueError(f"out must be float32 or bfloat16, got {out.dtype}")
+    _need_cuda("out", out, out.dtype, 2)
+    if tuple(out.shape) != (m, n):
+        raise ValueError(f"out must have shape {(m, n)}, got {tuple(out.shape)}")
     need = linear_workspace_bytes(m, n, k)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    if workspace is None:
+        workspace = shared_workspace(x.device, need)
+    elif not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous CUDA (HIP) tensor")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = load().opq_linear(_ptr(x), _ptr(qw.packed), _ptr(qw.sign), _ptr(qw.scale), _ptr(bias),
-                           m, n, k, alpha, _ptr(out), _ptr(workspace), ws_bytes,
+                           m, n, k, alpha, _ptr(out), y_dtype, _ptr(workspace), ws_bytes,
                            _stream(x.device))
     _check("opq_linear", st)
     return out
