@@ -32,24 +32,47 @@ namespace {
 constexpr int kRowsPerBlock = 4;       // one wave per row
 constexpr int kChunk = kWave * 8;      // elements per wave-wide step (8 per lane)
 
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2_t, a),
+                                                                 __builtin_bit_cast(u16x2_t, b)));
+}
+
 // Eight consecutive elements of one lane, raw.
 template <typename T>
 struct Slot;
 template <>
 struct Slot<uint16_t> {
-  uint32_t r[4];  // bf16 pairs, element 2i in the low half
+  typedef uint32_t Acc;  // running max of |w|: two bf16 magnitude patterns
+  uint32_t r[4];         // bf16 pairs, element 2i in the low half
   __device__ __forceinline__ void load(const uint16_t* p) {
     const uint4 v = *reinterpret_cast<const uint4*>(p);
     r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
   }
   __device__ __forceinline__ void zero() { r[0] = r[1] = r[2] = r[3] = 0u; }
+  // Element i widened to binary32 (exact).
   __device__ __forceinline__ float at(int i) const {
     const uint32_t v = r[i >> 1];
     return __uint_as_float((i & 1) ? (v & 0xFFFF0000u) : (v << 16));
   }
+  // w_i < 0 on the raw pattern: sign set and magnitude not zero (-0.0 is not < 0).
+  __device__ __forceinline__ bool neg(int i) const {
+    const uint32_t v = r[i >> 1];
+    return (i & 1) ? (v > 0x8000FFFFu) : ((uint16_t)v > (uint16_t)0x8000u);
+  }
+  __device__ __forceinline__ static Acc acc0() { return 0u; }
+  __device__ __forceinline__ void absmax(Acc& a) const {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a = pk_max_u16(a, r[j] & 0x7FFF7FFFu);
+  }
+  __device__ __forceinline__ static float finish(Acc a) {
+    return __uint_as_float(max(a & 0xFFFFu, a >> 16) << 16);
+  }
 };
 template <>
 struct Slot<float> {
+  typedef float Acc;
   float r[8];
   __device__ __forceinline__ void load(const float* p) {
     const float4 a = reinterpret_cast<const float4*>(p)[0];
@@ -62,14 +85,20 @@ struct Slot<float> {
     for (int i = 0; i < 8; ++i) r[i] = 0.0f;
   }
   __device__ __forceinline__ float at(int i) const { return r[i]; }
+  __device__ __forceinline__ bool neg(int i) const { return r[i] < 0.0f; }
+  __device__ __forceinline__ static Acc acc0() { return 0.0f; }
+  __device__ __forceinline__ void absmax(Acc& a) const {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(r[i]));
+  }
+  __device__ __forceinline__ static float finish(Acc a) { return a; }
 };
 
 template <typename T>
 __device__ __forceinline__ float slot_absmax(const Slot<T>& s) {
-  float m = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(s.at(i)));
-  return m;
+  typename Slot<T>::Acc a = Slot<T>::acc0();
+  s.absmax(a);
+  return Slot<T>::finish(a);
 }
 
 __device__ __forceinline__ float next_up(float a) { return __uint_as_float(__float_as_uint(a) + 1u); }
@@ -92,40 +121,22 @@ __device__ __forceinline__ float pick_point(const DecisionPoints& dp, int j) {
   return t;
 }
 
-// Encode one lane's eight elements: returns the packed word, sets the sign byte.
+// Sign bits of one lane's eight elements (bit i = [w_i < 0]).
 template <typename T>
-__device__ __forceinline__ uint32_t encode8(const Slot<T>& s, const float (&A)[kLevels],
-                                            uint32_t& signs) {
-  uint32_t word = 0u, sb = 0u;
+__device__ __forceinline__ uint32_t sign_byte(const Slot<T>& s) {
+  uint32_t sb = 0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float x = s.at(i);
-    const float ax = fabsf(x);
-    uint32_t q = 0u;
-#pragma unroll
-    for (int j = 0; j < kLevels; ++j) q += (ax >= A[j]) ? 1u : 0u;
-    word |= q << (4 * i);
-    sb |= (x < 0.0f ? 1u : 0u) << i;
-  }
-  signs = sb;
-  return word;
-}
-
-// Row thresholds A_1..A_15, uniform across the wave.
-__device__ __forceinline__ void row_thresholds(const DecisionPoints& dp, float m, int lane,
-                                               float (&A)[kLevels]) {
-  float a = __builtin_inff();
-  if (m > 0.0f && lane < kLevels) a = magnitude_threshold(pick_point(dp, lane), m);
-#pragma unroll
-  for (int j = 0; j < kLevels; ++j) A[j] = readlane_f(a, j);
+  for (int i = 7; i >= 0; --i) sb = (sb << 1) + (s.neg(i) ? 1u : 0u);
+  return sb;
 }
 
 // Store one chunk's packed word and the sign word shared by four lanes.
 __device__ __forceinline__ void store_chunk(uint32_t* prow, uint32_t* srow, int c, int lane,
                                             bool valid, uint32_t word, uint32_t sbyte) {
   uint32_t s32 = valid ? (sbyte << (8 * (lane & 3))) : 0u;
-  s32 |= __shfl_xor(s32, 1, kWave);
-  s32 |= __shfl_xor(s32, 2, kWave);
+  // OR over each group of four lanes (quad permutes 1,0,3,2 and 2,3,0,1)
+  s32 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)s32, 0xB1, 0xF, 0xF, false);
+  s32 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)s32, 0x4E, 0xF, 0xF, false);
   if (valid) {
     prow[c * kWave + lane] = word;
     if ((lane & 3) == 0) srow[c * (kChunk / 32) + (lane >> 2)] = s32;
@@ -134,45 +145,41 @@ __device__ __forceinline__ void store_chunk(uint32_t* prow, uint32_t* srow, int 
 
 // ---------------------------------------------------------------- bucket table
 
-constexpr uint32_t kGuard = 16;     // ulps around a decision point decided exactly
-constexpr int kMaxBuckets = 2048;   // LDS words of the table
-constexpr uint32_t kNoPoint = 0x7F000000u;  // above every bits(u'): never reached
-constexpr int kMaxBlocks = 2048;    // grid of the table kernel (rows are strided)
+constexpr uint32_t kGuard = 16;             // ulps around a decision point decided exactly
+constexpr int kMaxBuckets = 1024;           // 8-byte entries
+constexpr uint32_t kNoPoint = 0x7F000000u;  // above every clamped bits(u')
+constexpr uint32_t kTop = 0x40000000u;      // bits(2.0f): u' is clamped to [floor, 2]
+constexpr int kMaxBlocks = 2048;            // grid of the table kernel (rows are strided)
 
-// Bucket b covers bit patterns [b0 + (b << shift), b0 + ((b + 1) << shift)).
+// Buckets b = 0 .. nb-1 cover bit patterns [b0 + (b << shift), b0 + ((b + 1) << shift));
+// the last one reaches past bits(2.0f).
 struct BucketGrid {
   uint32_t b0;
   int shift;
   int nb;
 };
 
-// The decision point's bit pattern with its low 4 bits replaced by 8: a table
-// entry keeps bits 4..31 only; comparing against this centre and widening the
-// guard by 8 covers every pattern that shares those bits.
-__host__ __device__ inline uint32_t point_centre(float t) {
+__host__ __device__ inline uint32_t float_bits(float t) {
   uint32_t b;
   __builtin_memcpy(&b, &t, 4);
-  return (b & ~15u) + 8u;
+  return b;
 }
-constexpr uint32_t kWindow = kGuard + 8;
 
 // The coarsest grid (3..10 index bits per binade) on which the windows
-// [centre - kWindow, centre + kWindow] of consecutive decision points never
+// [bits(T_j) - kGuard, bits(T_j) + kGuard] of consecutive decision points never
 // share a bucket.  False when none fits in kMaxBuckets.
 bool bucket_grid(const DecisionPoints& dp, BucketGrid& g) {
   uint32_t c[kLevels];
-  for (int j = 0; j < kLevels; ++j) c[j] = point_centre(dp.t[j]);
-  if (c[0] <= 2 * kWindow) return false;
-  const uint32_t top = 0x3F800000u + 64u;  // a little above bits(1.0f)
+  for (int j = 0; j < kLevels; ++j) c[j] = float_bits(dp.t[j]);
+  if (c[0] <= 2 * kGuard) return false;
   for (int mbits = 3; mbits <= 10; ++mbits) {
     const int shift = 23 - mbits;
-    const uint32_t b0 = (c[0] - kWindow) & ~((1u << shift) - 1u);
-    if (b0 >= top) return false;
-    const int64_t nb = (int64_t)((top - b0) >> shift) + 1;
+    const uint32_t b0 = (c[0] - kGuard) & ~((1u << shift) - 1u);
+    const int64_t nb = (int64_t)((kTop - b0) >> shift) + 1;
     if (nb > kMaxBuckets) return false;
     bool ok = true;
     for (int j = 0; j + 1 < kLevels && ok; ++j)
-      ok = ((c[j] + kWindow - b0) >> shift) < ((c[j + 1] - kWindow - b0) >> shift);
+      ok = ((c[j] + kGuard - b0) >> shift) < ((c[j + 1] - kGuard - b0) >> shift);
     if (ok) {
       g.b0 = b0;
       g.shift = shift;
@@ -183,155 +190,202 @@ bool bucket_grid(const DecisionPoints& dp, BucketGrid& g) {
   return false;
 }
 
-// Entry = (bits 4..31 of the point that may fall in the bucket, or kNoPoint)
-// | (number of points wholly below the bucket).  Points are sorted, so the one
-// that may fall inside is always number `below` (0-based).
-__device__ void build_table(const DecisionPoints& dp, BucketGrid g, uint32_t* tab) {
+// Entry b: y = number of decision points wholly below the bucket (their guard
+// windows end before it); x = kGuard - bits(T_y) when point y's window reaches
+// into the bucket, kGuard - kNoPoint otherwise (arithmetic mod 2^32).  Points
+// are sorted, so only point y can reach in.  For a clamped u' in the bucket,
+// d = bits(u') + x = bits(u') - bits(T_y) + kGuard fits an int32:
+//   code = y + [d >= kGuard],  decided exactly unless 0 <= d <= 2 kGuard.
+__device__ void build_table(const DecisionPoints& dp, BucketGrid g, uint2* tab) {
   for (int b = threadIdx.x; b < g.nb; b += blockDim.x) {
     const uint32_t lo = g.b0 + ((uint32_t)b << g.shift);
     const uint32_t hi = lo + (1u << g.shift);
-    uint32_t below = 0u;
+    // Static indices only: a lane-dependent index into dp would become a
+    // load from the argument segment.
+    uint32_t below = 0u, next = kNoPoint;
 #pragma unroll
-    for (int j = 0; j < kLevels; ++j) below += (point_centre(dp.t[j]) + kWindow < lo) ? 1u : 0u;
-    uint32_t e = kNoPoint | below;
-    if (below < (uint32_t)kLevels) {
-      const uint32_t c = point_centre(pick_point(dp, (int)below));
-      if (c - kWindow < hi) e = (c - 8u) | below;
+    for (int j = kLevels - 1; j >= 0; --j) {
+      const uint32_t c = float_bits(dp.t[j]);
+      const bool under = c + kGuard < lo;
+      below += under ? 1u : 0u;
+      next = under ? next : c;  // ends at the lowest point not wholly below
     }
-    tab[b] = e;
+    const uint32_t x = (next != kNoPoint && next - kGuard < hi) ? kGuard - next : kGuard - kNoPoint;
+    tab[b] = make_uint2(x, below);
   }
 }
 
-__device__ __forceinline__ uint32_t table_at(const uint32_t* tab, BucketGrid g, uint32_t ub) {
-  const int b = (int)(ub - g.b0) >> g.shift;
-  return tab[min(max(b, 0), g.nb - 1)];
+// Table entry for a quotient already clamped to [floor, 2.0]; nbase8 is
+// -(b0 >> shift) * 8.
+__device__ __forceinline__ uint2 table_at(const uint2* tab, uint32_t ub, int shift, uint32_t nbase8) {
+  const uint32_t off = ((ub >> shift) << 3) + nbase8;
+  return *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(tab) + off);
 }
 
-// Exact code of magnitude a in a row with max m (any m >= a >= 0): the
-// correctly rounded quotient, its bucket, and one comparison.
-__device__ __forceinline__ uint32_t code_exact(float a, float m, const uint32_t* tab, BucketGrid g,
-                                               const float* pts) {
+// Exact code of magnitude a in a row with max m (m >= a >= 0): the correctly
+// rounded quotient, its bucket, and one comparison with the next point
+// (pts[15] = 2 is never reached).
+__device__ __forceinline__ uint32_t code_exact(float a, float m, const uint2* tab, int shift,
+                                               uint32_t nbase, float ulo, const float* pts) {
   const float u = m > 0.0f ? a / m : 0.0f;
-  const uint32_t e = table_at(tab, g, __float_as_uint(u));
-  const uint32_t below = e & 15u;
-  return below + ((below < (uint32_t)kLevels && u >= pts[below]) ? 1u : 0u);
+  const float uc = fminf(fmaxf(u, ulo), 2.0f);
+  const uint32_t below = table_at(tab, __float_as_uint(uc), shift, nbase).y;
+  return below + (u >= pts[below] ? 1u : 0u);
 }
 
 template <typename T>
-__device__ __forceinline__ uint32_t encode8_exact(const Slot<T>& s, float m, const uint32_t* tab,
-                                                  BucketGrid g, const float* pts) {
+__device__ __forceinline__ uint32_t encode8_exact(const Slot<T>& s, float m, const uint2* tab,
+                                                  int shift, uint32_t nbase, float ulo,
+                                                  const float* pts) {
   uint32_t word = 0u;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) word |= code_exact(fabsf(s.at(i)), m, tab, g, pts) << (4 * i);
+  for (int i = 7; i >= 0; --i)
+    word = (word << 4) + code_exact(fabsf(s.at(i)), m, tab, shift, nbase, ulo, pts);
   return word;
 }
 
-// Fast encode with u' = |x| * r; `amb` is set when some element lies within
-// kWindow patterns of its bucket's point (the caller then re-encodes exactly).
+// Fast encode with u' = |w| * r (r = fl32(1/m), u' within 3 ulps of u), clamped
+// to [floor, 2].  `near` ends at min over the elements of the unsigned d; the
+// caller re-encodes exactly when it is <= 2 kGuard.
 template <typename T>
-__device__ __forceinline__ uint32_t encode8_fast(const Slot<T>& s, float r, const uint32_t* tab,
-                                                 BucketGrid g, bool& amb) {
-  uint32_t word = 0u;
-  bool near = false;
+__device__ __forceinline__ uint32_t encode8_fast(const Slot<T>& s, float r, const uint2* tab,
+                                                 int shift, uint32_t nbase, float ulo,
+                                                 uint32_t& near) {
+  uint32_t word = 0u, nr = 0xFFFFFFFFu;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t ub = __float_as_uint(fabsf(s.at(i)) * r);
-    const uint32_t e = table_at(tab, g, ub);
-    const uint32_t c = (e & ~15u) | 8u;
-    const uint32_t q = (e & 15u) + (ub >= c ? 1u : 0u);
-    near |= (ub - c + kWindow) <= 2u * kWindow;
-    word |= q << (4 * i);
+  for (int i = 7; i >= 0; --i) {
+    // finite here: the row max is normal and 1/m too
+    const float up = __builtin_amdgcn_fmed3f(fabsf(s.at(i)) * r, ulo, 2.0f);
+    const uint32_t ub = __float_as_uint(up);
+    const uint2 e = table_at(tab, ub, shift, nbase);
+    const int d = (int)(ub + e.x);
+    word = (word << 4) + e.y + (d >= (int)kGuard ? 1u : 0u);
+    nr = min(nr, (uint32_t)d);
   }
-  amb = near;
+  near = nr;
   return word;
-}
-
-template <typename T>
-__device__ __forceinline__ uint32_t sign_byte(const Slot<T>& s) {
-  uint32_t sb = 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) sb |= (s.at(i) < 0.0f ? 1u : 0u) << i;
-  return sb;
 }
 
 template <typename T>
 __device__ __forceinline__ uint32_t encode_chunk(const Slot<T>& v, float mx, float r, bool fast,
-                                                 const uint32_t* tab, BucketGrid g,
-                                                 const float* pts) {
+                                                 const uint2* tab, int shift, uint32_t nbase,
+                                                 float ulo, const float* pts) {
   if (fast) {
-    bool amb;
-    const uint32_t word = encode8_fast(v, r, tab, g, amb);
-    if (!amb) return word;
+    uint32_t near;
+    const uint32_t word = encode8_fast(v, r, tab, shift, nbase, ulo, near);
+    if (near > 2u * kGuard) return word;
   }
-  return encode8_exact(v, mx, tab, g, pts);
+  return encode8_exact(v, mx, tab, shift, nbase, ulo, pts);
 }
 
-// Table kernel.  Blocks build the table once and stride over rows, one row per
-// wave at a time.  NCH > 0: the row (k <= NCH * 512) stays in registers.
-// NCH == 0: any k, the row is streamed twice (max pass, then encode pass).
+// Table kernel: blocks build the table, then each wave takes one row at a time
+// (rows strided over the grid).  NCH > 0: the row (k <= NCH * 512) stays in
+// registers.  NCH == 0: any k, the row is streamed twice (max, then encode).
 template <typename T, int NCH>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
     const T* __restrict__ w, int64_t n, int k, DecisionPoints dp, BucketGrid g,
     uint32_t* __restrict__ packed, uint32_t* __restrict__ sign, float* __restrict__ scale) {
-  __shared__ uint32_t s_tab[kMaxBuckets];
+  __shared__ uint2 s_tab[kMaxBuckets];
   __shared__ float s_pts[kLevels + 1];
-  build_table(dp, g, s_tab);
-  if (threadIdx.x <= kLevels) s_pts[threadIdx.x] = threadIdx.x < kLevels ? pick_point(dp, threadIdx.x) : 2.0f;
-  __syncthreads();
-
   const int lane = threadIdx.x & (kWave - 1);
-  for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave); row < n;
-       row += (int64_t)gridDim.x * kRowsPerBlock) {
-    const T* wr = w + row * (int64_t)k;
+  const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
+  int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+
+  // The first row's loads go out before the table is built.
+  Slot<T> v[NCH > 0 ? NCH : 1];
+  auto load_row = [&](int64_t rr) {
+    const T* wr = w + rr * (int64_t)k;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e0 = c * kChunk + lane * 8;
+      if (e0 < k) v[c].load(wr + e0); else v[c].zero();
+    }
+  };
+  if constexpr (NCH > 0) {
+    if (row < n) load_row(row);
+  }
+
+  build_table(dp, g, s_tab);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int j = 0; j < kLevels; ++j) s_pts[j] = dp.t[j];
+    s_pts[kLevels] = 2.0f;
+  }
+  // The table is in LDS once lgkmcnt drains; the row loads stay in flight
+  // (a full __syncthreads would wait for them too).
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left open
+  __builtin_amdgcn_s_barrier();
+  const int shift = g.shift;
+  const uint32_t nbase = (0u - (g.b0 >> g.shift)) << 3;
+  const float ulo = __uint_as_float(g.b0);
+
+  for (; row < n; row += stride) {
     uint32_t* prow = packed + row * (int64_t)(k / 8);
     uint32_t* srow = sign + row * (int64_t)(k / 32);
     if constexpr (NCH > 0) {
-      Slot<T> v[NCH];
-      float mx = 0.0f;
+      typename Slot<T>::Acc acc = Slot<T>::acc0();
 #pragma unroll
-      for (int c = 0; c < NCH; ++c) {
-        const int e0 = c * kChunk + lane * 8;
-        if (e0 < k) {
-          v[c].load(wr + e0);
-          mx = fmaxf(mx, slot_absmax(v[c]));
-        } else {
-          v[c].zero();
-        }
-      }
-      mx = wave_max(mx);
+      for (int c = 0; c < NCH; ++c) v[c].absmax(acc);
+      const float mx = wave_max(Slot<T>::finish(acc));
       const bool fast = mx >= 0x1p-125f && mx <= 0x1p125f;  // 1/m normal, u' <= 1 + ulps
       const float r = 1.0f / mx;
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int e0 = c * kChunk + lane * 8;
-        const uint32_t word = encode_chunk(v[c], mx, r, fast, s_tab, g, s_pts);
+        const uint32_t word = encode_chunk(v[c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts);
         store_chunk(prow, srow, c, lane, e0 < k, word, sign_byte(v[c]));
       }
       if (lane == 0) scale[row] = mx;
+      if (row + stride < n) load_row(row + stride);
     } else {
+      const T* wr = w + row * (int64_t)k;
       const int nch = (k + kChunk - 1) / kChunk;
-      float mx = 0.0f;
+      typename Slot<T>::Acc acc = Slot<T>::acc0();
       for (int c = 0; c < nch; ++c) {
         const int e0 = c * kChunk + lane * 8;
         if (e0 < k) {
           Slot<T> sl;
           sl.load(wr + e0);
-          mx = fmaxf(mx, slot_absmax(sl));
+          sl.absmax(acc);
         }
       }
-      mx = wave_max(mx);
+      const float mx = wave_max(Slot<T>::finish(acc));
       const bool fast = mx >= 0x1p-125f && mx <= 0x1p125f;
       const float r = 1.0f / mx;
       for (int c = 0; c < nch; ++c) {
         const int e0 = c * kChunk + lane * 8;
         Slot<T> sl;
         if (e0 < k) sl.load(wr + e0); else sl.zero();
-        const uint32_t word = encode_chunk(sl, mx, r, fast, s_tab, g, s_pts);
+        const uint32_t word = encode_chunk(sl, mx, r, fast, s_tab, shift, nbase, ulo, s_pts);
         store_chunk(prow, srow, c, lane, e0 < k, word, sign_byte(sl));
       }
       if (lane == 0) scale[row] = mx;
     }
   }
+}
+
+// Encode against per-row magnitude thresholds A_1..A_15 (fallback kernel).
+template <typename T>
+__device__ __forceinline__ uint32_t encode8(const Slot<T>& s, const float (&A)[kLevels]) {
+  uint32_t word = 0u;
+#pragma unroll
+  for (int i = 7; i >= 0; --i) {
+    const float ax = fabsf(s.at(i));
+    uint32_t q = 0u;
+#pragma unroll
+    for (int j = 0; j < kLevels; ++j) q += (ax >= A[j]) ? 1u : 0u;
+    word = (word << 4) + q;
+  }
+  return word;
+}
+
+// Row thresholds A_1..A_15, uniform across the wave.
+__device__ __forceinline__ void row_thresholds(const DecisionPoints& dp, float m, int lane,
+                                               float (&A)[kLevels]) {
+  float a = __builtin_inff();
+  if (m > 0.0f && lane < kLevels) a = magnitude_threshold(pick_point(dp, lane), m);
+#pragma unroll
+  for (int j = 0; j < kLevels; ++j) A[j] = readlane_f(a, j);
 }
 
 // ---------------------------------------------------------------- threshold kernel (fallback)
@@ -368,9 +422,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows(
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int e0 = c * kChunk + lane * 8;
-      uint32_t sb;
-      const uint32_t word = encode8(v[c], A, sb);
-      store_chunk(prow, srow, c, lane, e0 < k, word, sb);
+      store_chunk(prow, srow, c, lane, e0 < k, encode8(v[c], A), sign_byte(v[c]));
     }
     if (lane == 0) scale[row] = mx;
   } else {
@@ -391,9 +443,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows(
       const int e0 = c * kChunk + lane * 8;
       Slot<T> s;
       if (e0 < k) s.load(wr + e0); else s.zero();
-      uint32_t sb;
-      const uint32_t word = encode8(s, A, sb);
-      store_chunk(prow, srow, c, lane, e0 < k, word, sb);
+      store_chunk(prow, srow, c, lane, e0 < k, encode8(s, A), sign_byte(s));
     }
     if (lane == 0) scale[row] = mx;
   }
