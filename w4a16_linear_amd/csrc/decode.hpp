@@ -86,8 +86,10 @@ __device__ __forceinline__ void dequant_word(uint32_t w, uint32_t sb, const RowL
 }
 
 // Eight bfloat16 values of one packed word in k order: out = {(k0,k1),
-// (k2,k3), (k4,k5), (k6,k7)}.  A sign bit only marks a nonzero code, so code 0
-// always gives +0.0.  `sb` holds the sign byte in bits 0..7.
+// (k2,k3), (k4,k5), (k6,k7)}.  `sb` holds the sign byte in bits 0..7.  With
+// kPlusZero a sign bit only marks a nonzero code, so code 0 always gives +0.0
+// (without it, a negative zero may come out, which no product can tell apart).
+template <bool kPlusZero = true>
 __device__ __forceinline__ void decode_word_ordered(uint32_t w, uint32_t sb, const RowLut& t,
                                                     uint32_t (&out)[4]) {
   const uint32_t se7 = w & 0x07070707u;
@@ -98,8 +100,8 @@ __device__ __forceinline__ void decode_word_ordered(uint32_t w, uint32_t sb, con
   const uint32_t lo_e = plane4(t.lo, se7, me), hi_e = plane4(t.hi, se7, me);
   const uint32_t lo_o = plane4(t.lo, so7, mo), hi_o = plane4(t.hi, so7, mo);
   // bit 7 of each byte: the code is not 0
-  const uint32_t nz_e = (w & 0x0F0F0F0Fu) + 0x7F7F7F7Fu;
-  const uint32_t nz_o = ((w >> 4) & 0x0F0F0F0Fu) + 0x7F7F7F7Fu;
+  const uint32_t nz_e = kPlusZero ? (w & 0x0F0F0F0Fu) + 0x7F7F7F7Fu : 0xFFFFFFFFu;
+  const uint32_t nz_o = kPlusZero ? ((w >> 4) & 0x0F0F0F0Fu) + 0x7F7F7F7Fu : 0xFFFFFFFFu;
   const uint32_t sge = __umul24((sb << 7) & 0x2A80u, 0x41041u);
   const uint32_t sgo = __umul24((sb << 6) & 0x2A80u, 0x41041u);
   const uint32_t hs_e = hi_e | (sge & nz_e & 0x80808080u);

@@ -47,81 +47,88 @@ __device__ __forceinline__ void store_y(void* y, bool y_bf16, int64_t at, float 
 // its eight waves take the 128-wide k blocks in turn and meet in LDS at the
 // end, so no partial sums leave the block.
 //
-// For one 128-wide k block, lane l (row r = l % 16, group g = l / 16) loads
-// packed words 4g..4g+3 of its row (four groups read 64 contiguous bytes of
-// the row), sign word g, and x[.][32g .. 32g+31] of its x rows.  Sub-step t
-// contracts the 8-wide k chunks {t, 4+t, 8+t, 12+t}, group g supplying word t
-// of its four; x chunks are put in the dequantizer's pair order so both
-// operands list k the same way.
+// Loads are laid out for the memory system, not for the MFMA: in a load, each
+// group of four lanes reads 64 contiguous bytes (packed words: lane l reads
+// part l%4 of weight row l/4; x: lane l reads 16-byte chunk l%16 of x row
+// l/16 + 4i).  Packed words and sign words then move to the MFMA layout with
+// ds_bpermute (lane (r, g) = (l%16, l/16) takes part g of row r), and x goes
+// through a wave-private LDS stage, read back as B fragments.  Sub-step t of a
+// k block contracts the 8-wide chunks {t, 4+t, 8+t, 12+t}: lane (r, g)
+// supplies word t of part g, and chunk 4g + t of x.
 
 constexpr int kSkinnyMaxM = 64;
 constexpr int kSkRows = 16;                     // weight rows per block
-constexpr int kSkFrags = kSkRows / 16;          // 16-row MFMA fragments per block
 constexpr int kSkWaves = 8;
 constexpr int kSkThreads = kSkWaves * kWave;
 constexpr int kSkBlockK = 128;                  // k per wave step
 
-template <int NMB>
+// Element offset of 16-byte chunk c (0..15) of x row R in a wave's stage:
+// 256-byte rows, chunks XOR-swizzled by the row so that the sixteen rows of a
+// B fragment (same chunk) and the sixteen chunks of a row fall in different
+// banks.
+__device__ __forceinline__ int xs_off(int R, int c) { return R * kSkBlockK + ((c ^ (R & 15)) << 3); }
+
+template <int NMB>             // 16-row blocks of x: 1, 2 or 4
 __global__ __launch_bounds__(kSkThreads) void linear_skinny(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
     const float* __restrict__ bias, int m, int n, int k, Levels lv, void* __restrict__ y,
     int y_bf16) {
   constexpr int CH = NMB == 4 ? 1 : 2;                  // k blocks per load batch
-  constexpr int kOut = kSkFrags * NMB * 4 * kWave;      // block outputs, accumulator order
+  constexpr int kXRows = 16 * NMB;
+  constexpr int kXLoads = kXRows / 4;                   // x loads per lane per k block
+  constexpr int kStage = kXRows * kSkBlockK;            // bf16 per wave stage
+  constexpr int kOut = NMB * 4 * kWave;                 // outputs per wave, accumulator order
+  static_assert(kSkWaves * kOut * 4 <= kSkWaves * kStage * 2, "reduction fits the stages");
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[kSkWaves * kStage];
   __shared__ uint32_t s_lut[kSkRows][8];
-  __shared__ float s_red[kSkWaves][kOut];
+  float* s_red = reinterpret_cast<float*>(s_x);         // after the k loop
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
   const int n0 = blockIdx.x * kSkRows;
-  const int r = lane & 15, g = lane >> 4;
   const int kwords = k / 8, swords = k / 32;
 
   // This wave's k blocks: wave, wave + kSkWaves, ...
   const int nkb = (k + kSkBlockK - 1) / kSkBlockK;
   const int mine = nkb > wave ? (nkb - 1 - wave) / kSkWaves + 1 : 0;
 
-  // Byte offsets from uniform bases.  Weight rows past n read row n - 1 and x
-  // rows past m read row m - 1; neither is stored.
+  // Loader lanes.  Weight rows past n read row n - 1 and x rows past m read
+  // row m - 1; neither is stored.
+  const int lr = lane >> 2, lp = lane & 3;     // packed/sign: row lr, part lp
+  const int xr = lane >> 4, xc = lane & 15;    // x: rows xr + 4i, chunk xc
   const int n0c = min(n0, n - 1);
   const char* pbase = reinterpret_cast<const char*>(packed + (int64_t)n0c * kwords);
   const char* sbase = reinterpret_cast<const char*>(sign + (int64_t)n0c * swords);
-  uint32_t p_off[kSkFrags], s_off[kSkFrags];
-#pragma unroll
-  for (int f = 0; f < kSkFrags; ++f) {
-    const uint32_t rel = (uint32_t)(min(n0 + 16 * f + r, n - 1) - n0c);
-    p_off[f] = rel * (uint32_t)kwords * 4u;
-    s_off[f] = rel * (uint32_t)swords * 4u;
-  }
+  const uint32_t rel = (uint32_t)(min(n0 + lr, n - 1) - n0c);
+  const uint32_t p_off = rel * (uint32_t)kwords * 4u, s_off = rel * (uint32_t)swords * 4u;
   const char* xbase = reinterpret_cast<const char*>(x);
-  uint32_t x_off[NMB];
+  uint32_t x_off[kXLoads];
 #pragma unroll
-  for (int b = 0; b < NMB; ++b) x_off[b] = (uint32_t)min(b * 16 + r, m - 1) * (uint32_t)k * 2u;
+  for (int i = 0; i < kXLoads; ++i) x_off[i] = (uint32_t)min(4 * i + xr, m - 1) * (uint32_t)k * 2u;
 
-  uint4 wd[2][CH][kSkFrags];
-  uint32_t sw[2][CH][kSkFrags];
-  uint4 xv[2][CH][NMB][4];
+  // MFMA lanes: (r, g) takes its packed part from loader lane 4r + g.
+  const int r = lane & 15, g = lane >> 4;
+  const int src = (4 * r + g) * 4;
+
+  uint4 wd[2][CH];
+  uint32_t sw[2][CH];
+  uint4 xv[2][CH][kXLoads];
   // Batch bi holds this wave's k blocks bi*CH .. bi*CH + CH - 1 (clamped to the
-  // last).  In a final part block (k % 128 != 0) groups past k re-read group 0
-  // of the block and the dequantizer zeroes their fragments.
-  auto load_batch = [&](int bi, int buf) {
+  // last).  In a final part block (k % 128 != 0) parts and chunks past k
+  // re-read the block's first ones; the dequantizer zeroes those fragments.
+  auto load_batch = [&](int bi, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int blk = wave + kSkWaves * min(bi * CH + j, mine - 1);
-      const int kk = blk * kSkBlockK + 32 * g;
-      const uint32_t ke = (uint32_t)(kk < k ? kk : blk * kSkBlockK);
+      const int kb = (wave + kSkWaves * min(bi * CH + j, mine - 1)) * kSkBlockK;
+      const uint32_t kw = (uint32_t)(kb + 32 * lp < k ? kb + 32 * lp : kb);
+      const uint32_t kx = (uint32_t)(kb + 8 * xc < k ? kb + 8 * xc : kb);
+      wd[buf][j] = *reinterpret_cast<const uint4*>(pbase + p_off + kw / 2u);
+      sw[buf][j] = *reinterpret_cast<const uint32_t*>(sbase + s_off + kw / 8u);
 #pragma unroll
-      for (int f = 0; f < kSkFrags; ++f) {
-        wd[buf][j][f] = *reinterpret_cast<const uint4*>(pbase + p_off[f] + ke / 2u);
-        sw[buf][j][f] = *reinterpret_cast<const uint32_t*>(sbase + s_off[f] + ke / 8u);
-      }
-#pragma unroll
-      for (int b = 0; b < NMB; ++b)
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-          xv[buf][j][b][t] = *reinterpret_cast<const uint4*>(xbase + x_off[b] + (ke + 8u * t) * 2u);
+      for (int i = 0; i < kXLoads; ++i)  // m <= 16: groups of 4 x rows wholly past m are skipped
+        if (NMB > 1 || 4 * i < m) xv[buf][j][i] = *reinterpret_cast<const uint4*>(xbase + x_off[i] + kx * 2u);
     }
   };
 
@@ -129,61 +136,68 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   if (nbatch > 0) load_batch(0, 0);
   if (nbatch > 1) load_batch(1, 1);
 
-  // Byte planes of the block's 64 row tables, four entries per thread: thread
-  // t makes entries 4(t%4) .. 4(t%4)+3 of row t/4.
-  if (tid < kSkRows * 4) {
-    const int row = tid >> 2, j = tid & 3;
-    const float mr = scale[min(n0 + row, n - 1)];
+  // Byte planes of the block's 16 row tables: wave w < 4 makes entries
+  // 4w .. 4w+3 of row `lane` (a wave-uniform code, so the levels stay in
+  // scalar registers).
+  if (wave < 4 && lane < kSkRows) {
+    const float mr = scale[min(n0 + lane, n - 1)];
     uint32_t lo = 0u, hi = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t e = lut_entry(lv, 4 * j + i, mr);
+      const uint32_t e = lut_entry(lv, 4 * wave + i, mr);
       lo |= (e & 0xFFu) << (8 * i);
       hi |= (e >> 8) << (8 * i);
     }
-    s_lut[row][j] = lo;
-    s_lut[row][4 + j] = hi;
+    s_lut[lane][wave] = lo;
+    s_lut[lane][4 + wave] = hi;
   }
-  __syncthreads();
-  RowLut lut[kSkFrags];
-#pragma unroll
-  for (int f = 0; f < kSkFrags; ++f) {
-    const uint4 lo = *reinterpret_cast<const uint4*>(&s_lut[16 * f + r][0]);
-    const uint4 hi = *reinterpret_cast<const uint4*>(&s_lut[16 * f + r][4]);
-    lut[f].lo[0] = lo.x; lut[f].lo[1] = lo.y; lut[f].lo[2] = lo.z; lut[f].lo[3] = lo.w;
-    lut[f].hi[0] = hi.x; lut[f].hi[1] = hi.y; lut[f].hi[2] = hi.z; lut[f].hi[3] = hi.w;
+  // LDS writes done and visible; the loads stay in flight.
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  RowLut lut;
+  {
+    const uint4 lo = *reinterpret_cast<const uint4*>(&s_lut[r][0]);
+    const uint4 hi = *reinterpret_cast<const uint4*>(&s_lut[r][4]);
+    lut.lo[0] = lo.x; lut.lo[1] = lo.y; lut.lo[2] = lo.z; lut.lo[3] = lo.w;
+    lut.hi[0] = hi.x; lut.hi[1] = hi.y; lut.hi[2] = hi.z; lut.hi[3] = hi.w;
   }
 
-  floatx4_t acc[kSkFrags][NMB];
+  floatx4_t acc[NMB];
 #pragma unroll
-  for (int f = 0; f < kSkFrags; ++f)
-#pragma unroll
-    for (int b = 0; b < NMB; ++b) acc[f][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  for (int b = 0; b < NMB; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute_batch = [&](int bi, int buf) {
+  uint16_t* stage = s_x + wave * kStage;
+  auto compute_batch = [&](int bi, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int idx = bi * CH + j;
       if (idx < mine) {
-        const int blk = wave + kSkWaves * idx;
-        const bool live = blk * kSkBlockK + 32 * g < k;
+        const int kb = (wave + kSkWaves * idx) * kSkBlockK;
+        const bool live = kb + 32 * g < k;
+#pragma unroll
+        for (int i = 0; i < kXLoads; ++i) {
+          // x rows past m only feed output columns that are never stored
+          if (NMB == 1 && 4 * i >= m) continue;
+          // element-wise: a whole-struct copy becomes a memcpy that keeps xv in scratch
+          const uint4 v = xv[buf][j][i];
+          *reinterpret_cast<u32x4_t*>(stage + xs_off(4 * i + xr, xc)) = u32x4_t{v.x, v.y, v.z, v.w};
+        }
+        const uint32_t words[4] = {
+            (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)wd[buf][j].x),
+            (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)wd[buf][j].y),
+            (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)wd[buf][j].z),
+            (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)wd[buf][j].w)};
+        const uint32_t sb = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sw[buf][j]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          bf16x8_t xs[NMB];
+          uint32_t o[4];
+          decode_word_ordered<false>(words[t], sb >> (8 * t), lut, o);
+          if (!live) o[0] = o[1] = o[2] = o[3] = 0u;
+          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 #pragma unroll
-          for (int b = 0; b < NMB; ++b)
-            xs[b] = __builtin_bit_cast(bf16x8_t, sigma_order(xv[buf][j][b][t]));
-#pragma unroll
-          for (int f = 0; f < kSkFrags; ++f) {
-            const uint4 wv = wd[buf][j][f];
-            const uint32_t word = t == 0 ? wv.x : (t == 1 ? wv.y : (t == 2 ? wv.z : wv.w));
-            uint32_t o[4];
-            dequant_word(word, sw[buf][j][f] >> (8 * t), lut[f], o);
-            if (!live) o[0] = o[1] = o[2] = o[3] = 0u;
-            const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-#pragma unroll
-            for (int b = 0; b < NMB; ++b)
-              acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, xs[b], acc[f][b], 0, 0, 0);
+          for (int b = 0; b < NMB; ++b) {
+            const bf16x8_t bx = *reinterpret_cast<const bf16x8_t*>(stage + xs_off(16 * b + r, 4 * g + t));
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bx, acc[b], 0, 0, 0);
           }
         }
       }
@@ -199,25 +213,24 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
     }
   }
 
-  // Waves meet in LDS; element o = ((f * NMB + b) * 4 + e) * 64 + lane.
-#pragma unroll
-  for (int f = 0; f < kSkFrags; ++f)
-#pragma unroll
-    for (int b = 0; b < NMB; ++b)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_red[wave][((f * NMB + b) * 4 + e) * kWave + lane] = acc[f][b][e];
+  // Waves meet in LDS (the stages are free once every wave is here);
+  // element o = (b * 4 + e) * 64 + lane.
   __syncthreads();
-  // Output (x row mm, weight row i): fragment f = i / 16, register (i % 16) % 4
-  // of lane 16 * ((i % 16) / 4) + mm % 16; waves summed in a fixed order.
-  for (int o = tid; o < kSkRows * NMB * 16; o += kSkThreads) {
+#pragma unroll
+  for (int b = 0; b < NMB; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_red[wave * kOut + (b * 4 + e) * kWave + lane] = acc[b][e];
+  __syncthreads();
+  // Output (x row mm, weight row i): register i % 4 of lane 16 * (i / 4) + mm % 16
+  // in block mm / 16; waves summed in a fixed order.
+  for (int o = tid; o < kSkRows * kXRows; o += kSkThreads) {
     const int i = o % kSkRows, mm = o / kSkRows;
     const int gcol = n0 + i;
     if (mm < m && gcol < n) {
-      const int f = i / 16, ii = i % 16, b = mm / 16;
-      const int src = ((f * NMB + b) * 4 + (ii & 3)) * kWave + 16 * (ii >> 2) + (mm & 15);
-      float val = s_red[0][src];
+      const int src_o = ((mm >> 4) * 4 + (i & 3)) * kWave + 16 * (i >> 2) + (mm & 15);
+      float val = s_red[src_o];
 #pragma unroll
-      for (int w = 1; w < kSkWaves; ++w) val += s_red[w][src];
+      for (int w = 1; w < kSkWaves; ++w) val += s_red[w * kOut + src_o];
       store_y(y, y_bf16, (int64_t)mm * n + gcol, val + (bias ? bias[gcol] : 0.0f));
     }
   }
