@@ -263,6 +263,25 @@ constexpr int kAStage = kTM * kTK;                 // bf16 per stage
 // 16-lane passes of ds_read_b128 conflict-free.
 __device__ __forceinline__ int a_off(int r, int c) { return r * kTK + ((c ^ ((r >> 1) & 7)) << 3); }
 
+// Scheduling hint for one sub-step (16 MFMAs): alternate each MFMA with V
+// VALU instructions so the dequantizer runs in the MFMAs' shadow, and spread
+// the x fragment reads (R), the x stage writes (W) and global loads (G) over
+// the first MFMAs (V = 0 would leave the order to the compiler; 3 measured
+// best for the DiT shapes, ahead of 1, 2, 4, 5, 6).
+constexpr int kInterleaveV = 3;
+
+template <int I, int V, int R, int W, int G>
+__device__ __forceinline__ void interleave_substep() {
+  if constexpr (V > 0 && I < 16) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
+    if constexpr (I < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    if constexpr (I < W) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+    if constexpr (I < G) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);          // VALU
+    interleave_substep<I + 1, V, R, W, G>();
+  }
+}
+
 template <bool kHalfTail>
 __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
@@ -372,40 +391,46 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
       a[mi] = *reinterpret_cast<const bf16x8_t*>(sa + a_off(mi * 32 + (lane & 31), 4 * g + s));
   };
 
-  // Pipeline per k step kt (x in LDS stage kt & 1):
+  // Pipeline per k step kt (x in LDS stage kt & 1); fragments of sub-step 0
+  // are ready when the step starts:
   //   issue the weights of step kt + 1;
-  //   sub-step 0;
-  //   store x of step kt + 1 (loaded during step kt - 1) into the other stage,
-  //   then issue the x loads of step kt + 2 into the freed registers;
-  //   sub-steps 1..3;  barrier.
-  // The other stage was last read in step kt - 1, before the barrier that
-  // ended it, so the mid-step store is safe; x loads get a full step in flight.
+  //   sub-steps s = 0..2: read x fragments and dequantize weights of s + 1,
+  //     MFMAs of s; after sub-step 0's MFMAs store x of step kt + 1 (loaded
+  //     during step kt - 1) into the other stage and issue the x loads of
+  //     step kt + 2;
+  //   sub-step 3: barrier, then read x fragments of step kt + 1 from the other
+  //     stage and dequantize its weights for sub-step 0, MFMAs of 3.
+  // The barrier orders every wave's store into the other stage (sub-step 0)
+  // before its reads, and every read of this stage (last issued in sub-step
+  // 2) before the next step's store into it.
   uint4 pw[2], pw_next[2];
   uint32_t sw[2], sw_next[2];
   uint4 xa[8];
+  bf16x8_t a_buf[2][8], b_buf[2][2];
   if (nsteps > 0) {
     load_a(0, xa);
     load_b(0, pw, sw);
     store_a(0, xa);
+    load_a(1, xa);
+    __syncthreads();
+    read_a(s_a, 0, a_buf[0]);
+    dequant_b(0, 0, pw, sw, b_buf[0]);
   }
-  if (nsteps > 0) load_a(1, xa);
-  __syncthreads();
 
-  bf16x8_t a_buf[2][8], b_buf[2][2];
   for (int kt = 0; kt < nsteps; ++kt) {
     const int stage = kt & 1;
     load_b(kt + 1, pw_next, sw_next);
     const uint16_t* sa = s_a + stage * kAStage;
-    read_a(sa, 0, a_buf[0]);
-    dequant_b(kt, 0, pw, sw, b_buf[0]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
       if (s < 3) {
         read_a(sa, s + 1, a_buf[nxt]);
-        // the next fragments' LDS reads stay ahead of this sub-step's MFMAs
-        __builtin_amdgcn_sched_barrier(0);
         dequant_b(kt, s + 1, pw, sw, b_buf[nxt]);
+      } else {
+        __syncthreads();
+        read_a(s_a + (stage ^ 1) * kAStage, 0, a_buf[nxt]);
+        dequant_b(kt + 1, 0, pw_next, sw_next, b_buf[nxt]);
       }
 #pragma unroll
       for (int mi = 0; mi < 8; ++mi)
@@ -416,6 +441,9 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
       if (s == 0) {
         store_a(stage ^ 1, xa);
         load_a(kt + 2, xa);
+        interleave_substep<0, kInterleaveV + 2, 8, 8, 12>();
+      } else {
+        interleave_substep<0, kInterleaveV, 8, 0, 0>();
       }
     }
 #pragma unroll
@@ -423,7 +451,6 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
       pw[f] = pw_next[f];
       sw[f] = sw_next[f];
     }
-    __syncthreads();
   }
 
   // 32x32 accumulator layout: register e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
