@@ -86,8 +86,10 @@ def ideal_us(kind, alg, m):
 
 
 def source_hash(kind):
+    """Hash of the kernel's source file and every shared device header."""
     h = hashlib.sha256()
-    for f in (KERNEL_SOURCE[kind], "device_common.hpp"):
+    headers = sorted(f for f in os.listdir(CSRC) if f.endswith(".hpp"))
+    for f in [KERNEL_SOURCE[kind]] + headers:
         with open(os.path.join(CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
