@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="skinny", choices=["skinny", "qkv", "ffn_up", "ffn_down", "tiny"])
+    ap.add_argument("--workload", default="skinny",
+                    choices=["skinny", "qkv", "ffn_up", "ffn_down", "tiny", "model"])
     ap.add_argument("--alpha", type=float, default=0.73)
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for > 768 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -170,6 +171,8 @@ def main():
     opq.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload == "model":
+        return model_pass(args, dev)
     L = workload(args.workload)
     m, n, k = L.m, L.n, L.k
     alpha = args.alpha
@@ -311,6 +314,141 @@ def main():
         out["cpu_baseline"] = cpu_baseline(L, xb, wv, alpha, args.cpu_seconds, ideal_total)
     else:
         out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+# ------------------------------------------------------------------ whole-model pass
+
+def student_t_gpu(seed, shape, dev, std=0.02, nu=4):
+    """Student-t(4) at std 0.02 drawn on the GPU (z / sqrt(chi2_4 / 4)), as bf16.
+
+    Same distribution and per-layer seed as the host recipe of the parity
+    tests, drawn with torch's Philox generator so that 5.3 B values take well
+    under a second."""
+    g = torch_gen(dev, seed)
+    import torch
+    z = torch.randn(shape, device=dev, generator=g)
+    chi2 = torch.zeros(shape, device=dev)
+    for _ in range(nu):
+        chi2.add_(torch.randn(shape, device=dev, generator=g).square_())
+    w = z.mul_(torch.rsqrt(chi2.div_(nu))).mul_(std / (nu / (nu - 2)) ** 0.5)
+    del chi2
+    return w.to(torch.bfloat16)
+
+
+def torch_gen(dev, seed):
+    import torch
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return g
+
+
+def model_pass(args, dev):
+    """One step = quantize + dequantize of every layer of 30 synthetic DiT
+    blocks (QKV 11520x3840, O 3840x3840, FFN 20480x3840 and 3840x10240): 5.308 B
+    bf16 weights.  Also reports SNR(alpha) - SNR(1) over the whole model."""
+    import numpy as np
+    import torch
+    from w4a16_linear_amd import opq
+    from w4a16_linear_amd import workloads as WL
+
+    alpha = args.alpha
+    shapes = [(f"block{b}.{nm}", 5000 + 4 * b + i, n, k)
+              for b in range(WL.BLOCKS) for i, (nm, n, k) in enumerate(WL.BLOCK_LAYERS)]
+    weights, qws, outs = [], [], {}
+    for _, seed, n, k in shapes:
+        weights.append(student_t_gpu(seed, (n, k), dev))
+        qws.append(opq.QuantizedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
+                                       torch.empty((n, k // 32), dtype=torch.int32, device=dev),
+                                       torch.empty((n,), dtype=torch.float32, device=dev)))
+        if (n, k) not in outs:  # one bf16 output per shape: the pass rewrites it per layer
+            outs[(n, k)] = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    nweights = sum(n * k for _, _, n, k in shapes)
+    alg_q = sum(n * k * 2.625 + 4 * n for _, _, n, k in shapes)
+    alg_d = alg_q
+    stream = torch.cuda.current_stream(dev)
+
+    def quant_all(a):
+        for w, qw in zip(weights, qws):
+            opq.quantize(w, a, out=qw)
+
+    def dequant_all(a):
+        for qw, (_, _, n, k) in zip(qws, shapes):
+            opq.dequantize(qw, a, out=outs[(n, k)])
+
+    for _ in range(args.warmup):
+        quant_all(alpha)
+        dequant_all(alpha)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for _ in range(args.steps):
+        quant_all(alpha)
+        dequant_all(alpha)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(stop) / args.steps
+
+    kern = {}
+    for name, fn, alg in (("quantize", quant_all, alg_q), ("dequantize", dequant_all, alg_d)):
+        per = []
+        for _ in range(3):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn(alpha)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(per))
+        ideal = alg / (HBM_PEAK_GBS * 1e9) * 1e6
+        kern[name] = {"us": round(us, 1), "bound": "hbm", "ideal_us": round(ideal, 1),
+                      "frac": round(ideal / us, 4), "GBps": round(alg / (us * 1e-6) / 1e9, 1),
+                      "algorithmic_bytes": int(alg), "launches": len(shapes)}
+    ideal_total = sum(v["ideal_us"] for v in kern.values())
+
+    # SNR(alpha) - SNR(1) over the whole model (reporting only, not timed)
+    def snr_db(a):
+        num = den = 0.0
+        for w, qw, (_, _, n, k) in zip(weights, qws, shapes):
+            opq.quantize(w, a, out=qw)
+            d = opq.dequantize(qw, a, out=outs[(n, k)])
+            wf = w.float()
+            num += float(wf.double().square().sum())
+            den += float((wf - d.float()).double().square().sum())
+        return 10.0 * np.log10(num / den)
+    snr = {a: snr_db(a) for a in (0.45, 0.73, 1.0)}
+    dom = max(kern, key=lambda kk: kern[kk]["us"])
+    out = {
+        "metric": METRIC,
+        "value": round(100.0 * (ideal_total * 1e-3) / ms_step, 3),
+        "unit": "% of MI355X roofline",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (drawn on the GPU)",
+        "config": {"workload": "model: 30 DiT blocks (QKV 11520x3840, O 3840x3840, FFN "
+                               "20480x3840 + 3840x10240), Student-t(4) std 0.02",
+                   "weights": nweights, "layers": len(shapes), "alpha": alpha,
+                   "step": "quantize every layer -> dequantize every layer"},
+        "roofline": {"bound": "hbm", "achieved": kern[dom]["GBps"], "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(kern[dom]["GBps"] / HBM_PEAK_GBS, 4),
+                     "kernel": dom, "traffic": None},
+        "kernels": kern,
+        "snr_db": {str(a): round(v, 3) for a, v in snr.items()},
+        "snr_gain_vs_alpha1_db": {str(a): round(v - snr[1.0], 3) for a, v in snr.items()},
+        "wall_s": round(wall, 3),
+        "cpu_baseline": None,
+    }
     print(json.dumps(out), flush=True)
 
 
