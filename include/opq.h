@@ -30,8 +30,8 @@
  *   - the caller owns every buffer (scratch comes in as a workspace argument);
  *     the library allocates nothing, frees nothing and synchronises nothing;
  *     its only global state is a mutex-guarded memo of the per-alpha host
- *     tables, so calls are reentrant and thread-safe; outputs must not
- *     overlap inputs;
+ *     tables and, per kernel, a once-computed occupancy figure, so calls are
+ *     reentrant and thread-safe; outputs must not overlap inputs;
  *   - `stream` is a hipStream_t (NULL = the default stream); work is enqueued
  *     on it and the call returns at once; faults inside kernels show up at the
  *     caller's next synchronisation;

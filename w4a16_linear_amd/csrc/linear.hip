@@ -253,7 +253,7 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
 // Only x is staged in LDS (two stages, rows XOR-swizzled by 16-byte chunk).
 
 constexpr int kTM = 256, kTN = 256, kTK = 64;
-constexpr int kMfmaThreads = 256;
+constexpr int kMfmaWaves = 8;   // 8: 32 weight rows per wave, two waves per SIMD (4: 64 rows, one)
 constexpr int kAChunks = kTK / 8;                  // 16-byte chunks per LDS row
 constexpr int kAStage = kTM * kTK;                 // bf16 per stage
 
@@ -263,31 +263,35 @@ constexpr int kAStage = kTM * kTK;                 // bf16 per stage
 // 16-lane passes of ds_read_b128 conflict-free.
 __device__ __forceinline__ int a_off(int r, int c) { return r * kTK + ((c ^ ((r >> 1) & 7)) << 3); }
 
-// Scheduling hint for one sub-step (16 MFMAs): alternate each MFMA with V
+// Scheduling hint for one sub-step (N MFMAs): alternate each MFMA with V
 // VALU instructions so the dequantizer runs in the MFMAs' shadow, and spread
 // the x fragment reads (R), the x stage writes (W) and global loads (G) over
-// the first MFMAs (V = 0 would leave the order to the compiler; 3 measured
-// best for the DiT shapes, ahead of 1, 2, 4, 5, 6).
-constexpr int kInterleaveV = 3;
+// the first MFMAs.  V = 0 leaves the order to the compiler.  With one wave per
+// SIMD, V = 3 measured best; with two waves per SIMD (the default) the other
+// wave fills the MFMA shadow and the hints only cost registers (V = 3 spills).
+constexpr int kInterleaveV = 0;
 
-template <int I, int V, int R, int W, int G>
+template <int I, int N, int V, int R, int W, int G>
 __device__ __forceinline__ void interleave_substep() {
-  if constexpr (V > 0 && I < 16) {
+  if constexpr (V > 0 && I < N) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
     if constexpr (I < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     if constexpr (I < W) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
     if constexpr (I < G) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
     __builtin_amdgcn_sched_group_barrier(0x002, V, 0);          // VALU
-    interleave_substep<I + 1, V, R, W, G>();
+    interleave_substep<I + 1, N, V, R, W, G>();
   }
 }
 
-template <bool kHalfTail>
-__global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
+template <bool kHalfTail, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
     const float* __restrict__ bias, int m, int n, int k, int tiles_m, Levels lv,
     void* __restrict__ y, int y_bf16) {
+  constexpr int kThreads = WAVES * kWave;
+  constexpr int NF = 8 / WAVES;                     // 32-row weight fragments per wave
+  constexpr int XCH = kTM * kTK / 8 / kThreads;     // x chunks each thread stages per step
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kAStage];
 
   const int tid = threadIdx.x;
@@ -296,21 +300,21 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
   // consecutive blocks share a weight tile and walk the x tiles
   const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
   const int m0 = tile_m * kTM;
-  const int nw = tile_n * kTN + wave * 64;       // first weight row of this wave
+  const int nw = tile_n * kTN + wave * 32 * NF;  // first weight row of this wave
   const int g = lane >> 5;                        // which half of the k step
   const int kwords = k / 8, swords = k / 32;
   const int nsteps = (k + kTK - 1) / kTK;
 
-  // This lane's two weight rows (B fragments f = 0, 1).  Rows past n are
-  // clamped to row n - 1: their columns are computed and never stored.
-  int brow[2];
-  RowLut lut[2];
-  uint32_t pw_off[2], sw_off[2];  // byte offsets from the wave's first row
+  // This lane's weight rows (B fragments f < NF).  Rows past n are clamped to
+  // row n - 1: their columns are computed and never stored.
+  int brow[NF];
+  RowLut lut[NF];
+  uint32_t pw_off[NF], sw_off[NF];  // byte offsets from the wave's first row
   const int nw_c = min(nw, n - 1);
   const char* pbase = reinterpret_cast<const char*>(packed + (int64_t)nw_c * kwords);
   const char* sbase = reinterpret_cast<const char*>(sign + (int64_t)nw_c * swords);
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < NF; ++f) {
     brow[f] = nw + 32 * f + (lane & 31);
     const int rc = min(brow[f], n - 1);
     lut[f] = make_row_lut(lv, scale[rc]);
@@ -322,60 +326,60 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
   // the end re-read the last one (every prefetch is issued unconditionally, so
   // the wait counts stay static); in a final half step (k % 64 == 32) lanes
   // g = 1 re-read the first half and the dequantizer zeroes their fragments.
-  auto load_b = [&](int kt, uint4 (&pw)[2], uint32_t (&sw)[2]) {
+  auto load_b = [&](int kt, uint4 (&pw)[NF], uint32_t (&sw)[NF]) {
     const int kc = min(min(kt, nsteps - 1) * kTK + 32 * g, k - 32);
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < NF; ++f) {
       pw[f] = *reinterpret_cast<const uint4*>(pbase + pw_off[f] + (uint32_t)kc / 2u);
       sw[f] = *reinterpret_cast<const uint32_t*>(sbase + sw_off[f] + (uint32_t)kc / 8u);
     }
   };
-  // x of step kt: thread tid moves chunks tid + 256 i (row c/8, chunk c%8).
+  // x of step kt: thread tid moves chunks tid + kThreads i (row c/8, chunk c%8).
   // Rows past m read row m - 1 (never stored); chunks past k read the last
   // chunk, which only meets zero weights.
   const char* xbase = reinterpret_cast<const char*>(x + (int64_t)m0 * k);
-  uint32_t x_off[8];
+  uint32_t x_off[XCH];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int c = tid + kMfmaThreads * i;
+  for (int i = 0; i < XCH; ++i) {
+    const int c = tid + kThreads * i;
     const int r = min(m0 + (c >> 3), m - 1) - m0;
     x_off[i] = ((uint32_t)r * (uint32_t)k + 8u * (uint32_t)(c & 7)) * 2u;
   }
-  auto load_a = [&](int kt, uint4 (&xa)[8]) {
+  auto load_a = [&](int kt, uint4 (&xa)[XCH]) {
     const int kc = min(kt, nsteps - 1) * kTK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < XCH; ++i) {
       uint32_t off = x_off[i] + (uint32_t)kc * 2u;
       if constexpr (kHalfTail) {
-        const int c = tid + kMfmaThreads * i;
+        const int c = tid + kThreads * i;
         if (kc + 8 * (c & 7) >= k) off -= 64u;  // step back into the row
       }
       xa[i] = *reinterpret_cast<const uint4*>(xbase + off);
     }
   };
-  auto store_a = [&](int stage, const uint4 (&xa)[8]) {
+  auto store_a = [&](int stage, const uint4 (&xa)[XCH]) {
     uint16_t* base = s_a + stage * kAStage;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int c = tid + kMfmaThreads * i;
+    for (int i = 0; i < XCH; ++i) {
+      const int c = tid + kThreads * i;
       *reinterpret_cast<uint4*>(base + a_off(c >> 3, c & 7)) = sigma_order(xa[i]);
     }
   };
 
-  floatx16_t acc[8][2];
+  floatx16_t acc[8][NF];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int f = 0; f < 2; ++f)
+    for (int f = 0; f < NF; ++f)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][f][e] = 0.0f;
 
   // Sub-step s of a k step: dequantize word s of both B fragments, read the
   // eight x fragments of k-blocks {s, 4 + s}.
-  auto dequant_b = [&](int kt, int s, const uint4 (&pwv)[2], const uint32_t (&swv)[2],
-                       bf16x8_t (&b)[2]) {
+  auto dequant_b = [&](int kt, int s, const uint4 (&pwv)[NF], const uint32_t (&swv)[NF],
+                       bf16x8_t (&b)[NF]) {
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < NF; ++f) {
       const uint32_t words[4] = {pwv[f].x, pwv[f].y, pwv[f].z, pwv[f].w};
       uint32_t o[4];
       dequant_word(words[s], swv[f] >> (8 * s), lut[f], o);
@@ -403,10 +407,10 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
   // The barrier orders every wave's store into the other stage (sub-step 0)
   // before its reads, and every read of this stage (last issued in sub-step
   // 2) before the next step's store into it.
-  uint4 pw[2], pw_next[2];
-  uint32_t sw[2], sw_next[2];
-  uint4 xa[8];
-  bf16x8_t a_buf[2][8], b_buf[2][2];
+  uint4 pw[NF], pw_next[NF];
+  uint32_t sw[NF], sw_next[NF];
+  uint4 xa[XCH];
+  bf16x8_t a_buf[2][8], b_buf[2][NF];
   if (nsteps > 0) {
     load_a(0, xa);
     load_b(0, pw, sw);
@@ -435,19 +439,19 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
 #pragma unroll
       for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-        for (int f = 0; f < 2; ++f)
+        for (int f = 0; f < NF; ++f)
           acc[mi][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_buf[cur][mi], b_buf[cur][f],
                                                                acc[mi][f], 0, 0, 0);
       if (s == 0) {
         store_a(stage ^ 1, xa);
         load_a(kt + 2, xa);
-        interleave_substep<0, kInterleaveV + 2, 8, 8, 12>();
+        interleave_substep<0, 8 * NF, kInterleaveV + 2, 8, XCH, XCH + NF * 2>();
       } else {
-        interleave_substep<0, kInterleaveV, 8, 0, 0>();
+        interleave_substep<0, 8 * NF, kInterleaveV, 8, 0, 0>();
       }
     }
 #pragma unroll
-    for (int f = 0; f < 2; ++f) {
+    for (int f = 0; f < NF; ++f) {
       pw[f] = pw_next[f];
       sw[f] = sw_next[f];
     }
@@ -456,7 +460,7 @@ __global__ __launch_bounds__(kMfmaThreads, 1) void linear_mfma(
   // 32x32 accumulator layout: register e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32.
 #pragma unroll
-  for (int f = 0; f < 2; ++f) {
+  for (int f = 0; f < NF; ++f) {
     const int col = brow[f];
     const float bv = (bias && col < n) ? bias[col] : 0.0f;
 #pragma unroll
@@ -483,8 +487,8 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32
                        sign, scale, bias, (int)m, (int)n, (int)k, lv, y, (int)y_bf16);
   } else {
     const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
-    auto kernel = (k % kTK) ? linear_mfma<true> : linear_mfma<false>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMfmaThreads), 0, stream,
+    auto kernel = (k % kTK) ? linear_mfma<true, kMfmaWaves> : linear_mfma<false, kMfmaWaves>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMfmaWaves * kWave), 0, stream,
                        x, packed, sign, scale, bias, (int)m, (int)n, (int)k, (int)tiles_m, lv, y,
                        (int)y_bf16);
   }

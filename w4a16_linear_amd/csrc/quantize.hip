@@ -364,6 +364,106 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
   }
 }
 
+// ---------------------------------------------------------------- block-per-row kernel
+//
+// A block of 256 threads owns one row at a time: thread t holds elements
+// c*2048 + 8t .. c*2048 + 8t + 7 of chunk c (NCT chunks, k <= NCT * 2048), so a
+// wave's share of a row is a quarter of the one-wave-per-row kernel's and the
+// encode tail after the last load is short.  Blocks stay resident and stride
+// over rows; the next row's loads are issued before the current row is
+// encoded, into the other register buffer.  The row max meets in LDS behind a
+// barrier that waits for LDS traffic only, so those loads stay in flight.
+
+constexpr int kBlockThreads = 256;
+constexpr int kBlockChunk = kBlockThreads * 8;  // elements per block-wide chunk
+constexpr int kPersistBlocks = 2048;
+
+// Store word `wi` of a row and, from the first lane of each quad, the sign word
+// wi / 4 made of the quad's four sign bytes.
+__device__ __forceinline__ void store_word(uint32_t* prow, uint32_t* srow, int wi, int lane,
+                                           bool valid, uint32_t word, uint32_t sbyte) {
+  uint32_t s32 = valid ? (sbyte << (8 * (lane & 3))) : 0u;
+  s32 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)s32, 0xB1, 0xF, 0xF, false);
+  s32 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)s32, 0x4E, 0xF, 0xF, false);
+  if (valid) {
+    prow[wi] = word;
+    if ((lane & 3) == 0) srow[wi >> 2] = s32;
+  }
+}
+
+template <typename T, int NCT>
+__global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
+    const T* __restrict__ w, int64_t n, int k, DecisionPoints dp, BucketGrid g,
+    uint32_t* __restrict__ packed, uint32_t* __restrict__ sign, float* __restrict__ scale) {
+  __shared__ uint2 s_tab[kMaxBuckets];
+  __shared__ float s_pts[kLevels + 1];
+  __shared__ float s_wmax[2][kBlockThreads / kWave];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int64_t stride = gridDim.x;
+
+  Slot<T> v[2][NCT];
+  auto load_row = [&](int64_t rr, int buf) __attribute__((always_inline)) {
+    const T* wr = w + rr * (int64_t)k;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int e0 = c * kBlockChunk + tid * 8;
+      if (e0 < k) v[buf][c].load(wr + e0); else v[buf][c].zero();
+    }
+  };
+  int64_t row = blockIdx.x;
+  if (row < n) load_row(row, 0);
+
+  build_table(dp, g, s_tab);
+  if (tid == 0) {
+#pragma unroll
+    for (int j = 0; j < kLevels; ++j) s_pts[j] = dp.t[j];
+    s_pts[kLevels] = 2.0f;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the table is written
+  __builtin_amdgcn_s_barrier();
+  const int shift = g.shift;
+  const uint32_t nbase = (0u - (g.b0 >> g.shift)) << 3;
+  const float ulo = __uint_as_float(g.b0);
+
+  // Encode the row held in buffer `buf`; `ms` picks the LDS slot of its max
+  // (slots alternate, so one barrier per row keeps writes after old reads).
+  auto process = [&](int64_t rr, int buf, int ms) __attribute__((always_inline)) {
+    typename Slot<T>::Acc acc = Slot<T>::acc0();
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) v[buf][c].absmax(acc);
+    float mx = wave_max(Slot<T>::finish(acc));
+    if (lane == 0) s_wmax[ms][wave] = mx;
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    mx = fmaxf(fmaxf(s_wmax[ms][0], s_wmax[ms][1]), fmaxf(s_wmax[ms][2], s_wmax[ms][3]));
+    const bool fast = mx >= 0x1p-125f && mx <= 0x1p125f;  // 1/m normal, u' <= 1 + ulps
+    const float r = 1.0f / mx;
+    uint32_t* prow = packed + rr * (int64_t)(k / 8);
+    uint32_t* srow = sign + rr * (int64_t)(k / 32);
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int e0 = c * kBlockChunk + tid * 8;
+      const uint32_t word = encode_chunk(v[buf][c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts);
+      store_word(prow, srow, e0 >> 3, lane, e0 < k, word, sign_byte(v[buf][c]));
+    }
+    if (tid == 0) scale[rr] = mx;
+  };
+
+  // Rows alternate between the two buffers (register arrays need constant indices).
+  while (row < n) {
+    const int64_t r1 = row + stride;
+    if (r1 < n) load_row(r1, 1);
+    process(row, 0, 0);
+    if (r1 >= n) break;
+    const int64_t r2 = r1 + stride;
+    if (r2 < n) load_row(r2, 0);
+    process(r1, 1, 1);
+    row = r2;
+  }
+}
+
 // Encode against per-row magnitude thresholds A_1..A_15 (fallback kernel).
 template <typename T>
 __device__ __forceinline__ uint32_t encode8(const Slot<T>& s, const float (&A)[kLevels]) {
@@ -467,9 +567,52 @@ hipError_t launch_rows(const T* w, int64_t n, int64_t k, const DecisionPoints& d
   return hipGetLastError();
 }
 
+// Blocks of the strided kernel that fit on the device at once (the grid must
+// not exceed it: a block waiting for a slot would start only after another
+// block had finished all of its rows).  Per-CU occupancy is computed once per
+// kernel; the CU count is asked of the current device per call.
+template <typename T, int NCT>
+int64_t resident_blocks() {
+  static const int per_cu = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, quantize_block_rows<T, NCT>,
+                                                     kBlockThreads, 0) != hipSuccess || b < 1)
+      b = 1;
+    return b;
+  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 1;
+  return (int64_t)per_cu * cus;
+}
+
+template <typename T, int NCT>
+hipError_t launch_block_rows(const T* w, int64_t n, int64_t k, const DecisionPoints& dp,
+                             const BucketGrid& g, uint32_t* packed, uint32_t* sign, float* scale,
+                             hipStream_t stream) {
+  int64_t blocks = resident_blocks<T, NCT>();
+  if (blocks > kPersistBlocks) blocks = kPersistBlocks;
+  if (blocks > n) blocks = n;
+  hipLaunchKernelGGL((quantize_block_rows<T, NCT>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
+                     stream, w, n, (int)k, dp, g, packed, sign, scale);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t dispatch(const T* w, int64_t n, int64_t k, const DecisionPoints& dp, uint32_t* packed,
                     uint32_t* sign, float* scale, hipStream_t stream) {
+  BucketGrid g;
+  if (bucket_grid(dp, g)) {
+    const int64_t nct = (k + kBlockChunk - 1) / kBlockChunk;
+    if (nct <= 1) return launch_block_rows<T, 1>(w, n, k, dp, g, packed, sign, scale, stream);
+    if (nct <= 2) return launch_block_rows<T, 2>(w, n, k, dp, g, packed, sign, scale, stream);
+    if (nct <= 3) return launch_block_rows<T, 3>(w, n, k, dp, g, packed, sign, scale, stream);
+    if (nct <= 4) return launch_block_rows<T, 4>(w, n, k, dp, g, packed, sign, scale, stream);
+    if (nct <= 5) return launch_block_rows<T, 5>(w, n, k, dp, g, packed, sign, scale, stream);
+    if (nct <= 6) return launch_block_rows<T, 6>(w, n, k, dp, g, packed, sign, scale, stream);
+    if (nct <= 8) return launch_block_rows<T, 8>(w, n, k, dp, g, packed, sign, scale, stream);
+  }
   const int64_t nch = (k + kChunk - 1) / kChunk;
   // bf16 slots take 4 VGPRs per chunk, fp32 slots 8: fp32 rows stay in
   // registers up to 16 chunks, bf16 rows up to 32.
