@@ -253,7 +253,8 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
 // Only x is staged in LDS (two stages, rows XOR-swizzled by 16-byte chunk).
 
 constexpr int kTM = 256, kTN = 256, kTK = 64;
-constexpr int kMfmaWaves = 8;   // 8: 32 weight rows per wave, two waves per SIMD (4: 64 rows, one)
+constexpr int kMfmaWaves = 8;   // waves per 256x256 tile (8: two per SIMD)
+constexpr int kMfmaXSplit = 1;  // waves sharing a weight row, each with 256 / kMfmaXSplit x rows
 constexpr int kAChunks = kTK / 8;                  // 16-byte chunks per LDS row
 constexpr int kAStage = kTM * kTK;                 // bf16 per stage
 
@@ -283,14 +284,16 @@ __device__ __forceinline__ void interleave_substep() {
   }
 }
 
-template <bool kHalfTail, int WAVES>
+template <bool kHalfTail, int WAVES, int XSPLIT>
 __global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
     const float* __restrict__ bias, int m, int n, int k, int tiles_m, Levels lv,
     void* __restrict__ y, int y_bf16) {
   constexpr int kThreads = WAVES * kWave;
-  constexpr int NF = 8 / WAVES;                     // 32-row weight fragments per wave
+  constexpr int WG = WAVES / XSPLIT;                // weight groups (waves sharing x rows)
+  constexpr int NF = 8 / WG;                        // 32-row weight fragments per wave
+  constexpr int MI = 8 / XSPLIT;                    // 32-row x blocks per wave
   constexpr int XCH = kTM * kTK / 8 / kThreads;     // x chunks each thread stages per step
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kAStage];
 
@@ -300,7 +303,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
   // consecutive blocks share a weight tile and walk the x tiles
   const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
   const int m0 = tile_m * kTM;
-  const int nw = tile_n * kTN + wave * 32 * NF;  // first weight row of this wave
+  const int wg = wave % WG, xh = wave / WG;
+  const int nw = tile_n * kTN + wg * 32 * NF;    // first weight row of this wave
+  const int mx0 = xh * 32 * MI;                   // first x row of this wave in the tile
   const int g = lane >> 5;                        // which half of the k step
   const int kwords = k / 8, swords = k / 32;
   const int nsteps = (k + kTK - 1) / kTK;
@@ -366,9 +371,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
     }
   };
 
-  floatx16_t acc[8][NF];
+  floatx16_t acc[MI][NF];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < MI; ++i)
 #pragma unroll
     for (int f = 0; f < NF; ++f)
 #pragma unroll
@@ -389,10 +394,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
       b[f] = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
     }
   };
-  auto read_a = [&](const uint16_t* sa, int s, bf16x8_t (&a)[8]) {
+  auto read_a = [&](const uint16_t* sa, int s, bf16x8_t (&a)[MI]) {
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
-      a[mi] = *reinterpret_cast<const bf16x8_t*>(sa + a_off(mi * 32 + (lane & 31), 4 * g + s));
+    for (int mi = 0; mi < MI; ++mi)
+      a[mi] = *reinterpret_cast<const bf16x8_t*>(sa + a_off(mx0 + mi * 32 + (lane & 31), 4 * g + s));
   };
 
   // Pipeline per k step kt (x in LDS stage kt & 1); fragments of sub-step 0
@@ -410,7 +415,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
   uint4 pw[NF], pw_next[NF];
   uint32_t sw[NF], sw_next[NF];
   uint4 xa[XCH];
-  bf16x8_t a_buf[2][8], b_buf[2][NF];
+  bf16x8_t a_buf[2][MI], b_buf[2][NF];
   if (nsteps > 0) {
     load_a(0, xa);
     load_b(0, pw, sw);
@@ -437,7 +442,7 @@ __global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
         dequant_b(kt + 1, 0, pw_next, sw_next, b_buf[nxt]);
       }
 #pragma unroll
-      for (int mi = 0; mi < 8; ++mi)
+      for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
         for (int f = 0; f < NF; ++f)
           acc[mi][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_buf[cur][mi], b_buf[cur][f],
@@ -445,9 +450,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
       if (s == 0) {
         store_a(stage ^ 1, xa);
         load_a(kt + 2, xa);
-        interleave_substep<0, 8 * NF, kInterleaveV + 2, 8, XCH, XCH + NF * 2>();
+        interleave_substep<0, MI * NF, kInterleaveV + 2, MI, XCH, XCH + NF * 2>();
       } else {
-        interleave_substep<0, 8 * NF, kInterleaveV, 8, 0, 0>();
+        interleave_substep<0, MI * NF, kInterleaveV, MI, 0, 0>();
       }
     }
 #pragma unroll
@@ -464,10 +469,10 @@ __global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
     const int col = brow[f];
     const float bv = (bias && col < n) ? bias[col] : 0.0f;
 #pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = m0 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+        const int row = m0 + mx0 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
         if (row < m && col < n) store_y(y, y_bf16, (int64_t)row * n + col, acc[mi][f][e] + bv);
       }
   }
@@ -487,7 +492,8 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32
                        sign, scale, bias, (int)m, (int)n, (int)k, lv, y, (int)y_bf16);
   } else {
     const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
-    auto kernel = (k % kTK) ? linear_mfma<true, kMfmaWaves> : linear_mfma<false, kMfmaWaves>;
+    auto kernel = (k % kTK) ? linear_mfma<true, kMfmaWaves, kMfmaXSplit>
+                            : linear_mfma<false, kMfmaWaves, kMfmaXSplit>;
     hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMfmaWaves * kWave), 0, stream,
                        x, packed, sign, scale, bias, (int)m, (int)n, (int)k, (int)tiles_m, lv, y,
                        (int)y_bf16);
