@@ -255,6 +255,7 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
 constexpr int kTM = 256, kTN = 256, kTK = 64;
 constexpr int kMfmaWaves = 8;   // waves per 256x256 tile (8: two per SIMD)
 constexpr int kMfmaXSplit = 1;  // waves sharing a weight row, each with 256 / kMfmaXSplit x rows
+constexpr bool kWeightStage = true;  // linear_mfma_ws (weights through LDS) instead of linear_mfma
 constexpr int kAChunks = kTK / 8;                  // 16-byte chunks per LDS row
 constexpr int kAStage = kTM * kTK;                 // bf16 per stage
 
@@ -478,6 +479,198 @@ __global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
   }
 }
 
+// Eight-wave tile with the weights staged through LDS.  Every two k steps the
+// block loads its 256 weight rows x 64 bytes of codes (and the two steps' sign
+// words) with loads in which each group of four lanes reads 64 contiguous
+// bytes, two steps before use, into one of two LDS stages of 80-byte row
+// records (codes of the two steps, then their sign words: a stride that keeps
+// the 32-row fragment reads below free of bank conflicts).  Wave w reads the
+// codes of its rows 32w .. 32w + 31 for a step with one ds_read_b128 and one
+// ds_read_b32 per lane.  Everything else is as in linear_mfma.
+constexpr int kWRec = 20;  // uint32 per weight row record: 16 code words + 4 sign words
+
+template <bool kHalfTail>
+__global__ __launch_bounds__(512, 1) void linear_mfma_ws(
+    const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
+    const uint32_t* __restrict__ sign, const float* __restrict__ scale,
+    const float* __restrict__ bias, int m, int n, int k, int tiles_m, Levels lv,
+    void* __restrict__ y, int y_bf16) {
+  constexpr int kThreads = 512;
+  constexpr int XCH = kTM * kTK / 8 / kThreads;     // x chunks each thread stages per step (4)
+  __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kAStage];
+  __shared__ __attribute__((aligned(16))) uint32_t s_w[2][kTN][kWRec];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
+  const int m0 = tile_m * kTM;
+  const int n0 = tile_n * kTN;
+  const int nw = n0 + wave * 32;                  // first weight row of this wave
+  const int g = lane >> 5;                        // which half of the k step
+  const int kwords = k / 8, swords = k / 32;
+  const int nsteps = (k + kTK - 1) / kTK;
+  const int npairs = (nsteps + 1) / 2;
+
+  const int brow = nw + (lane & 31);
+  const RowLut lut = make_row_lut(lv, scale[min(brow, n - 1)]);
+
+  // Weight loads for step pair p (steps 2p, 2p + 1): thread t moves 16 code
+  // bytes (quarter t % 4) of tile rows t/4 and t/4 + 128, and sign words
+  // 2(t%2), 2(t%2) + 1 of the pair for tile row t/2.  Rows past n read row
+  // n - 1; parts past k read the row's last 16 code bytes or last sign word
+  // (only ever met by zeroed fragments or steps that are never used).
+  const int wq = tid & 3;
+  const int n0c = min(n0, n - 1);
+  const char* pbase = reinterpret_cast<const char*>(packed + (int64_t)n0c * kwords);
+  const uint32_t* sbase = sign + (int64_t)n0c * swords;
+  const uint32_t pa_off = (uint32_t)(min(n0 + (tid >> 2), n - 1) - n0c) * (uint32_t)kwords * 4u;
+  const uint32_t pb_off = (uint32_t)(min(n0 + 128 + (tid >> 2), n - 1) - n0c) * (uint32_t)kwords * 4u;
+  const uint32_t s_off = (uint32_t)(min(n0 + (tid >> 1), n - 1) - n0c) * (uint32_t)swords;
+  uint4 wv[2];
+  uint32_t wsg[2];
+  auto load_w = [&](int p) __attribute__((always_inline)) {
+    const int pc = min(p, npairs - 1);
+    const uint32_t e = (uint32_t)min(pc * 2 * kTK + 32 * wq, k - 32);  // first element of the part
+    wv[0] = *reinterpret_cast<const uint4*>(pbase + pa_off + e / 2u);
+    wv[1] = *reinterpret_cast<const uint4*>(pbase + pb_off + e / 2u);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wsg[i] = sbase[s_off + (uint32_t)min(pc * 4 + 2 * (tid & 1) + i, swords - 1)];
+  };
+  auto store_w = [&](int p) __attribute__((always_inline)) {
+    uint32_t (*st)[kWRec] = s_w[p & 1];
+    *reinterpret_cast<u32x4_t*>(&st[tid >> 2][4 * wq]) = u32x4_t{wv[0].x, wv[0].y, wv[0].z, wv[0].w};
+    *reinterpret_cast<u32x4_t*>(&st[128 + (tid >> 2)][4 * wq]) = u32x4_t{wv[1].x, wv[1].y, wv[1].z, wv[1].w};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) st[tid >> 1][16 + 2 * (tid & 1) + i] = wsg[i];
+  };
+  // This lane's codes and sign word of step kt (from stage (kt/2) & 1).
+  auto read_w = [&](int kt, uint4& pw, uint32_t& sw) __attribute__((always_inline)) {
+    const uint32_t* rec = s_w[(kt >> 1) & 1][wave * 32 + (lane & 31)];
+    const int half = kt & 1;
+    pw = *reinterpret_cast<const uint4*>(rec + 8 * half + 4 * g);
+    sw = rec[16 + 2 * half + g];
+  };
+
+  const char* xbase = reinterpret_cast<const char*>(x + (int64_t)m0 * k);
+  uint32_t x_off[XCH];
+#pragma unroll
+  for (int i = 0; i < XCH; ++i) {
+    const int c = tid + kThreads * i;
+    const int r = min(m0 + (c >> 3), m - 1) - m0;
+    x_off[i] = ((uint32_t)r * (uint32_t)k + 8u * (uint32_t)(c & 7)) * 2u;
+  }
+  auto load_a = [&](int kt, uint4 (&xa)[XCH]) __attribute__((always_inline)) {
+    const int kc = min(kt, nsteps - 1) * kTK;
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      uint32_t off = x_off[i] + (uint32_t)kc * 2u;
+      if constexpr (kHalfTail) {
+        const int c = tid + kThreads * i;
+        if (kc + 8 * (c & 7) >= k) off -= 64u;  // step back into the row
+      }
+      xa[i] = *reinterpret_cast<const uint4*>(xbase + off);
+    }
+  };
+  auto store_a = [&](int stage, const uint4 (&xa)[XCH]) __attribute__((always_inline)) {
+    uint16_t* base = s_a + stage * kAStage;
+#pragma unroll
+    for (int i = 0; i < XCH; ++i) {
+      const int c = tid + kThreads * i;
+      const uint4 v = sigma_order(xa[i]);
+      *reinterpret_cast<u32x4_t*>(base + a_off(c >> 3, c & 7)) = u32x4_t{v.x, v.y, v.z, v.w};
+    }
+  };
+
+  floatx16_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+
+  auto dequant_b = [&](int kt, int s, const uint4& pwv, uint32_t swv, bf16x8_t& b)
+      __attribute__((always_inline)) {
+    const uint32_t words[4] = {pwv.x, pwv.y, pwv.z, pwv.w};
+    uint32_t o[4];
+    dequant_word(words[s], swv >> (8 * s), lut, o);
+    if constexpr (kHalfTail) {
+      if (kt == nsteps - 1 && g == 1) o[0] = o[1] = o[2] = o[3] = 0u;
+    }
+    b = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+  };
+  auto read_a = [&](const uint16_t* sa, int s, bf16x8_t (&a)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+      a[mi] = *reinterpret_cast<const bf16x8_t*>(sa + a_off(mi * 32 + (lane & 31), 4 * g + s));
+  };
+
+  // Step pair q is stored at step 2q - 2 (sub-step 0) from registers loaded at
+  // step 2q - 4, and first read at step 2q - 1 after that step's barrier; the
+  // stage it overwrites last served step 2q - 3, read at step 2q - 4.
+  uint4 pw;        // codes of the current step (read at the previous step's sub-step 3)
+  uint32_t sw;
+  uint4 xa[XCH];
+  bf16x8_t a_buf[2][8], b_buf[2];
+  if (nsteps > 0) {
+    load_a(0, xa);
+    load_w(0);
+    store_a(0, xa);
+    store_w(0);
+    load_a(1, xa);
+    load_w(1);
+    __syncthreads();
+    read_w(0, pw, sw);
+    read_a(s_a, 0, a_buf[0]);
+    dequant_b(0, 0, pw, sw, b_buf[0]);
+  }
+
+  auto step = [&](int kt, bool even) __attribute__((always_inline)) {
+    const int stage = kt & 1;
+    const uint16_t* sa = s_a + stage * kAStage;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int cur = s & 1, nxt = cur ^ 1;
+      if (s < 3) {
+        read_a(sa, s + 1, a_buf[nxt]);
+        dequant_b(kt, s + 1, pw, sw, b_buf[nxt]);
+      } else {
+        __syncthreads();
+        read_a(s_a + (stage ^ 1) * kAStage, 0, a_buf[nxt]);
+        read_w(kt + 1, pw, sw);  // this step's words are dead after sub-step 2
+        dequant_b(kt + 1, 0, pw, sw, b_buf[nxt]);
+      }
+#pragma unroll
+      for (int mi = 0; mi < 8; ++mi)
+        acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_buf[cur][mi], b_buf[cur], acc[mi], 0, 0, 0);
+      if (s == 0) {
+        store_a(stage ^ 1, xa);
+        load_a(kt + 2, xa);
+        if (even) {
+          store_w(kt / 2 + 1);
+          load_w(kt / 2 + 2);
+        }
+      }
+    }
+  };
+  int kt = 0;
+  for (; kt + 1 < nsteps; kt += 2) {
+    step(kt, true);
+    step(kt + 1, false);
+  }
+  if (kt < nsteps) step(kt, true);
+
+  // 32x32 accumulator layout: register e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
+  // column l%32.
+  const float bv = (bias && brow < n) ? bias[brow] : 0.0f;
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = m0 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
+      if (row < m && brow < n) store_y(y, y_bf16, (int64_t)row * n + brow, acc[mi][e] + bv);
+    }
+}
+
 }  // namespace
 
 size_t linear_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
@@ -492,9 +685,11 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32
                        sign, scale, bias, (int)m, (int)n, (int)k, lv, y, (int)y_bf16);
   } else {
     const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
-    auto kernel = (k % kTK) ? linear_mfma<true, kMfmaWaves, kMfmaXSplit>
-                            : linear_mfma<false, kMfmaWaves, kMfmaXSplit>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMfmaWaves * kWave), 0, stream,
+    auto kernel = kWeightStage ? ((k % kTK) ? linear_mfma_ws<true> : linear_mfma_ws<false>)
+                  : ((k % kTK) ? linear_mfma<true, kMfmaWaves, kMfmaXSplit>
+                               : linear_mfma<false, kMfmaWaves, kMfmaXSplit>);
+    const int threads = kWeightStage ? 512 : kMfmaWaves * kWave;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(threads), 0, stream,
                        x, packed, sign, scale, bias, (int)m, (int)n, (int)k, (int)tiles_m, lv, y,
                        (int)y_bf16);
   }
