@@ -48,7 +48,7 @@ SIGNS_PER_WORD = 32  # "32 个打包进 1 个 uint32"
 __all__ = [
     "LEVELS", "alpha_f32", "bf16_bits_to_f32", "f64_to_bf16_bits", "row_absmax",
     "encode", "pack", "unpack", "quantize", "reconstruct", "dequantize",
-    "linear", "snr_db", "decision_thresholds_f32",
+    "linear", "snr_db", "error_sums", "decision_thresholds_f32",
 ]
 
 
@@ -199,6 +199,19 @@ def linear(x_bf16: np.ndarray, wdq_bf16: np.ndarray, bias=None) -> np.ndarray:
     if bias is not None:
         y = y + np.asarray(bias, dtype=np.float64)[None, :]
     return y
+
+
+def error_sums(w32: np.ndarray, alpha: float) -> np.ndarray:
+    """Per row of w[N, K]: (sum w^2, sum (w - w')^2) in float64, w' the bfloat16
+    reconstruction of w's stored form (quantize then dequantize).  The card's
+    section "为什么 α=0.73？" picks alpha from the flat optimum of this error;
+    "OPQ 原理" compares it against uniform rounding (alpha = 1)."""
+    w32 = np.ascontiguousarray(w32, dtype=np.float32)
+    packed, sign, scale = quantize(w32, alpha)
+    w_rec = bf16_bits_to_f32(dequantize(packed, sign, scale, alpha)).astype(np.float64)
+    w64 = w32.astype(np.float64)
+    e = w64 - w_rec
+    return np.stack([np.sum(w64 * w64, axis=1), np.sum(e * e, axis=1)], axis=1)
 
 
 def snr_db(w: np.ndarray, w_rec: np.ndarray) -> float:

@@ -54,6 +54,10 @@ MUTATIONS = {
     "sign_of_zero": ("s = (w32 < 0).astype(np.uint8)", "s = (w32 <= 0).astype(np.uint8)"),
     # bias subtracted
     "bias_sign": ("y = y + np.asarray(bias", "y = y - np.asarray(bias"),
+    # reconstruction error taken with the wrong sign
+    "error_sign": ("    e = w64 - w_rec\n", "    e = w64 + w_rec\n"),
+    # error measured against the float32 input instead of its reconstruction
+    "error_self": ("    e = w64 - w_rec\n", "    e = w64 - w64.astype(np.float32)\n"),
 }
 
 

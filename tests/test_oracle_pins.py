@@ -417,3 +417,63 @@ def test_snr_closed_form():
     e = w.astype(np.float64) - d.astype(np.float64)
     assert math.isclose(snr, 10 * math.log10(np.sum(w.astype(np.float64) ** 2) / np.sum(e ** 2)))
     assert O.snr_db(d, d) == math.inf
+
+
+# ------------------------------------------------------------------ error sums (alpha sweep)
+
+def _exact_code(u: Fraction, alpha_num: int) -> int:
+    """round(15 u) for alpha = 1, halves up, in exact arithmetic."""
+    v = 15 * u
+    fl = v.numerator // v.denominator
+    return fl + (1 if v - fl >= Fraction(1, 2) else 0)
+
+
+def test_error_sums_closed_form_alpha1():
+    """alpha = 1: codes are round(15 u) on the binary32 quotient and the
+    reconstruction is bf16((q/15) m); the squared error is summed exactly."""
+    m = np.float32(0.7)
+    vals = [m, m / 2, np.float32(m / 3), -np.float32(m / 7), np.float32(0.05), -np.float32(0.31),
+            np.float32(1e-3), np.float32(0.0)]
+    w = np.zeros((1, 32), np.float32)
+    w[0, :len(vals)] = vals
+    got = O.error_sums(w, 1.0)
+    mf = Fraction(float(m))
+    sw2 = Fraction(0)
+    se2 = Fraction(0)
+    for a in w[0]:
+        af = Fraction(float(a))
+        sw2 += af * af
+        u = exact_quotient_f32(np.float32(abs(a)), m)
+        q = _exact_code(u, 1)
+        rec = round_fraction(Fraction(q, 15) * mf, 8)
+        if a < 0:
+            rec = -rec
+        se2 += (af - rec) ** 2
+    assert got.shape == (1, 2)
+    assert math.isclose(got[0, 0], float(sw2), rel_tol=1e-15)
+    assert math.isclose(got[0, 1], float(se2), rel_tol=1e-12)
+
+
+@pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0])
+def test_error_sums_zero_on_reconstructions(alpha):
+    """bfloat16 weights that already are reconstructions come back exactly (the
+    row max, a bfloat16 value, reconstructs to itself), so their error sum is 0."""
+    rng = np.random.default_rng(31)
+    w = (rng.standard_t(4, (6, 64)) * 0.02).astype(np.float32)
+    w = torch.from_numpy(w).to(torch.bfloat16).float().numpy()  # bfloat16 values
+    w[2] = 0.0
+    d = O.bf16_bits_to_f32(O.dequantize(*O.quantize(w, alpha), alpha))
+    got = O.error_sums(d, alpha)
+    assert np.all(got[:, 1] == 0.0)
+    assert np.allclose(got[:, 0], np.sum(d.astype(np.float64) ** 2, axis=1), rtol=1e-14, atol=0)
+    assert got[2, 0] == 0.0
+
+
+def test_error_sums_grow_away_from_reconstructions():
+    """Moving a weight off its reconstruction adds exactly that squared gap."""
+    w = np.zeros((1, 32), np.float32)
+    w[0, 0] = 1.0                   # the max: reconstructs exactly
+    w[0, 1] = 0.5                   # alpha = 1: code 8, level 8/15
+    got = O.error_sums(w, 1.0)
+    rec = float(round_fraction(Fraction(8, 15), 8))
+    assert math.isclose(got[0, 1], (0.5 - rec) ** 2, rel_tol=1e-15)
