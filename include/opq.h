@@ -112,6 +112,26 @@ int opq_quantize(const void* w, int w_dtype, int64_t n, int64_t k, float alpha,
                  uint32_t* packed, uint32_t* sign, float* scale, void* stream);
 
 /*
+ * Reconstruction error for choosing alpha ("OPQ 原理": OPQ against uniform
+ * rounding, which alpha = 1 is; "为什么 α=0.73？": alpha sits in the flat optimum
+ * of this error).  Quantizes w as opq_quantize would, reconstructs it as
+ * opq_dequantize would, and stores nothing but, per row,
+ *   row_sums[2i]     = sum_k w[i][k]^2
+ *   row_sums[2i + 1] = sum_k (w[i][k] - w'[i][k])^2
+ * (float per lane over at most 64 elements, then double in a fixed order, so
+ * the sums are reproducible and within ~1e-5 relative of exact).  SNR in dB
+ * over a tensor is 10 log10(sum of the first column / sum of the second).
+ *   w         device, [n][k] float32 (OPQ_F32) or bfloat16 (OPQ_BF16)
+ *   row_sums  device out, [n][2] double
+ * k <= 16384, and alpha must have a separating bucket grid (every alpha in
+ * [0.05, 60] does); otherwise OPQ_ERR_UNSUPPORTED.
+ * Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN,
+ * OPQ_ERR_DTYPE, OPQ_ERR_UNSUPPORTED, OPQ_ERR_HIP.
+ */
+int opq_error_sums(const void* w, int w_dtype, int64_t n, int64_t k, float alpha,
+                   double* row_sums, void* stream);
+
+/*
  * Dequantize ("推理解码").
  *   packed, sign, scale  device, as written by opq_quantize
  *   w_out   device out, [n][k] bfloat16: bf16(G_q * scale[n]) with the sign

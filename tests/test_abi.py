@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 9
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(opq._SIGNATURES)
@@ -93,6 +93,20 @@ def test_quantize_argument_checks(lib):
     assert q(FAKE, 7, 4, 64, 0.73, FAKE, FAKE, FAKE, None) == DTYPE
     assert q(FAKE, 1, 4, 65536 + 32, 0.73, FAKE, FAKE, FAKE, None) == UNSUPPORTED
     assert q(FAKE, 1, 0, 64, 0.73, FAKE, FAKE, FAKE, None) == OK         # empty: nothing enqueued
+
+
+def test_error_sums_argument_checks(lib):
+    e = lib.opq_error_sums
+    assert e(None, 1, 4, 64, 0.73, FAKE, None) == NULL
+    assert e(FAKE, 1, 4, 64, 0.73, None, None) == NULL
+    assert e(FAKE, 1, 4, 40, 0.73, FAKE, None) == SHAPE
+    assert e(FAKE, 1, 4, 64, -1.0, FAKE, None) == ALPHA
+    assert e(FAKE, 1, 4, 64, 0.73, MISALIGNED, None) == ALIGN
+    assert e(FAKE, 5, 4, 64, 0.73, FAKE, None) == DTYPE
+    assert e(FAKE, 1, 4, 16384 + 32, 0.73, FAKE, None) == UNSUPPORTED
+    assert e(FAKE, 1, 4, 64, 100.0, FAKE, None) == UNSUPPORTED  # no separating bucket grid
+    assert e(FAKE, 1, 4, 64, 0.03, FAKE, None) == UNSUPPORTED   # nor here (T_1 below 2^-126)
+    assert e(FAKE, 1, 0, 64, 0.73, FAKE, None) == OK           # empty: nothing enqueued
 
 
 def test_dequantize_argument_checks(lib):

@@ -360,3 +360,43 @@ def test_model_layer_shapes(gpu_lib, alpha):
     cfg = WL.config("model")
     for L in cfg.layers[:4] + cfg.layers[-4:]:
         _check_layer(gpu_lib, L, alpha, with_linear=False, q_rows=128)
+
+
+# ------------------------------------------------------------------ error sums (alpha sweep)
+
+ERR_RTOL = 1e-5   # float partial sums over <= 64 elements per lane, then double
+
+
+def _assert_sums_close(got, ref):
+    got = np.asarray(got, np.float64)
+    scale_ = np.maximum(np.abs(ref), 1e-300)
+    bad = np.abs(got - ref) > ERR_RTOL * scale_ + 1e-30
+    assert not bad.any(), f"rows {np.argwhere(bad)[:5].ravel().tolist()}: {got[bad][:4]} vs {ref[bad][:4]}"
+
+
+@pytest.mark.parametrize("alpha", [0.3, 0.45, 0.73, 1.0])
+@pytest.mark.parametrize("dtype,n,k", [("bf16", 64, 3840), ("bf16", 33, 96), ("f32", 40, 544),
+                                       ("bf16", 8, 16384), ("f32", 5, 32)])
+def test_error_sums_match_oracle(gpu_lib, alpha, dtype, n, k):
+    opq = gpu_lib
+    w32 = WL.student_t(1000 + n + k, (n, k))
+    w32[0] = 0.0                       # an all-zero row
+    if n > 3:
+        w32[3] = 0.0
+        w32[3, k // 2] = -0.5          # a row with a single (negative) weight
+    w_vals, w_dev = weight_tensor(w32, dtype)
+    got = opq.error_sums(w_dev, alpha).cpu().numpy()
+    ref = O.error_sums(w_vals, alpha)
+    _assert_sums_close(got, ref)
+    assert np.all(got[0] == 0.0)
+
+
+def test_error_sums_agree_with_stored_form(gpu_lib):
+    """The fused sums equal those of the library's own quantize + dequantize."""
+    opq = gpu_lib
+    _, w_dev = weight_tensor(WL.student_t(77, (128, 3840)), "bf16")
+    for alpha in (0.45, 0.73, 1.0):
+        d = opq.dequantize(opq.quantize(w_dev, alpha), alpha).double()
+        wd = w_dev.double()
+        ref = torch.stack([(wd * wd).sum(1), ((wd - d) ** 2).sum(1)], 1).cpu().numpy()
+        _assert_sums_close(opq.error_sums(w_dev, alpha).cpu().numpy(), ref)

@@ -73,6 +73,23 @@ int opq_quantize(const void* w, int w_dtype, int64_t n, int64_t k, float alpha,
                                          static_cast<hipStream_t>(stream)));
 }
 
+int opq_error_sums(const void* w, int w_dtype, int64_t n, int64_t k, float alpha,
+                   double* row_sums, void* stream) {
+  if ((n > 0 && k > 0 && !w) || (n > 0 && !row_sums)) return OPQ_ERR_NULL;
+  if (!shape_ok(n, k)) return OPQ_ERR_SHAPE;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  if (!aligned16(w) || !aligned16(row_sums)) return OPQ_ERR_ALIGN;
+  if (w_dtype != OPQ_F32 && w_dtype != OPQ_BF16) return OPQ_ERR_DTYPE;
+  if (n == 0) return OPQ_OK;
+  opq::DecisionPoints dp;
+  if (!opq::decision_points(alpha, dp.t)) return OPQ_ERR_ALPHA;
+  if (!opq::error_sums_supported(dp, k)) return OPQ_ERR_UNSUPPORTED;
+  opq::Levels lv;  // k == 0 runs the kernel too: it writes zero sums
+  opq::levels(alpha, lv.g);
+  return hip_status(opq::launch_error_sums(w, w_dtype == OPQ_BF16, n, k, dp, lv, row_sums,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int opq_dequantize(const uint32_t* packed, const uint32_t* sign, const float* scale, int64_t n,
                    int64_t k, float alpha, uint16_t* w_out, void* stream) {
   if (n > 0 && k > 0 && (!packed || !sign || !scale || !w_out)) return OPQ_ERR_NULL;

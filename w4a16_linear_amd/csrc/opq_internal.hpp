@@ -28,6 +28,12 @@ hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, int64_t k,
                            const DecisionPoints& dp, uint32_t* packed, uint32_t* sign,
                            float* scale, hipStream_t stream);
 
+// quantize.hip: per-row (sum w^2, sum (w - w')^2) without storing the stored form
+bool error_sums_supported(const DecisionPoints& dp, int64_t k);
+hipError_t launch_error_sums(const void* w, bool w_is_bf16, int64_t n, int64_t k,
+                             const DecisionPoints& dp, const Levels& lv, double* row_sums,
+                             hipStream_t stream);
+
 // dequantize.hip
 hipError_t launch_dequantize(const uint32_t* packed, const uint32_t* sign, const float* scale,
                              int64_t n, int64_t k, const Levels& lv, uint16_t* out,

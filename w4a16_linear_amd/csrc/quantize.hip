@@ -391,13 +391,21 @@ __device__ __forceinline__ void store_word(uint32_t* prow, uint32_t* srow, int w
   }
 }
 
-template <typename T, int NCT>
+// kErr: instead of storing the stored form, reconstruct every element as
+// opq_dequantize would (the row's table L[q] = bf16(G_q m) built in LDS once the
+// max is known) and write the row's (sum w^2, sum (w - w')^2): float per lane
+// over its at most 64 elements, then double across lanes and waves in a fixed
+// order.
+template <typename T, int NCT, bool kErr>
 __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
     const T* __restrict__ w, int64_t n, int k, DecisionPoints dp, BucketGrid g,
-    uint32_t* __restrict__ packed, uint32_t* __restrict__ sign, float* __restrict__ scale) {
+    uint32_t* __restrict__ packed, uint32_t* __restrict__ sign, float* __restrict__ scale,
+    Levels lv, double* __restrict__ row_sums) {
   __shared__ uint2 s_tab[kMaxBuckets];
   __shared__ float s_pts[kLevels + 1];
   __shared__ float s_wmax[2][kBlockThreads / kWave];
+  __shared__ uint32_t s_rec[2][16];
+  __shared__ double s_sum[2][kBlockThreads / kWave][2];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -440,15 +448,56 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
     mx = fmaxf(fmaxf(s_wmax[ms][0], s_wmax[ms][1]), fmaxf(s_wmax[ms][2], s_wmax[ms][3]));
     const bool fast = mx >= 0x1p-125f && mx <= 0x1p125f;  // 1/m normal, u' <= 1 + ulps
     const float r = 1.0f / mx;
-    uint32_t* prow = packed + rr * (int64_t)(k / 8);
-    uint32_t* srow = sign + rr * (int64_t)(k / 32);
+    if constexpr (!kErr) {
+      uint32_t* prow = packed + rr * (int64_t)(k / 8);
+      uint32_t* srow = sign + rr * (int64_t)(k / 32);
 #pragma unroll
-    for (int c = 0; c < NCT; ++c) {
-      const int e0 = c * kBlockChunk + tid * 8;
-      const uint32_t word = encode_chunk(v[buf][c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts);
-      store_word(prow, srow, e0 >> 3, lane, e0 < k, word, sign_byte(v[buf][c]));
+      for (int c = 0; c < NCT; ++c) {
+        const int e0 = c * kBlockChunk + tid * 8;
+        const uint32_t word = encode_chunk(v[buf][c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts);
+        store_word(prow, srow, e0 >> 3, lane, e0 < k, word, sign_byte(v[buf][c]));
+      }
+      if (tid == 0) scale[rr] = mx;
+    } else {
+      if (tid < 16) s_rec[ms][tid] = lut_entry(lv, tid, mx);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      float sw2 = 0.0f, se2 = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        const uint32_t word = encode_chunk(v[buf][c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float xv = v[buf][c].at(i);  // zero past k
+          const float rec = __uint_as_float(s_rec[ms][(word >> (4 * i)) & 15u] << 16);
+          const float e = xv - (v[buf][c].neg(i) ? -rec : rec);
+          sw2 = fmaf(xv, xv, sw2);
+          se2 = fmaf(e, e, se2);
+        }
+      }
+      double d0 = sw2, d1 = se2;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        d0 += __shfl_xor(d0, off, kWave);
+        d1 += __shfl_xor(d1, off, kWave);
+      }
+      if (lane == 0) {
+        s_sum[ms][wave][0] = d0;
+        s_sum[ms][wave][1] = d1;
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      if (tid == 0) {
+        double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+        for (int q = 0; q < kBlockThreads / kWave; ++q) {
+          a0 += s_sum[ms][q][0];
+          a1 += s_sum[ms][q][1];
+        }
+        row_sums[2 * rr] = a0;
+        row_sums[2 * rr + 1] = a1;
+      }
     }
-    if (tid == 0) scale[rr] = mx;
   };
 
   // Rows alternate between the two buffers (register arrays need constant indices).
@@ -571,11 +620,11 @@ hipError_t launch_rows(const T* w, int64_t n, int64_t k, const DecisionPoints& d
 // not exceed it: a block waiting for a slot would start only after another
 // block had finished all of its rows).  Per-CU occupancy is computed once per
 // kernel; the CU count is asked of the current device per call.
-template <typename T, int NCT>
+template <typename T, int NCT, bool kErr>
 int64_t resident_blocks() {
   static const int per_cu = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, quantize_block_rows<T, NCT>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, quantize_block_rows<T, NCT, kErr>,
                                                      kBlockThreads, 0) != hipSuccess || b < 1)
       b = 1;
     return b;
@@ -587,16 +636,36 @@ int64_t resident_blocks() {
   return (int64_t)per_cu * cus;
 }
 
-template <typename T, int NCT>
+template <typename T, int NCT, bool kErr = false>
 hipError_t launch_block_rows(const T* w, int64_t n, int64_t k, const DecisionPoints& dp,
                              const BucketGrid& g, uint32_t* packed, uint32_t* sign, float* scale,
-                             hipStream_t stream) {
-  int64_t blocks = resident_blocks<T, NCT>();
+                             hipStream_t stream, const Levels* lv = nullptr,
+                             double* row_sums = nullptr) {
+  int64_t blocks = resident_blocks<T, NCT, kErr>();
   if (blocks > kPersistBlocks) blocks = kPersistBlocks;
   if (blocks > n) blocks = n;
-  hipLaunchKernelGGL((quantize_block_rows<T, NCT>), dim3((unsigned)blocks), dim3(kBlockThreads), 0,
-                     stream, w, n, (int)k, dp, g, packed, sign, scale);
+  Levels lvv{};
+  if (lv) lvv = *lv;
+  hipLaunchKernelGGL((quantize_block_rows<T, NCT, kErr>), dim3((unsigned)blocks),
+                     dim3(kBlockThreads), 0, stream, w, n, (int)k, dp, g, packed, sign, scale,
+                     lvv, row_sums);
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_error(const T* w, int64_t n, int64_t k, const DecisionPoints& dp,
+                          const Levels& lv, double* row_sums, hipStream_t stream) {
+  BucketGrid g;
+  if (!bucket_grid(dp, g)) return hipErrorNotSupported;
+  const int64_t nct = (k + kBlockChunk - 1) / kBlockChunk;
+#define OPQ_ERR_CASE(N)                                                                        \
+  if (nct <= N)                                                                                \
+    return launch_block_rows<T, N, true>(w, n, k, dp, g, nullptr, nullptr, nullptr, stream, &lv, \
+                                         row_sums);
+  OPQ_ERR_CASE(1) OPQ_ERR_CASE(2) OPQ_ERR_CASE(3) OPQ_ERR_CASE(4) OPQ_ERR_CASE(5)
+  OPQ_ERR_CASE(6) OPQ_ERR_CASE(8)
+#undef OPQ_ERR_CASE
+  return hipErrorNotSupported;
 }
 
 template <typename T>
@@ -631,6 +700,19 @@ hipError_t dispatch(const T* w, int64_t n, int64_t k, const DecisionPoints& dp, 
 }
 
 }  // namespace
+
+bool error_sums_supported(const DecisionPoints& dp, int64_t k) {
+  BucketGrid g;
+  return bucket_grid(dp, g) && k <= 8 * kBlockChunk;
+}
+
+hipError_t launch_error_sums(const void* w, bool w_is_bf16, int64_t n, int64_t k,
+                             const DecisionPoints& dp, const Levels& lv, double* row_sums,
+                             hipStream_t stream) {
+  if (w_is_bf16)
+    return dispatch_error(static_cast<const uint16_t*>(w), n, k, dp, lv, row_sums, stream);
+  return dispatch_error(static_cast<const float*>(w), n, k, dp, lv, row_sums, stream);
+}
 
 hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, int64_t k,
                            const DecisionPoints& dp, uint32_t* packed, uint32_t* sign,

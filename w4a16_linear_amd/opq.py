@@ -32,6 +32,8 @@ _SIGNATURES = {
     "opq_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                     ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]),
+    "opq_error_sums": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
+                                      ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]),
     "opq_dequantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                       ctypes.c_void_p, ctypes.c_void_p]),
@@ -162,6 +164,37 @@ def dequantize(qw: QuantizedWeight, alpha: float, out: Optional[torch.Tensor] = 
 
 def linear_workspace_bytes(m: int, n: int, k: int) -> int:
     return int(load().opq_linear_workspace_bytes(m, n, k))
+
+
+def error_sums(w: torch.Tensor, alpha: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per row of w: (sum w^2, sum (w - w')^2) as float64 [n, 2], w' the bf16
+    reconstruction opq_quantize + opq_dequantize would give (nothing stored)."""
+    _need_cuda("w", w, w.dtype, 2)
+    if w.dtype == torch.float32:
+        dt = OPQ_F32
+    elif w.dtype == torch.bfloat16:
+        dt = OPQ_BF16
+    else:
+        raise ValueError(f"w must be float32 or bfloat16, got {w.dtype}")
+    n, k = w.shape
+    if out is None:
+        out = torch.empty((n, 2), dtype=torch.float64, device=w.device)
+    _need_cuda("out", out, torch.float64, 2)
+    st = load().opq_error_sums(_ptr(w), dt, n, k, alpha, _ptr(out), _stream(w.device))
+    _check("opq_error_sums", st)
+    return out
+
+
+def snr_db(weights, alpha: float) -> float:
+    """10 log10(sum w^2 / sum (w - w')^2) over one tensor or a list of tensors."""
+    if isinstance(weights, torch.Tensor):
+        weights = [weights]
+    tot = None
+    for w in weights:
+        s = error_sums(w, alpha).sum(dim=0)
+        tot = s if tot is None else tot + s
+    num, den = (float(v) for v in tot.cpu())
+    return float("inf") if den == 0.0 else 10.0 * float(np.log10(num / den))
 
 
 # One zero-filled workspace per device, grown on demand.  opq_linear puts the
