@@ -118,8 +118,9 @@ int opq_quantize(const void* w, int w_dtype, int64_t n, int64_t k, float alpha,
  * opq_dequantize would, and stores nothing but, per row,
  *   row_sums[2i]     = sum_k w[i][k]^2
  *   row_sums[2i + 1] = sum_k (w[i][k] - w'[i][k])^2
- * (float per lane over at most 64 elements, then double in a fixed order, so
- * the sums are reproducible and within ~1e-5 relative of exact).  SNR in dB
+ * (binary32 over each wave's at most 4096 elements, then double across waves
+ * in a fixed order: reproducible, and within 70 * 2^-24 relative of the exact
+ * sums of these nonnegative terms).  SNR in dB
  * over a tensor is 10 log10(sum of the first column / sum of the second).
  *   w         device, [n][k] float32 (OPQ_F32) or bfloat16 (OPQ_BF16)
  *   row_sums  device out, [n][2] double

@@ -391,12 +391,29 @@ def test_error_sums_match_oracle(gpu_lib, alpha, dtype, n, k):
     assert np.all(got[0] == 0.0)
 
 
-def test_error_sums_agree_with_stored_form(gpu_lib):
-    """The fused sums equal those of the library's own quantize + dequantize."""
+@pytest.mark.parametrize("dtype,n,k", [("bf16", 6007, 3840), ("bf16", 4099, 10240), ("f32", 2500, 1056)])
+def test_error_sums_agree_with_stored_form(gpu_lib, dtype, n, k):
+    """More rows than the persistent grid (each block takes several rows, odd
+    and even counts): the fused sums equal those of the library's own quantize +
+    dequantize at every row, and the oracle's at sampled rows."""
     opq = gpu_lib
-    _, w_dev = weight_tensor(WL.student_t(77, (128, 3840)), "bf16")
+    w32 = WL.student_t(77 + n, (n, k))
+    w32[n // 3] = 0.0
+    w_vals, w_dev = weight_tensor(w32, dtype)
+    rows = _sample_rows(n, 24, n)
     for alpha in (0.45, 0.73, 1.0):
+        got = opq.error_sums(w_dev, alpha).cpu().numpy()
         d = opq.dequantize(opq.quantize(w_dev, alpha), alpha).double()
         wd = w_dev.double()
         ref = torch.stack([(wd * wd).sum(1), ((wd - d) ** 2).sum(1)], 1).cpu().numpy()
-        _assert_sums_close(opq.error_sums(w_dev, alpha).cpu().numpy(), ref)
+        _assert_sums_close(got, ref)
+        _assert_sums_close(got[rows], O.error_sums(w_vals[rows], alpha))
+        del d, wd
+
+
+def test_error_sums_empty(gpu_lib):
+    opq = gpu_lib
+    z = torch.empty((7, 0), dtype=torch.bfloat16, device=DEV)
+    out = torch.full((7, 2), -1.0, dtype=torch.float64, device=DEV)
+    assert np.all(opq.error_sums(z, 0.73, out=out).cpu().numpy() == 0.0)
+    assert opq.error_sums(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV), 0.73).shape == (0, 2)

@@ -393,9 +393,9 @@ __device__ __forceinline__ void store_word(uint32_t* prow, uint32_t* srow, int w
 
 // kErr: instead of storing the stored form, reconstruct every element as
 // opq_dequantize would (the row's table L[q] = bf16(G_q m) built in LDS once the
-// max is known) and write the row's (sum w^2, sum (w - w')^2): float per lane
-// over its at most 64 elements, then double across lanes and waves in a fixed
-// order.
+// max is known) and write the row's (sum w^2, sum (w - w')^2): binary32 per lane
+// over its at most 64 elements and across the wave, then double across the
+// block's waves in a fixed order.
 template <typename T, int NCT, bool kErr>
 __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
     const T* __restrict__ w, int64_t n, int k, DecisionPoints dp, BucketGrid g,
@@ -404,8 +404,8 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
   __shared__ uint2 s_tab[kMaxBuckets];
   __shared__ float s_pts[kLevels + 1];
   __shared__ float s_wmax[2][kBlockThreads / kWave];
-  __shared__ uint32_t s_rec[2][16];
   __shared__ double s_sum[2][kBlockThreads / kWave][2];
+  __shared__ uint32_t s_recw[kBlockThreads / kWave][16];
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid / kWave;
@@ -437,6 +437,19 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
 
   // Encode the row held in buffer `buf`; `ms` picks the LDS slot of its max
   // (slots alternate, so one barrier per row keeps writes after old reads).
+  int64_t pend = -1;  // row whose partial sums wait in s_sum (kErr)
+  auto flush_sums = [&](int slot) __attribute__((always_inline)) {
+    if (tid == 0 && pend >= 0) {
+      double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+      for (int q = 0; q < kBlockThreads / kWave; ++q) {
+        a0 += s_sum[slot][q][0];
+        a1 += s_sum[slot][q][1];
+      }
+      row_sums[2 * pend] = a0;
+      row_sums[2 * pend + 1] = a1;
+    }
+  };
   auto process = [&](int64_t rr, int buf, int ms) __attribute__((always_inline)) {
     typename Slot<T>::Acc acc = Slot<T>::acc0();
 #pragma unroll
@@ -446,6 +459,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     mx = fmaxf(fmaxf(s_wmax[ms][0], s_wmax[ms][1]), fmaxf(s_wmax[ms][2], s_wmax[ms][3]));
+    if constexpr (kErr) flush_sums(ms ^ 1);
     const bool fast = mx >= 0x1p-125f && mx <= 0x1p125f;  // 1/m normal, u' <= 1 + ulps
     const float r = 1.0f / mx;
     if constexpr (!kErr) {
@@ -459,9 +473,11 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
       }
       if (tid == 0) scale[rr] = mx;
     } else {
-      if (tid < 16) s_rec[ms][tid] = lut_entry(lv, tid, mx);
+      // Each wave writes the row's table L[q] = bf16(G_q m) into its own LDS
+      // slot (lanes 0..15 one entry each): LDS ops of one wave complete in
+      // order, so no block barrier is needed before the lookups.
+      if (lane < 16) s_recw[wave][lane] = lut_entry(lv, lane, mx);
       __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_s_barrier();
       float sw2 = 0.0f, se2 = 0.0f;
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
@@ -469,34 +485,27 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float xv = v[buf][c].at(i);  // zero past k
-          const float rec = __uint_as_float(s_rec[ms][(word >> (4 * i)) & 15u] << 16);
-          const float e = xv - (v[buf][c].neg(i) ? -rec : rec);
+          // a nonzero code carries the weight's sign, so |w - w'| = ||w| - L[q]|
+          const float e = fabsf(xv) - __uint_as_float(s_recw[wave][(word >> (4 * i)) & 15u] << 16);
           sw2 = fmaf(xv, xv, sw2);
           se2 = fmaf(e, e, se2);
         }
       }
-      double d0 = sw2, d1 = se2;
+      // binary32 over the wave (at most 64 x 64 positive terms: relative
+      // error below 70 * 2^-24), double across the block's waves
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) {
-        d0 += __shfl_xor(d0, off, kWave);
-        d1 += __shfl_xor(d1, off, kWave);
+        sw2 += __shfl_xor(sw2, off, kWave);
+        se2 += __shfl_xor(se2, off, kWave);
       }
+      const double d0 = sw2, d1 = se2;
+      // The block's partials are summed after the next row's barrier (or the
+      // one after the loop); slots alternate with the rows.
       if (lane == 0) {
         s_sum[ms][wave][0] = d0;
         s_sum[ms][wave][1] = d1;
       }
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_s_barrier();
-      if (tid == 0) {
-        double a0 = 0.0, a1 = 0.0;
-#pragma unroll
-        for (int q = 0; q < kBlockThreads / kWave; ++q) {
-          a0 += s_sum[ms][q][0];
-          a1 += s_sum[ms][q][1];
-        }
-        row_sums[2 * rr] = a0;
-        row_sums[2 * rr + 1] = a1;
-      }
+      pend = rr;
     }
   };
 
@@ -510,6 +519,13 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
     if (r2 < n) load_row(r2, 0);
     process(r1, 1, 1);
     row = r2;
+  }
+  if constexpr (kErr) {
+    // the last row's partials: which slot holds them follows the row count
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    const int64_t cnt = blockIdx.x < n ? (n - 1 - blockIdx.x) / stride + 1 : 0;
+    flush_sums((int)((cnt - 1) & 1));
   }
 }
 
