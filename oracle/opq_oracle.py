@@ -1,4 +1,5 @@
-"""Plain, slow CPU oracle for OPQ (Optimal Power Quantization), 4-bit, per output row.
+"""Plain, slow CPU oracle for OPQ (Optimal Power Quantization), 4-bit, with one
+scale per output row or one float16 scale per group of weights.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no code,
@@ -30,7 +31,9 @@ Readings taken where the page is silent (each is listed in the design doc):
 * the reconstruction is the real value sign (q/15)^(1/alpha) m rounded once to
   bfloat16 (round to nearest even); here it is evaluated in float64 first;
 * the linear layer is y = x W'^T (+ bias) over the bf16 reconstructions,
-  accumulated here in float64.
+  accumulated here in float64;
+* the group-wise form (the card's own stored format) is described where it is
+  defined, below.
 
 Every function below is pinned by the CPU tests in ``tests/test_oracle_pins.py``.
 """
@@ -48,7 +51,9 @@ SIGNS_PER_WORD = 32  # "32 个打包进 1 个 uint32"
 __all__ = [
     "LEVELS", "alpha_f32", "bf16_bits_to_f32", "f64_to_bf16_bits", "row_absmax",
     "encode", "pack", "unpack", "quantize", "reconstruct", "dequantize",
-    "linear", "snr_db", "error_sums", "decision_thresholds_f32",
+    "linear", "snr_db", "error_sums", "decision_thresholds_f32", "codes_of_u",
+    "F16_MAX", "group_absmax_f16", "encode_grouped", "quantize_grouped",
+    "reconstruct_grouped", "dequantize_grouped",
 ]
 
 
@@ -112,22 +117,28 @@ def encode(w32: np.ndarray, alpha: float):
     scale float32 [N]).
     """
     w32 = np.ascontiguousarray(w32, dtype=np.float32)
-    a64 = alpha_f32(alpha)
     m = row_absmax(w32)
     absw = np.abs(w32)
     u = np.zeros_like(absw)
     live = m > 0
     with np.errstate(divide="ignore", invalid="ignore"):
         u[live] = absw[live] / m[live, None]          # IEEE binary32 quotient
+    q = codes_of_u(u, alpha)
+    s = (w32 < 0).astype(np.uint8)                    # -0.0 is not < 0
+    return q, s, m
+
+
+def codes_of_u(u: np.ndarray, alpha: float) -> np.ndarray:
+    """q = round(15 u^alpha) for binary32 u >= 0, halves up, limited to 15
+    (u above 1 only arises against a rounded group max)."""
+    a64 = alpha_f32(alpha)
     v = LEVELS * np.power(u.astype(np.float64), a64)
     q = np.floor(v + 0.5)
     # Values whose float64 v sits next to a half are settled exactly.
     frac = v - np.floor(v)
     for r, c in np.argwhere(np.abs(frac - 0.5) < 1e-9):
         q[r, c] = _nearest_code_exact(float(u[r, c]), a64)
-    q = np.clip(q, 0, LEVELS).astype(np.uint8)
-    s = (w32 < 0).astype(np.uint8)                    # -0.0 is not < 0
-    return q, s, m
+    return np.clip(q, 0, LEVELS).astype(np.uint8)
 
 
 def pack(q: np.ndarray, s: np.ndarray):
@@ -184,6 +195,68 @@ def dequantize(packed: np.ndarray, sign: np.ndarray, scale: np.ndarray, alpha: f
     """Dequantize to bfloat16 bit patterns (uint16 [N, K]), rounded once."""
     q, s = unpack(packed, sign)
     return f64_to_bf16_bits(reconstruct(q, s, scale, alpha))
+
+
+# ---------------------------------------------------------------- group-wise scales
+#
+# The card's stored form ("技术细节 / 存储格式"): one float16 max per group of
+# weights ("每 128 个权重共享一个"; the configuration section offers group
+# sizes 32, 64, 128 and 256), and the decode multiplies by that group max
+# ("推理解码").  Readings: a group is `gs` consecutive weights of a row along K;
+# the stored max is max|w| over the group rounded to float16 (nearest, ties to
+# even; values past 65504 saturate to 65504); u is the binary32 quotient by the
+# stored max, so u may exceed 1 by less than 2^-11 and then codes 15; a group
+# whose stored max is 0 has all codes 0.
+
+F16_MAX = 65504.0
+
+
+def group_absmax_f16(w32: np.ndarray, gs: int) -> np.ndarray:
+    """Stored group maxima, float16 [N, K/gs]."""
+    w32 = np.asarray(w32, dtype=np.float32)
+    n, k = w32.shape
+    assert k % gs == 0
+    if k == 0:
+        return np.zeros((n, 0), np.float16)
+    a = np.max(np.abs(w32).reshape(n, k // gs, gs), axis=2)
+    return np.minimum(a, np.float32(F16_MAX)).astype(np.float16)   # numpy: nearest even
+
+
+def encode_grouped(w32: np.ndarray, alpha: float, gs: int):
+    """(q uint8 [N,K], s uint8 [N,K], m16 float16 [N,K/gs]) of w[N, K]."""
+    w32 = np.ascontiguousarray(w32, dtype=np.float32)
+    m16 = group_absmax_f16(w32, gs)
+    m = np.repeat(m16.astype(np.float32), gs, axis=1)   # each weight's stored max
+    absw = np.abs(w32)
+    u = np.zeros_like(absw)
+    live = m > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u[live] = absw[live] / m[live]                 # IEEE binary32 quotient
+    q = codes_of_u(u, alpha)
+    s = (w32 < 0).astype(np.uint8)
+    return q, s, m16
+
+
+def quantize_grouped(w32: np.ndarray, alpha: float, gs: int):
+    """(packed, sign, m16) of w[N, K] with one float16 max per gs weights."""
+    q, s, m16 = encode_grouped(w32, alpha, gs)
+    packed, sign = pack(q, s)
+    return packed, sign, m16
+
+
+def reconstruct_grouped(q, s, m16, alpha: float, gs: int) -> np.ndarray:
+    """w' = sign (q/15)^(1/alpha) m16 in float64; q = 0 gives +0."""
+    scale = np.repeat(np.asarray(m16, np.float16).astype(np.float64), gs, axis=1)
+    a64 = alpha_f32(alpha)
+    mag = np.power(np.asarray(q, np.float64) / LEVELS, 1.0 / a64) * scale
+    neg = (np.asarray(s) != 0) & (np.asarray(q) != 0)
+    return np.where(neg, -mag, mag)
+
+
+def dequantize_grouped(packed, sign, m16, alpha: float, gs: int) -> np.ndarray:
+    """bfloat16 bit patterns (uint16 [N, K]) of the group-wise stored form."""
+    q, s = unpack(packed, sign)
+    return f64_to_bf16_bits(reconstruct_grouped(q, s, m16, alpha, gs))
 
 
 # ---------------------------------------------------------------- linear layer

@@ -58,6 +58,19 @@ MUTATIONS = {
     "error_sign": ("    e = w64 - w_rec\n", "    e = w64 + w_rec\n"),
     # error measured against the float32 input instead of its reconstruction
     "error_self": ("    e = w64 - w_rec\n", "    e = w64 - w64.astype(np.float32)\n"),
+    # groups taken with a stride along K instead of as consecutive runs
+    "group_strided": ("a = np.max(np.abs(w32).reshape(n, k // gs, gs), axis=2)",
+                      "a = np.max(np.abs(w32).reshape(n, gs, k // gs), axis=1)"),
+    # group max not saturated (past 65504 it becomes infinity)
+    "group_no_saturation": ("return np.minimum(a, np.float32(F16_MAX)).astype(np.float16)",
+                            "return a.astype(np.float16)"),
+    # u taken against the exact group max instead of the stored float16 one
+    "group_exact_max": ("m = np.repeat(m16.astype(np.float32), gs, axis=1)",
+                        "m = np.repeat(np.max(np.abs(w32).reshape(w32.shape[0], -1, gs), axis=2)"
+                        ".astype(np.float32), gs, axis=1)"),
+    # group scales spread over K in the wrong order when reconstructing
+    "group_deq_tile": ("scale = np.repeat(np.asarray(m16, np.float16).astype(np.float64), gs, axis=1)",
+                       "scale = np.tile(np.asarray(m16, np.float16).astype(np.float64), (1, gs))"),
 }
 
 

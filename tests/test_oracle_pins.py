@@ -477,3 +477,134 @@ def test_error_sums_grow_away_from_reconstructions():
     got = O.error_sums(w, 1.0)
     rec = float(round_fraction(Fraction(8, 15), 8))
     assert math.isclose(got[0, 1], (0.5 - rec) ** 2, rel_tol=1e-15)
+
+
+# ------------------------------------------------------------------ group-wise scales
+#
+# The card's stored form keeps one float16 max per group of weights ("技术细节 /
+# 存储格式", group sizes 32/64/128/256 in the configuration section).
+
+def _f16_exact(a):
+    """Nearest float16 (ties to even) of a nonnegative value, saturated at
+    65504, by exact rational rounding (11 significant bits, emin = -14)."""
+    fr = min(Fraction(float(a)), Fraction(65504))
+    return round_fraction(fr, 11, emin=-14)
+
+
+def test_group_max_f16_exact_rounding():
+    rng = np.random.default_rng(40)
+    vals = np.concatenate([
+        (rng.random(3000) * np.exp2(rng.integers(-30, 17, 3000))).astype(np.float32),
+        np.array([0.0, 65504.0, 65519.0, 65520.0, 1e5, 3e38, 2.0 ** -24, 2.0 ** -25,
+                  1.5 * 2.0 ** -25, 2.0 ** -26, 2.0 ** -14, 2.0 ** -15 * 1.5], np.float32),
+        # exact midpoints between neighbouring float16 values: ties to even
+        (1.0 + (2 * rng.integers(0, 1024, 500) + 1) * 2.0 ** -11).astype(np.float32),
+        ((2 * rng.integers(0, 1024, 500) + 1) * 2.0 ** -25).astype(np.float32),
+    ])
+    gs = 32
+    w = np.zeros((len(vals), gs), np.float32)
+    w[:, 5] = vals
+    w[:, 9] = -vals * np.float32(0.5)
+    got = O.group_absmax_f16(w, gs)[:, 0].astype(np.float64)
+    ref = np.array([float(_f16_exact(v)) for v in vals])
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("gs", [32, 64, 128, 256])
+def test_groups_are_row_slabs(gs):
+    """With bf16 weights (every group max is a float16 value) the group form
+    is the per-row form applied to each slab of gs consecutive columns."""
+    w = _to_bf16_values(_rand_rows(41, 6, 512))
+    w[2, 64:128] = 0.0                                   # zero groups
+    q, s, m16 = O.encode_grouped(w, 0.73, gs)
+    pk, sg, _ = O.quantize_grouped(w, 0.73, gs)
+    d = O.dequantize_grouped(pk, sg, m16, 0.73, gs)
+    for j in range(512 // gs):
+        sl = slice(j * gs, (j + 1) * gs)
+        qr, sr, mr = O.encode(w[:, sl], 0.73)
+        assert np.array_equal(q[:, sl], qr) and np.array_equal(s[:, sl], sr)
+        assert np.array_equal(m16[:, j].astype(np.float32), mr)
+        pr, sgr, _ = O.quantize(w[:, sl], 0.73)
+        assert np.array_equal(d[:, sl], O.dequantize(pr, sgr, mr, 0.73))
+
+
+@pytest.mark.parametrize("alpha,rule", [
+    (1.0, lambda u: min(15, int(np.rint(15 * float(u))))),
+    # 15 sqrt(u) >= k - 1/2  <=>  900 u >= (2k-1)^2; codes stop at 15
+    (0.5, lambda u: sum(1 for k in range(1, 16) if 900 * u >= (2 * k - 1) ** 2)),
+])
+def test_group_codes_against_rounded_max(alpha, rule):
+    """float32 weights whose group max is no float16 value: u is the binary32
+    quotient by the stored (rounded) max, up to just above 1 (code 15)."""
+    rng = np.random.default_rng(42)
+    gs = 32
+    w = (rng.standard_normal((8, 4 * gs)) * 0.02).astype(np.float32)
+    w[0, 3] = np.float32(1.0 + 2.0 ** -12)               # rounds down to 1.0
+    w[0, 7] = np.float32(-(1.0 + 2.0 ** -13))
+    w[1, gs + 1] = np.float32(0.1)                        # rounds up
+    q, s, m16 = O.encode_grouped(w, alpha, gs)
+    for r in range(w.shape[0]):
+        for c in range(w.shape[1]):
+            mg = _f16_exact(np.max(np.abs(w[r, (c // gs) * gs:(c // gs + 1) * gs])))
+            assert float(m16[r, c // gs]) == float(mg)
+            u = Fraction(0) if mg == 0 else Fraction(float(round_fraction(
+                Fraction(float(abs(w[r, c]))) / mg, 24)))
+            assert q[r, c] == rule(u), (r, c)
+            assert s[r, c] == (1 if w[r, c] < 0 else 0)
+    assert q[0, 3] == 15 and q[0, 7] == 15 and s[0, 7] == 1
+
+
+def test_group_zero_tiny_and_saturated_groups():
+    gs = 32
+    w = np.zeros((3, 3 * gs), np.float32)
+    w[0, 1] = 2.0 ** -26                                  # stored max rounds to 0
+    w[0, 2] = -(2.0 ** -27)
+    w[0, gs] = 2.0 ** -25                                 # a tie: rounds to 0 (even)
+    w[0, 2 * gs + 4] = -1.5 * 2.0 ** -25                  # rounds up to 2^-24
+    w[1, 5] = 1e5                                         # saturates to 65504
+    w[1, 6] = 65504.0
+    w[1, 7] = -3e4
+    q, s, m16 = O.encode_grouped(w, 0.73, gs)
+    assert list(m16[0].astype(np.float64)) == [0.0, 0.0, 2.0 ** -24]
+    assert np.all(q[0, :2 * gs] == 0)
+    assert s[0, 2] == 1 and s[0, 1] == 0                  # signs still follow w < 0
+    # u = 0.75 against the rounded-up max: 15 * 0.75^0.73 = 12.16
+    assert q[0, 2 * gs + 4] == 12 and s[0, 2 * gs + 4] == 1
+    assert float(m16[1, 0]) == 65504.0 and q[1, 5] == 15 and q[1, 6] == 15
+    assert np.all(q[2] == 0) and np.all(s[2] == 0) and np.all(m16[2] == 0)
+    pk, sg, _ = O.quantize_grouped(w, 0.73, gs)
+    d = O.dequantize_grouped(pk, sg, m16, 0.73, gs)
+    assert np.all(d[0, :2 * gs] == 0)                      # +0.0, signs ignored at code 0
+    assert np.all(d[2] == 0)
+    # q = 15 reconstructs to the stored max itself (bf16 of 65504 is 65536)
+    assert d[1, 6] == bf16_bits_of(Fraction(65504))
+
+
+@pytest.mark.parametrize("alpha,level", [
+    (1.0, lambda q: Fraction(q, 15)),
+    (0.5, lambda q: Fraction(q, 15) ** 2),
+])
+def test_group_dequant_exact_rational(alpha, level):
+    rng = np.random.default_rng(43)
+    gs = 64
+    w = (rng.standard_normal((5, 4 * gs)) * np.exp2(rng.integers(-8, 3, (5, 1)))).astype(np.float32)
+    pk, sg, m16 = O.quantize_grouped(w, alpha, gs)
+    got = O.dequantize_grouped(pk, sg, m16, alpha, gs)
+    q, s = O.unpack(pk, sg)
+    for r in range(w.shape[0]):
+        for c in range(w.shape[1]):
+            v = level(int(q[r, c])) * Fraction(float(m16[r, c // gs]))
+            if s[r, c] and q[r, c]:
+                v = -v
+            assert got[r, c] == bf16_bits_of(v), (r, c)
+
+
+@pytest.mark.parametrize("gs", [32, 128])
+def test_group_quantize_dequantize_idempotent(gs):
+    w = _to_bf16_values(_rand_rows(44, 6, 256))
+    pk, sg, m16 = O.quantize_grouped(w, 0.73, gs)
+    d1 = O.dequantize_grouped(pk, sg, m16, 0.73, gs)
+    w1 = O.bf16_bits_to_f32(d1)
+    pk2, sg2, m2 = O.quantize_grouped(w1, 0.73, gs)
+    assert np.array_equal(pk2, pk) and np.array_equal(m2, m16)
+    assert np.array_equal(O.dequantize_grouped(pk2, sg2, m2, 0.73, gs), d1)
