@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OPQ_ABI_VERSION 2
+#define OPQ_ABI_VERSION 3
 
 typedef enum {
   OPQ_OK = 0,
@@ -177,6 +177,60 @@ int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
                float alpha, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/*
+ * Group-wise stored form: the card's own ("技术细节 / 存储格式": one float16
+ * max per group of weights; the configuration section offers groups of 32,
+ * 64, 128 or 256 weights; "推理解码": the decode multiplies by that group
+ * max).  The three calls below mirror opq_quantize, opq_dequantize and
+ * opq_linear with one float16 scale per group instead of one float32 scale
+ * per row; packing, signs and the level table are the same.
+ *   group    32, 64, 128 or 256: a group is `group` consecutive weights of a
+ *            row along k; k must be a multiple of it (OPQ_ERR_SHAPE
+ *            otherwise)
+ *   scale16  [n][k/group] float16 bit patterns: the group's max|w| rounded to
+ *            float16 (nearest, ties to even), saturated at 65504
+ * Codes are taken against the stored max m16: u = |w| / m16 (binary32,
+ * nearest even), q = the integer nearest to 15 u^alpha, and q = 15 whenever
+ * u >= 1 (u exceeds 1 by less than 2^-11 when the max was rounded down); a
+ * group whose m16 is 0 (every |w| < 2^-25) gets codes 0; sign bits are 1
+ * exactly when w < 0.  Code q of a group reconstructs to bf16(G_q * m16) with
+ * the sign, code 0 to +0.0.  alpha must have a separating bucket grid (every
+ * alpha in [0.05, 60] has one) and keep G_1 * 2^-24 a normal binary32;
+ * otherwise OPQ_ERR_UNSUPPORTED.  Other conventions as for the row form.
+ */
+
+/*
+ * Quantize to the group-wise form: w device [n][k] float32 or bfloat16;
+ * packed [n][k/8], sign [n][k/32], scale16 [n][k/group] device outputs.
+ * Any k (a multiple of group and of 32).  Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE,
+ * OPQ_ERR_ALPHA, OPQ_ERR_ALIGN, OPQ_ERR_DTYPE, OPQ_ERR_UNSUPPORTED, OPQ_ERR_HIP.
+ */
+int opq_quantize_grouped(const void* w, int w_dtype, int64_t n, int64_t k, int64_t group,
+                         float alpha, uint32_t* packed, uint32_t* sign, uint16_t* scale16,
+                         void* stream);
+
+/*
+ * Dequantize the group-wise form to w_out device [n][k] bfloat16.  Any k.
+ * Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN,
+ * OPQ_ERR_UNSUPPORTED, OPQ_ERR_HIP.
+ */
+int opq_dequantize_grouped(const uint32_t* packed, const uint32_t* sign, const uint16_t* scale16,
+                           int64_t n, int64_t k, int64_t group, float alpha, uint16_t* w_out,
+                           void* stream);
+
+/*
+ * The linear layer on the group-wise form: y = x W'^T (+ bias) with W' the
+ * reconstruction opq_dequantize_grouped writes, made on chip; otherwise as
+ * opq_linear (workspace sized by opq_linear_workspace_bytes, reproducible sum
+ * order, k <= 65536).  Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA,
+ * OPQ_ERR_ALIGN, OPQ_ERR_DTYPE, OPQ_ERR_WORKSPACE, OPQ_ERR_UNSUPPORTED,
+ * OPQ_ERR_HIP.
+ */
+int opq_linear_grouped(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
+                       const uint16_t* scale16, const float* bias, int64_t m, int64_t n,
+                       int64_t k, int64_t group, float alpha, void* y, int y_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

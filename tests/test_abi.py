@@ -33,14 +33,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 9
+    assert len(names) == 12
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(opq._SIGNATURES)
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.opq_abi_version() == opq.ABI_VERSION == 2
+    assert lib.opq_abi_version() == opq.ABI_VERSION == 3
     for s in range(9):
         assert opq.status_str(s) and opq.status_str(s) != "unknown status"
     assert opq.status_str(99) == "unknown status"
@@ -143,6 +143,48 @@ def test_linear_argument_checks(lib):
     assert call(n=0) == OK
     assert call(m=0, yd=1) == OK
     assert lib.opq_linear_workspace_bytes(8, 16, 64) == opq.linear_workspace_bytes(8, 16, 64)
+
+
+def test_grouped_argument_checks(lib):
+    q = lib.opq_quantize_grouped
+    assert q(None, 1, 4, 256, 128, 0.73, FAKE, FAKE, FAKE, None) == NULL
+    assert q(FAKE, 1, 4, 256, 128, 0.73, FAKE, FAKE, None, None) == NULL
+    for gs in (16, 48, 100, 512, 0, -32):
+        assert q(FAKE, 1, 4, 512, gs, 0.73, FAKE, FAKE, FAKE, None) == SHAPE, gs
+    assert q(FAKE, 1, 4, 96, 64, 0.73, FAKE, FAKE, FAKE, None) == SHAPE   # 64 does not divide 96
+    assert q(FAKE, 1, 4, 96, 64, 0.0, FAKE, FAKE, FAKE, None) == SHAPE    # shape before alpha
+    assert q(FAKE, 1, 4, 256, 128, -1.0, FAKE, FAKE, FAKE, None) == ALPHA
+    assert q(FAKE, 1, 4, 256, 128, 0.73, FAKE, FAKE, MISALIGNED, None) == ALIGN
+    assert q(FAKE, 3, 4, 256, 128, 0.73, FAKE, FAKE, FAKE, None) == DTYPE
+    assert q(FAKE, 1, 4, 256, 128, 100.0, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert q(FAKE, 1, 4, 256, 128, 0.03, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert q(FAKE, 1, 0, 256, 128, 0.73, FAKE, FAKE, FAKE, None) == OK
+    assert q(FAKE, 1, 4, 0, 128, 0.73, FAKE, FAKE, FAKE, None) == OK
+    d = lib.opq_dequantize_grouped
+    assert d(FAKE, FAKE, None, 4, 256, 128, 0.73, FAKE, None) == NULL
+    assert d(FAKE, FAKE, FAKE, 4, 256, 96, 0.73, FAKE, None) == SHAPE
+    assert d(FAKE, FAKE, FAKE, 4, 256, 128, float("inf"), FAKE, None) == ALPHA
+    assert d(FAKE, FAKE, MISALIGNED, 4, 256, 128, 0.73, FAKE, None) == ALIGN
+    assert d(FAKE, FAKE, FAKE, 4, 256, 128, 100.0, FAKE, None) == UNSUPPORTED
+    assert d(FAKE, FAKE, FAKE, 0, 256, 128, 0.73, FAKE, None) == OK
+    f = lib.opq_linear_grouped
+    args = dict(x=FAKE, p=FAKE, s=FAKE, sc=FAKE, b=None, m=8, n=16, k=256, gs=128, a=0.73, y=FAKE,
+                yd=0, ws=None, wsb=0)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["x"], a["p"], a["s"], a["sc"], a["b"], a["m"], a["n"], a["k"], a["gs"], a["a"],
+                 a["y"], a["yd"], a["ws"], a["wsb"], None)
+
+    assert call(sc=None) == NULL
+    assert call(gs=512) == SHAPE
+    assert call(k=320, gs=256) == SHAPE
+    assert call(a=-2.0) == ALPHA
+    assert call(sc=MISALIGNED) == ALIGN
+    assert call(yd=2) == DTYPE
+    assert call(a=100.0) == UNSUPPORTED
+    assert call(k=65536 + 256, gs=256) == UNSUPPORTED
+    assert call(m=0) == OK and call(n=0) == OK
 
 
 def test_linear_workspace_sizes(lib):

@@ -15,6 +15,7 @@
 //    through LDS (details below).
 #include "decode.hpp"
 #include "device_common.hpp"
+#include "group.hpp"
 
 namespace opq {
 namespace {
@@ -68,12 +69,15 @@ constexpr int kSkBlockK = 128;                  // k per wave step
 // banks.
 __device__ __forceinline__ int xs_off(int R, int c) { return R * kSkBlockK + ((c ^ (R & 15)) << 3); }
 
-template <int NMB>             // 16-row blocks of x: 1, 2 or 4
+// GS > 0: the group-wise form (group.hpp); the lane's table is rebuilt for
+// every k block from the LDS significand table and the group max of its part.
+template <int NMB, int GS>     // NMB: 16-row blocks of x (1, 2 or 4); GS: group or 0 (per row)
 __global__ __launch_bounds__(kSkThreads) void linear_skinny(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
-    const float* __restrict__ bias, int m, int n, int k, Levels lv, void* __restrict__ y,
-    int y_bf16) {
+    const uint16_t* __restrict__ scale16, const float* __restrict__ bias, int m, int n, int k,
+    Levels lv, void* __restrict__ y, int y_bf16) {
+  static_assert(GS == 0 || NMB <= 2, "the significand table and four x row blocks overfill LDS");
   constexpr int CH = NMB == 4 ? 1 : 2;                  // k blocks per load batch
   constexpr int kXRows = 16 * NMB;
   constexpr int kXLoads = kXRows / 4;                   // x loads per lane per k block
@@ -81,7 +85,8 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   constexpr int kOut = NMB * 4 * kWave;                 // outputs per wave, accumulator order
   static_assert(kSkWaves * kOut * 4 <= kSkWaves * kStage * 2, "reduction fits the stages");
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kSkWaves * kStage];
-  __shared__ uint32_t s_lut[kSkRows][8];
+  __shared__ uint32_t s_lut[GS ? 1 : kSkRows][8];
+  __shared__ __attribute__((aligned(16))) uint32_t s_mt[GS ? kMantissas * 8 : 4];
   float* s_red = reinterpret_cast<float*>(s_x);         // after the k loop
 
   const int tid = threadIdx.x;
@@ -114,7 +119,10 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
 
   uint4 wd[2][CH];
   uint32_t sw[2][CH];
+  uint32_t hv[2][CH];  // GS > 0: float16 max of the lane's group in each k block
   uint4 xv[2][CH][kXLoads];
+  const int ngroups = GS ? k / GS : 1;
+  const uint16_t* hrow = GS ? scale16 + (int64_t)min(n0 + r, n - 1) * ngroups : nullptr;
   // Batch bi holds this wave's k blocks bi*CH .. bi*CH + CH - 1 (clamped to the
   // last).  In a final part block (k % 128 != 0) parts and chunks past k
   // re-read the block's first ones; the dequantizer zeroes those fragments.
@@ -126,6 +134,7 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
       const uint32_t kx = (uint32_t)(kb + 8 * xc < k ? kb + 8 * xc : kb);
       wd[buf][j] = *reinterpret_cast<const uint4*>(pbase + p_off + kw / 2u);
       sw[buf][j] = *reinterpret_cast<const uint32_t*>(sbase + s_off + kw / 8u);
+      if constexpr (GS > 0) hv[buf][j] = hrow[min((kb + 32 * g) / GS, ngroups - 1)];
 #pragma unroll
       for (int i = 0; i < kXLoads; ++i)  // m <= 16: groups of 4 x rows wholly past m are skipped
         if (NMB > 1 || 4 * i < m) xv[buf][j][i] = *reinterpret_cast<const uint4*>(xbase + x_off[i] + kx * 2u);
@@ -139,7 +148,8 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   // Byte planes of the block's 16 row tables: wave w < 4 makes entries
   // 4w .. 4w+3 of row `lane` (a wave-uniform code, so the levels stay in
   // scalar registers).
-  if (wave < 4 && lane < kSkRows) {
+  if constexpr (GS > 0) build_mant_table(lv, s_mt);
+  if (GS == 0 && wave < 4 && lane < kSkRows) {
     const float mr = scale[min(n0 + lane, n - 1)];
     uint32_t lo = 0u, hi = 0u;
 #pragma unroll
@@ -155,7 +165,7 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __builtin_amdgcn_s_barrier();
   RowLut lut;
-  {
+  if constexpr (GS == 0) {
     const uint4 lo = *reinterpret_cast<const uint4*>(&s_lut[r][0]);
     const uint4 hi = *reinterpret_cast<const uint4*>(&s_lut[r][4]);
     lut.lo[0] = lo.x; lut.lo[1] = lo.y; lut.lo[2] = lo.z; lut.lo[3] = lo.w;
@@ -188,6 +198,7 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
             (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)wd[buf][j].z),
             (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)wd[buf][j].w)};
         const uint32_t sb = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sw[buf][j]);
+        if constexpr (GS > 0) lut = group_lut(s_mt, hv[buf][j]);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           uint32_t o[4];
@@ -489,16 +500,21 @@ __global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
 // ds_read_b32 per lane.  Everything else is as in linear_mfma.
 constexpr int kWRec = 20;  // uint32 per weight row record: 16 code words + 4 sign words
 
-template <bool kHalfTail>
+//
+// GS > 0: the group-wise form (group.hpp).  The lane's table is rebuilt from
+// the LDS significand table before the first sub-step of every k step; the
+// float16 group maxima are loaded two steps ahead.
+template <bool kHalfTail, int GS>
 __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
-    const float* __restrict__ bias, int m, int n, int k, int tiles_m, Levels lv,
-    void* __restrict__ y, int y_bf16) {
+    const uint16_t* __restrict__ scale16, const float* __restrict__ bias, int m, int n, int k,
+    int tiles_m, Levels lv, void* __restrict__ y, int y_bf16) {
   constexpr int kThreads = 512;
   constexpr int XCH = kTM * kTK / 8 / kThreads;     // x chunks each thread stages per step (4)
   __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kAStage];
   __shared__ __attribute__((aligned(16))) uint32_t s_w[2][kTN][kWRec];
+  __shared__ __attribute__((aligned(16))) uint32_t s_mt[GS ? kMantissas * 8 : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -513,7 +529,18 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
   const int npairs = (nsteps + 1) / 2;
 
   const int brow = nw + (lane & 31);
-  const RowLut lut = make_row_lut(lv, scale[min(brow, n - 1)]);
+  RowLut lut;
+  if constexpr (GS == 0) lut = make_row_lut(lv, scale[min(brow, n - 1)]);
+  // GS > 0: float16 max of this lane's group in step kt (its half of the step)
+  const int ngroups = GS ? k / GS : 1;
+  const uint16_t* hrow = GS ? scale16 + (int64_t)min(brow, n - 1) * ngroups : nullptr;
+  auto load_h = [&](int kt) __attribute__((always_inline)) -> uint32_t {
+    if constexpr (GS > 0)
+      return hrow[min((min(kt, nsteps - 1) * kTK + 32 * g) / GS, ngroups - 1)];
+    else
+      return 0u;
+  };
+  uint32_t h_next = 0u, h_load = 0u;  // maxima of steps kt + 1 and kt + 2
 
   // Weight loads for step pair p (steps 2p, 2p + 1): thread t moves 16 code
   // bytes (quarter t % 4) of tile rows t/4 and t/4 + 128, and sign words
@@ -612,13 +639,20 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
   uint4 xa[XCH];
   bf16x8_t a_buf[2][8], b_buf[2];
   if (nsteps > 0) {
+    uint32_t h0 = 0u;
+    if constexpr (GS > 0) {
+      h0 = load_h(0);
+      h_next = load_h(1);
+    }
     load_a(0, xa);
     load_w(0);
+    if constexpr (GS > 0) build_mant_table(lv, s_mt);
     store_a(0, xa);
     store_w(0);
     load_a(1, xa);
     load_w(1);
     __syncthreads();
+    if constexpr (GS > 0) lut = group_lut(s_mt, h0);
     read_w(0, pw, sw);
     read_a(s_a, 0, a_buf[0]);
     dequant_b(0, 0, pw, sw, b_buf[0]);
@@ -637,12 +671,17 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
         __syncthreads();
         read_a(s_a + (stage ^ 1) * kAStage, 0, a_buf[nxt]);
         read_w(kt + 1, pw, sw);  // this step's words are dead after sub-step 2
+        if constexpr (GS > 0) {
+          lut = group_lut(s_mt, h_next);  // the table of step kt + 1
+          h_next = h_load;
+        }
         dequant_b(kt + 1, 0, pw, sw, b_buf[nxt]);
       }
 #pragma unroll
       for (int mi = 0; mi < 8; ++mi)
         acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_buf[cur][mi], b_buf[cur], acc[mi], 0, 0, 0);
       if (s == 0) {
+        if constexpr (GS > 0) h_load = load_h(kt + 2);
         store_a(stage ^ 1, xa);
         load_a(kt + 2, xa);
         if (even) {
@@ -675,25 +714,75 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
 
 size_t linear_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
+namespace {
+
+template <int GS>
+hipError_t launch_linear_any(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
+                             const float* scale, const uint16_t* scale16, const float* bias,
+                             int64_t m, int64_t n, int64_t k, const Levels& lv, void* y,
+                             bool y_bf16, hipStream_t stream) {
+  if (m <= kSkinnyMaxM) {
+    const int64_t blocks = (n + kSkRows - 1) / kSkRows;
+    if (GS > 0 && m > 32) {
+      // The significand table leaves no room for four x row blocks: two
+      // launches of up to 32 x rows each.
+      hipLaunchKernelGGL((linear_skinny<2, GS>), dim3((unsigned)blocks), dim3(kSkThreads), 0,
+                         stream, x, packed, sign, scale, scale16, bias, 32, (int)n, (int)k, lv, y,
+                         (int)y_bf16);
+      const int64_t ybytes = y_bf16 ? 2 : 4;
+      hipLaunchKernelGGL((linear_skinny<2, GS>), dim3((unsigned)blocks), dim3(kSkThreads), 0,
+                         stream, x + 32 * k, packed, sign, scale, scale16, bias, (int)(m - 32),
+                         (int)n, (int)k, lv, static_cast<char*>(y) + 32 * n * ybytes,
+                         (int)y_bf16);
+      return hipGetLastError();
+    }
+    auto kernel = m <= 16 ? linear_skinny<1, GS>
+                          : (m <= 32 ? linear_skinny<2, GS> : linear_skinny<(GS ? 2 : 4), GS>);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kSkThreads), 0, stream, x, packed,
+                       sign, scale, scale16, bias, (int)m, (int)n, (int)k, lv, y, (int)y_bf16);
+  } else {
+    const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
+    if (GS > 0 || kWeightStage) {
+      auto kernel = (k % kTK) ? linear_mfma_ws<true, GS> : linear_mfma_ws<false, GS>;
+      hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream, x,
+                         packed, sign, scale, scale16, bias, (int)m, (int)n, (int)k,
+                         (int)tiles_m, lv, y, (int)y_bf16);
+    } else {
+      auto kernel = (k % kTK) ? linear_mfma<true, kMfmaWaves, kMfmaXSplit>
+                              : linear_mfma<false, kMfmaWaves, kMfmaXSplit>;
+      hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMfmaWaves * kWave), 0,
+                         stream, x, packed, sign, scale, bias, (int)m, (int)n, (int)k,
+                         (int)tiles_m, lv, y, (int)y_bf16);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
 hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                          const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
                          const Levels& lv, void* y, bool y_bf16, void*, hipStream_t stream) {
-  if (m <= kSkinnyMaxM) {
-    const int64_t blocks = (n + kSkRows - 1) / kSkRows;
-    auto kernel = m <= 16 ? linear_skinny<1> : (m <= 32 ? linear_skinny<2> : linear_skinny<4>);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kSkThreads), 0, stream, x, packed,
-                       sign, scale, bias, (int)m, (int)n, (int)k, lv, y, (int)y_bf16);
-  } else {
-    const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
-    auto kernel = kWeightStage ? ((k % kTK) ? linear_mfma_ws<true> : linear_mfma_ws<false>)
-                  : ((k % kTK) ? linear_mfma<true, kMfmaWaves, kMfmaXSplit>
-                               : linear_mfma<false, kMfmaWaves, kMfmaXSplit>);
-    const int threads = kWeightStage ? 512 : kMfmaWaves * kWave;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(threads), 0, stream,
-                       x, packed, sign, scale, bias, (int)m, (int)n, (int)k, (int)tiles_m, lv, y,
-                       (int)y_bf16);
+  return launch_linear_any<0>(x, packed, sign, scale, nullptr, bias, m, n, k, lv, y, y_bf16,
+                              stream);
+}
+
+hipError_t launch_linear_grouped(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
+                                 const uint16_t* scale16, const float* bias, int64_t m, int64_t n,
+                                 int64_t k, int gs, const Levels& lv, void* y, bool y_bf16,
+                                 void*, hipStream_t stream) {
+#define OPQ_GROUP_CASE(G)                                                                       \
+  case G:                                                                                       \
+    return launch_linear_any<G>(x, packed, sign, nullptr, scale16, bias, m, n, k, lv, y, y_bf16, \
+                                stream);
+  switch (gs) {
+    OPQ_GROUP_CASE(32)
+    OPQ_GROUP_CASE(64)
+    OPQ_GROUP_CASE(128)
+    OPQ_GROUP_CASE(256)
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+#undef OPQ_GROUP_CASE
 }
 
 }  // namespace opq

@@ -20,6 +20,10 @@ bool alpha_ok(float a) { return std::isfinite(a) && a > 0.0f; }
 
 bool shape_ok(int64_t n, int64_t k) { return n >= 0 && k >= 0 && k % 32 == 0; }
 
+bool group_ok(int64_t k, int64_t gs) {
+  return (gs == 32 || gs == 64 || gs == 128 || gs == 256) && k % gs == 0;
+}
+
 int hip_status(hipError_t e) { return e == hipSuccess ? OPQ_OK : OPQ_ERR_HIP; }
 
 }  // namespace
@@ -32,7 +36,9 @@ const char* opq_status_str(int status) {
   switch (status) {
     case OPQ_OK: return "ok";
     case OPQ_ERR_NULL: return "a required pointer is NULL";
-    case OPQ_ERR_SHAPE: return "bad shape: sizes must be >= 0 and k a multiple of 32";
+    case OPQ_ERR_SHAPE:
+      return "bad shape: sizes must be >= 0, k a multiple of 32 (and of the group, which is "
+             "32, 64, 128 or 256)";
     case OPQ_ERR_ALPHA: return "alpha must be finite and > 0";
     case OPQ_ERR_ALIGN: return "every array must be 16-byte aligned";
     case OPQ_ERR_DTYPE: return "unknown dtype code";
@@ -131,6 +137,72 @@ int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign, 
   return hip_status(opq::launch_linear(x, packed, sign, scale, bias, m, n, k, lv, y,
                                        y_dtype == OPQ_BF16, workspace,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int opq_quantize_grouped(const void* w, int w_dtype, int64_t n, int64_t k, int64_t group,
+                         float alpha, uint32_t* packed, uint32_t* sign, uint16_t* scale16,
+                         void* stream) {
+  const bool nk = n > 0 && k > 0;
+  if (nk && (!w || !packed || !sign || !scale16)) return OPQ_ERR_NULL;
+  if (!shape_ok(n, k) || !group_ok(k, group)) return OPQ_ERR_SHAPE;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(sign) || !aligned16(scale16))
+    return OPQ_ERR_ALIGN;
+  if (w_dtype != OPQ_F32 && w_dtype != OPQ_BF16) return OPQ_ERR_DTYPE;
+  if (!nk) return OPQ_OK;
+  opq::DecisionPoints dp;
+  if (!opq::decision_points(alpha, dp.t)) return OPQ_ERR_ALPHA;
+  opq::Levels lv;
+  opq::levels(alpha, lv.g);
+  if (!opq::grouped_supported(dp, lv)) return OPQ_ERR_UNSUPPORTED;
+  return hip_status(opq::launch_quantize_grouped(w, w_dtype == OPQ_BF16, n, k, (int)group, dp,
+                                                 packed, sign, scale16,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+int opq_dequantize_grouped(const uint32_t* packed, const uint32_t* sign, const uint16_t* scale16,
+                           int64_t n, int64_t k, int64_t group, float alpha, uint16_t* w_out,
+                           void* stream) {
+  if (n > 0 && k > 0 && (!packed || !sign || !scale16 || !w_out)) return OPQ_ERR_NULL;
+  if (!shape_ok(n, k) || !group_ok(k, group)) return OPQ_ERR_SHAPE;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  if (!aligned16(packed) || !aligned16(sign) || !aligned16(scale16) || !aligned16(w_out))
+    return OPQ_ERR_ALIGN;
+  if (n == 0 || k == 0) return OPQ_OK;
+  opq::DecisionPoints dp;
+  if (!opq::decision_points(alpha, dp.t)) return OPQ_ERR_ALPHA;
+  opq::Levels lv;
+  opq::levels(alpha, lv.g);
+  if (!opq::grouped_supported(dp, lv)) return OPQ_ERR_UNSUPPORTED;
+  return hip_status(opq::launch_dequantize_grouped(packed, sign, scale16, n, k, (int)group, lv,
+                                                   w_out, static_cast<hipStream_t>(stream)));
+}
+
+int opq_linear_grouped(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
+                       const uint16_t* scale16, const float* bias, int64_t m, int64_t n,
+                       int64_t k, int64_t group, float alpha, void* y, int y_dtype,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  if ((m > 0 && k > 0 && !x) || (n > 0 && k > 0 && (!packed || !sign || !scale16)) ||
+      (m > 0 && n > 0 && !y))
+    return OPQ_ERR_NULL;
+  if (m < 0 || !shape_ok(n, k) || !group_ok(k, group)) return OPQ_ERR_SHAPE;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(sign) || !aligned16(scale16) ||
+      !aligned16(y) || (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)))
+    return OPQ_ERR_ALIGN;
+  if (y_dtype != OPQ_F32 && y_dtype != OPQ_BF16) return OPQ_ERR_DTYPE;
+  const size_t need = opq::linear_workspace_bytes(m, n, k);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return OPQ_ERR_WORKSPACE;
+  if (m == 0 || n == 0) return OPQ_OK;
+  if (k > kMaxK) return OPQ_ERR_UNSUPPORTED;
+  opq::DecisionPoints dp;
+  if (!opq::decision_points(alpha, dp.t)) return OPQ_ERR_ALPHA;
+  opq::Levels lv;
+  opq::levels(alpha, lv.g);
+  if (!opq::grouped_supported(dp, lv)) return OPQ_ERR_UNSUPPORTED;
+  return hip_status(opq::launch_linear_grouped(x, packed, sign, scale16, bias, m, n, k,
+                                               (int)group, lv, y, y_dtype == OPQ_BF16, workspace,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -46,4 +46,20 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32
                          const Levels& lv, void* y, bool y_bf16, void* workspace,
                          hipStream_t stream);
 
+// Group-wise form (one float16 max per `gs` weights along k).
+// quantize.hip: alpha has a bucket grid and G_1 * 2^-24 is a normal binary32
+bool grouped_supported(const DecisionPoints& dp, const Levels& lv);
+hipError_t launch_quantize_grouped(const void* w, bool w_is_bf16, int64_t n, int64_t k, int gs,
+                                   const DecisionPoints& dp, uint32_t* packed, uint32_t* sign,
+                                   uint16_t* scale16, hipStream_t stream);
+// dequantize.hip
+hipError_t launch_dequantize_grouped(const uint32_t* packed, const uint32_t* sign,
+                                     const uint16_t* scale16, int64_t n, int64_t k, int gs,
+                                     const Levels& lv, uint16_t* out, hipStream_t stream);
+// linear.hip
+hipError_t launch_linear_grouped(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
+                                 const uint16_t* scale16, const float* bias, int64_t m, int64_t n,
+                                 int64_t k, int gs, const Levels& lv, void* y, bool y_bf16,
+                                 void* workspace, hipStream_t stream);
+
 }  // namespace opq

@@ -25,6 +25,9 @@
 // back to counting against per-row magnitude thresholds: u >= T_k  <=>
 // |w| >= A_k with A_k the smallest binary32 a such that fl32(a / m) >= T_k.
 #include "device_common.hpp"
+#include "group.hpp"
+
+#include <algorithm>
 
 namespace opq {
 namespace {
@@ -715,6 +718,125 @@ hipError_t dispatch(const T* w, int64_t n, int64_t k, const DecisionPoints& dp, 
   return launch_rows<T, 0>(w, n, k, dp, packed, sign, scale, stream);
 }
 
+// ---------------------------------------------------------------- group-wise form
+//
+// The weights stream as one flat array of n*k elements.  A wave takes 512
+// consecutive elements (8 per lane) at a time; groups never straddle them
+// (gs divides both 512 and k), so a group is gs/8 consecutive lanes and its
+// max comes from a butterfly over those lanes.  The codes are then found as in
+// the row kernels, against the stored float16 max, whose reciprocal is exact
+// enough for the fast path because m16 >= 2^-24 is a normal binary32.  After
+// the table build there is no block barrier: waves run independently, each
+// with its next chunks' loads in flight while it encodes.
+constexpr int kGThreads = 256;
+constexpr int kGWaves = kGThreads / kWave;
+constexpr int kGUnroll = 2;  // chunks per wave per batch
+
+template <typename T, int GS>
+__global__ __launch_bounds__(kGThreads) void quantize_grouped_rows(
+    const T* __restrict__ w, int64_t total, DecisionPoints dp, BucketGrid g,
+    uint32_t* __restrict__ packed, uint32_t* __restrict__ sign, uint16_t* __restrict__ scale16) {
+  static_assert(GS >= 32 && GS <= 256 && (GS & (GS - 1)) == 0, "group of 32..256");
+  constexpr int kLanes = GS / 8;  // lanes per group
+  __shared__ uint2 s_tab[kMaxBuckets];
+  __shared__ float s_pts[kLevels + 1];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t nchunks = (total + kChunk - 1) / kChunk;
+  const int64_t wid = (int64_t)blockIdx.x * kGWaves + threadIdx.x / kWave;
+  const int64_t step = (int64_t)gridDim.x * kGWaves * kGUnroll;
+
+  Slot<T> v[2][kGUnroll];
+  auto load = [&](int64_t cb, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kGUnroll; ++u) {
+      const int64_t e0 = (cb + u) * kChunk + lane * 8;
+      if (e0 < total) v[buf][u].load(w + e0); else v[buf][u].zero();
+    }
+  };
+  int64_t cb = wid * kGUnroll;  // first chunk of this wave's batch
+  if (cb < nchunks) load(cb, 0);
+
+  build_table(dp, g, s_tab);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int j = 0; j < kLevels; ++j) s_pts[j] = dp.t[j];
+    s_pts[kLevels] = 2.0f;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the table is written
+  __builtin_amdgcn_s_barrier();
+  const int shift = g.shift;
+  const uint32_t nbase = (0u - (g.b0 >> g.shift)) << 3;
+  const float ulo = __uint_as_float(g.b0);
+
+  auto process = [&](int64_t c, int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < kGUnroll; ++u) {
+      const int64_t e0 = (c + u) * kChunk + lane * 8;
+      const bool valid = e0 < total;
+      float mx = slot_absmax(v[buf][u]);
+#pragma unroll
+      for (int off = 1; off < kLanes; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+      const uint32_t h = f16_bits_rn(mx);
+      const float m16 = f16_value(h);
+      const bool fast = m16 > 0.0f;
+      const float r = fast ? 1.0f / m16 : 0.0f;
+      const uint32_t word = encode_chunk(v[buf][u], m16, r, fast, s_tab, shift, nbase, ulo, s_pts);
+      const int64_t wi = valid ? (e0 >> 3) : 0;
+      store_word(packed + wi, sign + (wi >> 2), 0, lane, valid, word, sign_byte(v[buf][u]));
+      if (valid && lane % kLanes == 0) scale16[e0 / GS] = (uint16_t)h;
+    }
+  };
+
+  while (cb < nchunks) {
+    const int64_t c1 = cb + step;
+    if (c1 < nchunks) load(c1, 1);
+    process(cb, 0);
+    if (c1 >= nchunks) break;
+    const int64_t c2 = c1 + step;
+    if (c2 < nchunks) load(c2, 0);
+    process(c1, 1);
+    cb = c2;
+  }
+}
+
+template <typename T, int GS>
+hipError_t launch_grouped_rows(const T* w, int64_t total, const DecisionPoints& dp,
+                               const BucketGrid& g, uint32_t* packed, uint32_t* sign,
+                               uint16_t* scale16, hipStream_t stream) {
+  static const int per_cu = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, quantize_grouped_rows<T, GS>, kGThreads,
+                                                     0) != hipSuccess || b < 1)
+      b = 1;
+    return b;
+  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 1;
+  const int64_t batches = (total + (int64_t)kChunk * kGUnroll - 1) / ((int64_t)kChunk * kGUnroll);
+  int64_t blocks = (int64_t)per_cu * cus;
+  blocks = std::min<int64_t>(blocks, (batches + kGWaves - 1) / kGWaves);
+  hipLaunchKernelGGL((quantize_grouped_rows<T, GS>), dim3((unsigned)blocks), dim3(kGThreads), 0,
+                     stream, w, total, dp, g, packed, sign, scale16);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dispatch_grouped(const T* w, int64_t total, int gs, const DecisionPoints& dp,
+                            uint32_t* packed, uint32_t* sign, uint16_t* scale16,
+                            hipStream_t stream) {
+  BucketGrid g;
+  if (!bucket_grid(dp, g)) return hipErrorNotSupported;
+  switch (gs) {
+    case 32: return launch_grouped_rows<T, 32>(w, total, dp, g, packed, sign, scale16, stream);
+    case 64: return launch_grouped_rows<T, 64>(w, total, dp, g, packed, sign, scale16, stream);
+    case 128: return launch_grouped_rows<T, 128>(w, total, dp, g, packed, sign, scale16, stream);
+    case 256: return launch_grouped_rows<T, 256>(w, total, dp, g, packed, sign, scale16, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 bool error_sums_supported(const DecisionPoints& dp, int64_t k) {
@@ -736,6 +858,22 @@ hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, int64_t k,
   if (w_is_bf16)
     return dispatch(static_cast<const uint16_t*>(w), n, k, dp, packed, sign, scale, stream);
   return dispatch(static_cast<const float*>(w), n, k, dp, packed, sign, scale, stream);
+}
+
+bool grouped_supported(const DecisionPoints& dp, const Levels& lv) {
+  BucketGrid g;
+  // every level times the smallest stored max (2^-24) stays a normal binary32
+  return bucket_grid(dp, g) && lv.g[1] * 0x1p-24 >= 0x1p-126;
+}
+
+hipError_t launch_quantize_grouped(const void* w, bool w_is_bf16, int64_t n, int64_t k, int gs,
+                                   const DecisionPoints& dp, uint32_t* packed, uint32_t* sign,
+                                   uint16_t* scale16, hipStream_t stream) {
+  if (w_is_bf16)
+    return dispatch_grouped(static_cast<const uint16_t*>(w), n * k, gs, dp, packed, sign, scale16,
+                            stream);
+  return dispatch_grouped(static_cast<const float*>(w), n * k, gs, dp, packed, sign, scale16,
+                          stream);
 }
 
 }  // namespace opq

@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libopq.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 OPQ_F32 = 0
 OPQ_BF16 = 1
@@ -44,6 +44,18 @@ _SIGNATURES = {
                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                   ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]),
+    "opq_quantize_grouped": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p]),
+    "opq_dequantize_grouped": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                              ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]),
+    "opq_linear_grouped": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                          ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
 }
 
 _lib: Optional[ctypes.CDLL] = None
@@ -130,6 +142,18 @@ class QuantizedWeight(NamedTuple):
         return (self.packed.shape[0], self.packed.shape[1] * 8)
 
 
+class GroupedWeight(NamedTuple):
+    """The group-wise stored form: one float16 max per `group` weights along k."""
+    packed: torch.Tensor   # int32 [n, k/8]
+    sign: torch.Tensor     # int32 [n, k/32]
+    scale16: torch.Tensor  # float16 [n, k/group]: stored group maxima
+    group: int             # 32, 64, 128 or 256
+
+    @property
+    def shape(self):
+        return (self.packed.shape[0], self.packed.shape[1] * 8)
+
+
 def quantize(w: torch.Tensor, alpha: float, out: Optional[QuantizedWeight] = None) -> QuantizedWeight:
     """Quantize a float32 or bfloat16 weight [n, k] on its device."""
     if w.dtype not in (torch.float32, torch.bfloat16):
@@ -148,9 +172,49 @@ def quantize(w: torch.Tensor, alpha: float, out: Optional[QuantizedWeight] = Non
     return out
 
 
-def dequantize(qw: QuantizedWeight, alpha: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """bfloat16 reconstruction [n, k] of a quantized weight."""
+def quantize_grouped(w: torch.Tensor, alpha: float, group: int = 128,
+                     out: Optional[GroupedWeight] = None) -> GroupedWeight:
+    """Quantize a float32 or bfloat16 weight [n, k] to the group-wise form."""
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("w must be float32 or bfloat16")
+    _need_cuda("w", w, w.dtype, 2)
+    n, k = w.shape
+    if group not in (32, 64, 128, 256) or k % group:
+        raise ValueError(f"group must be 32, 64, 128 or 256 and divide k={k}, got {group}")
+    if out is None:
+        out = GroupedWeight(
+            torch.empty((n, k // 8), dtype=torch.int32, device=w.device),
+            torch.empty((n, k // 32), dtype=torch.int32, device=w.device),
+            torch.empty((n, k // group), dtype=torch.float16, device=w.device), group)
+    _check_grouped(out, n, k)
+    dtype = OPQ_BF16 if w.dtype == torch.bfloat16 else OPQ_F32
+    st = load().opq_quantize_grouped(_ptr(w), dtype, n, k, out.group, alpha, _ptr(out.packed),
+                                     _ptr(out.sign), _ptr(out.scale16), _stream(w.device))
+    _check("opq_quantize_grouped", st)
+    return out
+
+
+def _check_grouped(gw: GroupedWeight, n: int, k: int) -> None:
+    for name, t, dt in (("packed", gw.packed, torch.int32), ("sign", gw.sign, torch.int32),
+                        ("scale16", gw.scale16, torch.float16)):
+        _need_cuda(name, t, dt, 2)
+    if (tuple(gw.packed.shape) != (n, k // 8) or tuple(gw.sign.shape) != (n, k // 32) or
+            gw.group not in (32, 64, 128, 256) or tuple(gw.scale16.shape) != (n, k // gw.group)):
+        raise ValueError(f"grouped weight buffers do not match n={n}, k={k}, group={gw.group}")
+
+
+def dequantize(qw, alpha: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """bfloat16 reconstruction [n, k] of a QuantizedWeight or GroupedWeight."""
     n, k = qw.shape
+    if isinstance(qw, GroupedWeight):
+        _check_grouped(qw, n, k)
+        if out is None:
+            out = torch.empty((n, k), dtype=torch.bfloat16, device=qw.packed.device)
+        _need_cuda("out", out, torch.bfloat16, 2)
+        st = load().opq_dequantize_grouped(_ptr(qw.packed), _ptr(qw.sign), _ptr(qw.scale16), n, k,
+                                           qw.group, alpha, _ptr(out), _stream(qw.packed.device))
+        _check("opq_dequantize_grouped", st)
+        return out
     for name, t, dt in (("packed", qw.packed, torch.int32), ("sign", qw.sign, torch.int32)):
         _need_cuda(name, t, dt, 2)
     _need_cuda("scale", qw.scale, torch.float32, 1)
@@ -216,10 +280,11 @@ def shared_workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor
     return ws
 
 
-def linear(x: torch.Tensor, qw: QuantizedWeight, alpha: float, bias: Optional[torch.Tensor] = None,
+def linear(x: torch.Tensor, qw, alpha: float, bias: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
-    """y[m, n] = x[m, k] W'^T (+ bias), W' made on chip from qw.
+    """y[m, n] = x[m, k] W'^T (+ bias), W' made on chip from qw (a QuantizedWeight
+    or a GroupedWeight).
 
     out_dtype is torch.float32 or torch.bfloat16 (the float32 result rounded
     to nearest even).  `workspace`, when given, must be a zero-filled uint8
@@ -250,6 +315,13 @@ def linear(x: torch.Tensor, qw: QuantizedWeight, alpha: float, bias: Optional[to
     elif not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous CUDA (HIP) tensor")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if isinstance(qw, GroupedWeight):
+        _check_grouped(qw, n, k)
+        st = load().opq_linear_grouped(_ptr(x), _ptr(qw.packed), _ptr(qw.sign), _ptr(qw.scale16),
+                                       _ptr(bias), m, n, k, qw.group, alpha, _ptr(out), y_dtype,
+                                       _ptr(workspace), ws_bytes, _stream(x.device))
+        _check("opq_linear_grouped", st)
+        return out
     st = load().opq_linear(_ptr(x), _ptr(qw.packed), _ptr(qw.sign), _ptr(qw.scale), _ptr(bias),
                            m, n, k, alpha, _ptr(out), y_dtype, _ptr(workspace), ws_bytes,
                            _stream(x.device))
