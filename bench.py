@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--workload", default="skinny",
                     choices=["skinny", "qkv", "ffn_up", "ffn_down", "tiny", "model"])
     ap.add_argument("--alpha", type=float, default=0.73)
+    ap.add_argument("--group", type=int, default=0, choices=[0, 32, 64, 128, 256],
+                    help="0: one float32 max per row; else the group-wise form (float16 max "
+                         "per this many weights along k)")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for > 768 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -72,11 +75,13 @@ def workload(name):
     return L
 
 
-def algorithmic(m, n, k, w_bytes):
-    """Per-launch algorithmic bytes / flops (what the method must move)."""
-    quant = {"bytes": n * k * (w_bytes + 0.625) + 4 * n, "flops": 0}
-    dequant = {"bytes": n * k * (0.625 + 2) + 4 * n, "flops": 0}
-    lin = {"bytes": 0.625 * n * k + 4 * n + 2 * m * k + 4 * m * n, "flops": 2 * m * n * k}
+def algorithmic(m, n, k, w_bytes, group=0):
+    """Per-launch algorithmic bytes / flops (what the method must move).  The
+    scales are 4 B per row, or 2 B per group of `group` weights."""
+    sc = 2 * n * (k // group) if group else 4 * n
+    quant = {"bytes": n * k * (w_bytes + 0.625) + sc, "flops": 0}
+    dequant = {"bytes": n * k * (0.625 + 2) + sc, "flops": 0}
+    lin = {"bytes": 0.625 * n * k + sc + 2 * m * k + 4 * m * n, "flops": 2 * m * n * k}
     return {"quantize": quant, "dequantize": dequant, "linear": lin}
 
 
@@ -98,7 +103,8 @@ def source_hash(kind):
 
 def measured_traffic(kind, workload_name):
     """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernel source changed since it was taken."""
+    there is none or the kernel source changed since it was taken.  Grouped
+    runs are named <workload>_g<group>."""
     path = os.path.join(PROFILES, f"{kind}_{workload_name}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -117,7 +123,7 @@ def measured_traffic(kind, workload_name):
 
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(L, x_bits, w_vals, alpha, seconds, ideal_total_us):
+def cpu_baseline(L, x_bits, w_vals, alpha, seconds, ideal_total_us, group=0):
     """The oracle, as it stands, over the whole workload, repeated until
     `seconds` have passed (at least once); BLAS limited to one thread."""
     import oracle as O
@@ -129,8 +135,12 @@ def cpu_baseline(L, x_bits, w_vals, alpha, seconds, ideal_total_us):
     reps = 0
     t0 = time.perf_counter()
     while True:
-        p, s, m = O.quantize(w_vals, alpha)
-        d = O.dequantize(p, s, m, alpha)
+        if group:
+            p, s, m = O.quantize_grouped(w_vals, alpha, group)
+            d = O.dequantize_grouped(p, s, m, alpha, group)
+        else:
+            p, s, m = O.quantize(w_vals, alpha)
+            d = O.dequantize(p, s, m, alpha)
         O.linear(x_bits, d)
         reps += 1
         el = time.perf_counter() - t0
@@ -187,15 +197,25 @@ def main():
         w_bytes = 4
     x_host = WL.to_bf16(L.make_x())
 
-    alg = algorithmic(m, n, k, w_bytes)
+    group = args.group
+    if group and k % group:
+        print(f"--group {group} does not divide k={k}", file=sys.stderr)
+        sys.exit(2)
+    alg = algorithmic(m, n, k, w_bytes, group)
     per_set = (n * k * w_bytes + n * k * 0.625 + 4 * n + n * k * 2 + m * k * 2 + m * n * 4)
     rot = args.rotate or max(2, int(np.ceil(800e6 / per_set)))
     sets = []
     for _ in range(rot):
         w = w_host.to(dev)
-        qw = opq.QuantizedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
-                                 torch.empty((n, k // 32), dtype=torch.int32, device=dev),
-                                 torch.empty((n,), dtype=torch.float32, device=dev))
+        if group:
+            qw = opq.GroupedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
+                                   torch.empty((n, k // 32), dtype=torch.int32, device=dev),
+                                   torch.empty((n, k // group), dtype=torch.float16, device=dev),
+                                   group)
+        else:
+            qw = opq.QuantizedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
+                                     torch.empty((n, k // 32), dtype=torch.int32, device=dev),
+                                     torch.empty((n,), dtype=torch.float32, device=dev))
         d = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
         x = x_host.to(dev)
         y = torch.empty((m, n), dtype=torch.float32, device=dev)
@@ -207,7 +227,10 @@ def main():
     def launch(kind, i):
         w, qw, d, x, y = sets[i % rot]
         if kind == "quantize":
-            opq.quantize(w, alpha, out=qw)
+            if group:
+                opq.quantize_grouped(w, alpha, group, out=qw)
+            else:
+                opq.quantize(w, alpha, out=qw)
         elif kind == "dequantize":
             opq.dequantize(qw, alpha, out=d)
         else:
@@ -281,7 +304,8 @@ def main():
         roof = {"bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4)}
     roof["kernel"] = dom
-    roof["traffic"] = measured_traffic(dom, args.workload)
+    wl_name = f"{args.workload}_g{group}" if group else args.workload
+    roof["traffic"] = measured_traffic(dom, wl_name)
 
     value = 100.0 * (ideal_total * 1e-3) / ms_step
 
@@ -300,6 +324,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{args.workload}: {WL_title(args.workload)}", "m": m, "n": n,
                    "k": k, "w_dtype": L.w_dtype, "alpha": alpha, "rotating_sets": rot,
+                   "scales": (f"float16 per group of {group}" if group else "float32 per row"),
                    "step": "quantize -> dequantize -> linear"},
         "roofline": roof,
         "kernels": kern,
@@ -311,7 +336,8 @@ def main():
         xb = WL.bf16_bits(x_host)
         wv = (O.bf16_bits_to_f32(WL.bf16_bits(w_host)) if L.w_dtype == "bf16"
               else w_host.numpy())
-        out["cpu_baseline"] = cpu_baseline(L, xb, wv, alpha, args.cpu_seconds, ideal_total)
+        out["cpu_baseline"] = cpu_baseline(L, xb, wv, alpha, args.cpu_seconds, ideal_total,
+                                           group)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

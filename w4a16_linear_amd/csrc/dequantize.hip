@@ -15,8 +15,6 @@
 #include "device_common.hpp"
 #include "group.hpp"
 
-#include <algorithm>
-
 namespace opq {
 namespace {
 
@@ -62,54 +60,53 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void dequantize_rows(
   }
 }
 
-// Group-wise form.  The codes stream as one flat array: a lane decodes one
-// packed word (eight codes of one group) per 512-element chunk, kGUnroll
-// chunks' loads in flight.  Each block first writes the 1024 x 16 table of
-// bf16(G_q (1 + mt/1024)) to LDS (group.hpp, while its first loads are in
-// flight); a lane's group table is then one table row with the group max's
-// exponent added, held as byte planes for the v_perm decoder.
+// Group-wise form.  The codes stream as one flat array; a lane decodes
+// kGWords consecutive packed words (8 kGWords codes, which lie in one group)
+// per chunk: it makes that group's table itself (make_row_lut with the
+// float16 max, the code index uniform so the levels stay in scalar
+// registers), then moves 4 kGWords bytes of codes and 16 kGWords of bf16.
+// Each wave takes kGUnroll chunks with all their loads in flight; there is no
+// LDS and no barrier, so the grid is simply one wave per kGUnroll chunks.
 constexpr int kGThreads = 256;
-constexpr int kGUnroll = 4;
+constexpr int kGUnroll = 2;
+constexpr int kGWords = 2;                   // packed words per lane per chunk
+constexpr int kGChunk = kWave * 8 * kGWords;  // elements per wave per chunk
 
 template <int GS>
 __global__ __launch_bounds__(kGThreads) void dequantize_grouped_rows(
     const uint32_t* __restrict__ packed, const uint32_t* __restrict__ sign,
     const uint16_t* __restrict__ scale16, int64_t total, Levels lv, uint16_t* __restrict__ out) {
-  __shared__ __attribute__((aligned(16))) uint32_t s_mt[kMantissas * 8];
+  static_assert(GS % (8 * kGWords) == 0, "a lane's codes lie in one group");
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t nchunks = (total + kChunk - 1) / kChunk;
   const int64_t wid = (int64_t)blockIdx.x * (kGThreads / kWave) + threadIdx.x / kWave;
-  const int64_t step = (int64_t)gridDim.x * (kGThreads / kWave) * kGUnroll;
-
-  uint32_t wv[kGUnroll], sv[kGUnroll], hv[kGUnroll];
-  auto load = [&](int64_t cb) __attribute__((always_inline)) {
+  uint32_t wv[kGUnroll][kGWords], sv[kGUnroll], hv[kGUnroll];
 #pragma unroll
-    for (int u = 0; u < kGUnroll; ++u) {
-      const int64_t e0 = (cb + u) * kChunk + lane * 8;
-      const bool valid = e0 < total;
-      wv[u] = valid ? packed[e0 >> 3] : 0u;
-      sv[u] = valid ? sign[e0 >> 5] : 0u;
-      hv[u] = valid ? scale16[e0 / GS] : 0u;
+  for (int u = 0; u < kGUnroll; ++u) {
+    const int64_t e0 = (wid * kGUnroll + u) * kGChunk + lane * 8 * kGWords;
+    const bool valid = e0 < total;
+    if constexpr (kGWords == 4) {
+      const uint4 v = valid ? *reinterpret_cast<const uint4*>(packed + (e0 >> 3)) : make_uint4(0, 0, 0, 0);
+      wv[u][0] = v.x; wv[u][1] = v.y; wv[u][2] = v.z; wv[u][3] = v.w;
+    } else if constexpr (kGWords == 2) {
+      const uint2 v = valid ? *reinterpret_cast<const uint2*>(packed + (e0 >> 3)) : make_uint2(0, 0);
+      wv[u][0] = v.x; wv[u][1] = v.y;
+    } else {
+      wv[u][0] = valid ? packed[e0 >> 3] : 0u;
     }
-  };
-  int64_t cb = wid * kGUnroll;
-  if (cb < nchunks) load(cb);
-  build_mant_table(lv, s_mt);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the table is written
-  __builtin_amdgcn_s_barrier();
-
-  for (; cb < nchunks; cb += step) {
-    uint32_t o[kGUnroll][4];
+    sv[u] = valid ? sign[e0 >> 5] >> (kGWords == 4 ? 0 : 8 * ((e0 >> 3) & 3)) : 0u;
+    hv[u] = valid ? scale16[e0 / GS] : 0u;
+  }
 #pragma unroll
-    for (int u = 0; u < kGUnroll; ++u)
-      decode_word_ordered(wv[u], sv[u] >> (8 * (lane & 3)), group_lut(s_mt, hv[u]), o[u]);
-    const int64_t c0 = cb;
-    if (cb + step < nchunks) load(cb + step);  // the next batch goes out before the stores
+  for (int u = 0; u < kGUnroll; ++u) {
+    const int64_t e0 = (wid * kGUnroll + u) * kGChunk + lane * 8 * kGWords;
+    if (e0 < total) {
+      const RowLut t = make_row_lut(lv, f16_value(hv[u]));
 #pragma unroll
-    for (int u = 0; u < kGUnroll; ++u) {
-      const int64_t e0 = (c0 + u) * kChunk + lane * 8;
-      if (e0 < total)
-        *reinterpret_cast<uint4*>(out + e0) = make_uint4(o[u][0], o[u][1], o[u][2], o[u][3]);
+      for (int j = 0; j < kGWords; ++j) {
+        uint32_t o[4];
+        decode_word_ordered(wv[u][j], sv[u] >> (8 * j), t, o);
+        *reinterpret_cast<uint4*>(out + e0 + 8 * j) = make_uint4(o[0], o[1], o[2], o[3]);
+      }
     }
   }
 }
@@ -117,20 +114,8 @@ __global__ __launch_bounds__(kGThreads) void dequantize_grouped_rows(
 template <int GS>
 hipError_t launch_grouped(const uint32_t* packed, const uint32_t* sign, const uint16_t* scale16,
                           int64_t total, const Levels& lv, uint16_t* out, hipStream_t stream) {
-  static const int per_cu = [] {
-    int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, dequantize_grouped_rows<GS>, kGThreads,
-                                                     0) != hipSuccess || b < 1)
-      b = 1;
-    return b;
-  }();
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 1;
-  const int64_t batches = (total + (int64_t)kChunk * kGUnroll - 1) / ((int64_t)kChunk * kGUnroll);
-  const int64_t blocks = std::min<int64_t>((int64_t)per_cu * cus,
-                                           (batches + kGThreads / kWave - 1) / (kGThreads / kWave));
+  const int64_t per_block = (int64_t)kGChunk * kGUnroll * (kGThreads / kWave);
+  const int64_t blocks = (total + per_block - 1) / per_block;
   hipLaunchKernelGGL((dequantize_grouped_rows<GS>), dim3((unsigned)blocks), dim3(kGThreads), 0,
                      stream, packed, sign, scale16, total, lv, out);
   return hipGetLastError();

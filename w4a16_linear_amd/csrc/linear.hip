@@ -672,7 +672,10 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
         read_a(s_a + (stage ^ 1) * kAStage, 0, a_buf[nxt]);
         read_w(kt + 1, pw, sw);  // this step's words are dead after sub-step 2
         if constexpr (GS > 0) {
-          lut = group_lut(s_mt, h_next);  // the table of step kt + 1
+          // the table of step kt + 1, when it starts a new group (every step
+          // for groups of 32 and 64: the two halves of a step differ or the
+          // group is one step long)
+          if (GS <= kTK || ((kt + 1) * kTK) % GS == 0) lut = group_lut(s_mt, h_next);
           h_next = h_load;
         }
         dequant_b(kt + 1, 0, pw, sw, b_buf[nxt]);
