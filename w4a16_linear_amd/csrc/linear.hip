@@ -637,7 +637,7 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
   uint4 pw;        // codes of the current step (read at the previous step's sub-step 3)
   uint32_t sw;
   uint4 xa[XCH];
-  bf16x8_t a_buf[2][8], b_buf[2];
+  bf16x8_t a_frag[8], b_buf[2];  // one x fragment set: its registers keep the kernel clear of scratch
   if (nsteps > 0) {
     uint32_t h0 = 0u;
     if constexpr (GS > 0) {
@@ -654,7 +654,7 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
     __syncthreads();
     if constexpr (GS > 0) lut = group_lut(s_mt, h0);
     read_w(0, pw, sw);
-    read_a(s_a, 0, a_buf[0]);
+    read_a(s_a, 0, a_frag);
     dequant_b(0, 0, pw, sw, b_buf[0]);
   }
 
@@ -664,12 +664,17 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
+      // The next sub-step's x fragments are read once this one's MFMAs are
+      // issued; the other wave on the SIMD covers the LDS latency.
+#pragma unroll
+      for (int mi = 0; mi < 8; ++mi)
+        acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag[mi], b_buf[cur], acc[mi], 0, 0, 0);
       if (s < 3) {
-        read_a(sa, s + 1, a_buf[nxt]);
+        read_a(sa, s + 1, a_frag);
         dequant_b(kt, s + 1, pw, sw, b_buf[nxt]);
       } else {
         __syncthreads();
-        read_a(s_a + (stage ^ 1) * kAStage, 0, a_buf[nxt]);
+        read_a(s_a + (stage ^ 1) * kAStage, 0, a_frag);
         read_w(kt + 1, pw, sw);  // this step's words are dead after sub-step 2
         if constexpr (GS > 0) {
           // the table of step kt + 1, when it starts a new group (every step
@@ -680,9 +685,6 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
         }
         dequant_b(kt + 1, 0, pw, sw, b_buf[nxt]);
       }
-#pragma unroll
-      for (int mi = 0; mi < 8; ++mi)
-        acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_buf[cur][mi], b_buf[cur], acc[mi], 0, 0, 0);
       if (s == 0) {
         if constexpr (GS > 0) h_load = load_h(kt + 2);
         store_a(stage ^ 1, xa);
