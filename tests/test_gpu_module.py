@@ -119,3 +119,31 @@ def test_shared_layer_save_load(gpu_lib, tmp_path):
     assert skel[0] is skel[2] and isinstance(skel[0], OPQLinear)
     x = torch.from_numpy(WL.normal(7400, (5, 64))).to(DEV)
     assert torch.equal(model(x), skel(x))
+
+
+@pytest.mark.parametrize("gs", [32, 128])
+def test_grouped_layers_match_oracle_and_reload(gpu_lib, gs, tmp_path):
+    model = _stack(torch.bfloat16, 7500)
+    ws = {name: (mod.weight.detach().float().cpu().numpy(), mod.bias)
+          for name, mod in model.named_modules() if isinstance(mod, nn.Linear)}
+    assert replace_with_opq(model, alpha=0.73, group_size=gs) == ["0", "2", "4"]
+    seen = {}
+    for name, mod in model.named_modules():
+        if isinstance(mod, OPQLinear):
+            mod.register_forward_hook(lambda m, i, o, nm=name: seen.__setitem__(nm, (i[0], o)))
+    x = torch.from_numpy(WL.normal(7501, (3, 30, 256))).to(DEV, torch.bfloat16)
+    y0 = model(x)
+    for name, (w, bias) in ws.items():
+        layer = model.get_submodule(name)
+        ref = O.quantize_grouped(w, 0.73, gs)
+        assert np.array_equal(layer.packed.cpu().numpy().view(np.uint32), ref[0])
+        assert np.array_equal(layer.mx.cpu().numpy().view(np.uint16), ref[2].view(np.uint16))
+        d_ref = O.dequantize_grouped(*ref, 0.73, gs)
+        assert np.array_equal(bf16_bits(layer.dequantized_weight().cpu()), d_ref)
+        _check_layer_output(*seen[name], d_ref, bias)
+    path = str(tmp_path / "grouped.safetensors")
+    save_opq(model, path)
+    fresh = _stack(torch.bfloat16, 1)
+    load_opq(fresh, path)
+    assert fresh[0].group_size == gs
+    assert torch.equal(y0.view(torch.int16), fresh(x).view(torch.int16))

@@ -111,7 +111,7 @@ def test_file_is_plain_tensors_with_a_json_header(tmp_path):
     with safe_open(path, framework="pt") as f:
         meta = json.loads(f.metadata()["opq"])
         assert meta["format"] == FORMAT and meta["bits"] == 4
-        assert meta["layers"]["0"] == {"in": 64, "out": 16, "alpha": 1.0, "bias": True}
+        assert meta["layers"]["0"] == {"in": 64, "out": 16, "alpha": 1.0, "bias": True, "group": 0}
         assert sorted(f.keys()) == ["0.bias", "0.mx", "0.packed", "0.sign_packed"]
 
 
@@ -128,3 +128,31 @@ def test_load_checks_shapes_and_format(tmp_path):
     save_file({"x": torch.zeros(2)}, other)
     with pytest.raises(ValueError, match="format"):
         load_opq(nn.Sequential(nn.Linear(64, 16)), other)
+
+
+def test_grouped_layer_buffers_and_round_trip(tmp_path):
+    m = OPQLinear(256, 24, bias=False, alpha=0.73, group_size=64)
+    assert m.mx.shape == (24, 4) and m.mx.dtype == torch.float16
+    assert "group_size=64" in repr(m)
+    g = torch.Generator().manual_seed(5)
+    m.packed.copy_(torch.randint(-2**31, 2**31 - 1, m.packed.shape, dtype=torch.int32, generator=g))
+    m.mx.copy_(torch.rand(m.mx.shape, generator=g).half())
+    path = str(tmp_path / "g.safetensors")
+    save_opq(nn.Sequential(m), path)
+    dst = nn.Sequential(nn.Linear(256, 24, bias=False))
+    load_opq(dst, path)
+    assert dst[0].group_size == 64 and dst[0].mx.dtype == torch.float16
+    assert torch.equal(dst[0].mx, m.mx) and torch.equal(dst[0].packed, m.packed)
+
+
+@pytest.mark.parametrize("gs", [16, 48, 512])
+def test_group_size_checks(gs):
+    with pytest.raises(ValueError):
+        OPQLinear(512, 8, group_size=gs)
+    with pytest.raises(ValueError):
+        replace_with_opq(nn.Sequential(nn.Linear(512, 8)), group_size=gs)
+
+
+def test_grouped_replace_skips_layers_the_group_does_not_tile():
+    model = nn.Sequential(nn.Linear(96, 8))      # 96 is no multiple of 64
+    assert replace_with_opq(model, group_size=64) == []

@@ -7,8 +7,9 @@ converts a loaded model in place with ``replace_with_opq(model, bits=4,
 alpha=0.73)``; "从量化权重加载的流程说明" rebuilds the ``OPQLinear`` structure
 over a model skeleton and then overwrites its ``packed`` / ``sign_packed`` /
 ``mx`` buffers from saved files.  The buffers here keep those names.  ``mx``
-is the per-output-row float32 max (the card stores a float16 max per group of
-128; this library keeps one exact max per row).
+is either one float32 max per output row, or (``group_size`` set) the card's
+own form: one float16 max per group of ``group_size`` weights along the input
+dimension ("技术细节 / 存储格式").
 
 Every step runs in libopq's kernels: a layer whose buffers are not on the GPU
 raises instead of computing anywhere else.  Saved files are safetensors (plain
@@ -25,7 +26,7 @@ from torch import nn
 
 from . import opq
 
-FORMAT = "opq-int4-rowmax-f32/1"
+FORMAT = "opq-int4/1"
 _META_KEY = "opq"
 
 
@@ -40,24 +41,35 @@ def _f32(alpha: float) -> float:
 class OPQLinear(nn.Module):
     """y = x W'^T (+ bias) with W' held as OPQ codes: 4-bit magnitudes
     (``packed`` [out, in/8] int32), a sign plane (``sign_packed`` [out, in/32]
-    int32) and one float32 max per output row (``mx`` [out]).  The bias, when
-    present, is float32.  x may be bfloat16 or float32 (it is rounded to
-    bfloat16, the layer's activation type); y has x's dtype."""
+    int32) and the maxima ``mx``: float32 [out] (one per output row), or
+    float16 [out, in/group_size] with ``group_size`` in 32, 64, 128, 256.  The
+    bias, when present, is float32.  x may be bfloat16 or float32 (it is
+    rounded to bfloat16, the layer's activation type); y has x's dtype."""
 
     def __init__(self, in_features: int, out_features: int, bias: bool = True,
-                 alpha: float = 0.73, device=None):
+                 alpha: float = 0.73, device=None, group_size: Optional[int] = None):
         super().__init__()
         if in_features <= 0 or in_features % 32:
             raise ValueError(f"in_features must be a positive multiple of 32, got {in_features}")
         if out_features <= 0:
             raise ValueError(f"out_features must be positive, got {out_features}")
+        if group_size is not None and (group_size not in (32, 64, 128, 256) or
+                                       in_features % group_size):
+            raise ValueError(f"group_size must be 32, 64, 128 or 256 and divide in_features="
+                             f"{in_features}, got {group_size}")
         self.in_features = int(in_features)
         self.out_features = int(out_features)
         self.alpha = _f32(alpha)
+        self.group_size = group_size
         kw = dict(dtype=torch.int32, device=device)
         self.register_buffer("packed", torch.zeros((out_features, in_features // 8), **kw))
         self.register_buffer("sign_packed", torch.zeros((out_features, in_features // 32), **kw))
-        self.register_buffer("mx", torch.zeros((out_features,), dtype=torch.float32, device=device))
+        if group_size:
+            self.register_buffer("mx", torch.zeros((out_features, in_features // group_size),
+                                                   dtype=torch.float16, device=device))
+        else:
+            self.register_buffer("mx", torch.zeros((out_features,), dtype=torch.float32,
+                                                   device=device))
         if bias:
             self.register_buffer("bias", torch.zeros((out_features,), dtype=torch.float32,
                                                      device=device))
@@ -67,7 +79,8 @@ class OPQLinear(nn.Module):
     # -- conversion ---------------------------------------------------------
 
     @classmethod
-    def from_linear(cls, lin: nn.Linear, alpha: float = 0.73) -> "OPQLinear":
+    def from_linear(cls, lin: nn.Linear, alpha: float = 0.73,
+                    group_size: Optional[int] = None) -> "OPQLinear":
         """Quantize an nn.Linear whose weight is on the GPU (float32 or bfloat16)."""
         w = lin.weight.detach()
         if not w.is_cuda:
@@ -76,13 +89,18 @@ class OPQLinear(nn.Module):
         if w.dtype not in (torch.float32, torch.bfloat16):
             w = w.float()
         out = cls(lin.in_features, lin.out_features, bias=lin.bias is not None, alpha=alpha,
-                  device=w.device)
-        opq.quantize(w.contiguous(), out.alpha, out=out.qweight())
+                  device=w.device, group_size=group_size)
+        if group_size:
+            opq.quantize_grouped(w.contiguous(), out.alpha, group_size, out=out.qweight())
+        else:
+            opq.quantize(w.contiguous(), out.alpha, out=out.qweight())
         if lin.bias is not None:
             out.bias.copy_(lin.bias.detach().float())
         return out
 
-    def qweight(self) -> opq.QuantizedWeight:
+    def qweight(self):
+        if self.group_size:
+            return opq.GroupedWeight(self.packed, self.sign_packed, self.mx, self.group_size)
         return opq.QuantizedWeight(self.packed, self.sign_packed, self.mx)
 
     def dequantized_weight(self) -> torch.Tensor:
@@ -103,12 +121,13 @@ class OPQLinear(nn.Module):
 
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
-                f"bias={self.bias is not None}, alpha={self.alpha:.8g}")
+                f"bias={self.bias is not None}, alpha={self.alpha:.8g}, "
+                f"group_size={self.group_size}")
 
 
 # ---------------------------------------------------------------- conversion
 
-def _targets(model: nn.Module, skip: Iterable[str]):
+def _targets(model: nn.Module, skip: Iterable[str], group_size: Optional[int] = None):
     skip = tuple(skip)
     for parent_name, parent in model.named_modules():
         # every slot, also a second one holding a module already seen
@@ -119,22 +138,26 @@ def _targets(model: nn.Module, skip: Iterable[str]):
                 continue
             if any(full == s or full.startswith(s + ".") for s in skip):
                 continue
-            if child.in_features % 32:
-                continue  # packed words hold whole groups of 32 along k
+            if child.in_features % (group_size or 32):
+                continue  # packed words (and groups) must tile the input dimension
             yield full, parent, cname, child
 
 
 def replace_with_opq(model: nn.Module, bits: int = 4, alpha: float = 0.73,
-                     skip: Iterable[str] = ()) -> List[str]:
+                     skip: Iterable[str] = (), group_size: Optional[int] = None) -> List[str]:
     """Swap every nn.Linear of `model` (in place) for an OPQLinear holding its
-    quantized weight; returns the qualified names replaced.  Layers whose
-    in_features is not a multiple of 32, and names under `skip`, stay as they
-    are.  A Linear reached under several names is quantized once and shared.
-    All eligible weights must be on the GPU: nothing is replaced otherwise."""
+    quantized weight; returns the qualified names replaced.  `group_size`
+    None keeps one float32 max per output row; 32, 64, 128 or 256 stores the
+    card's float16 max per group.  Layers whose in_features is not a multiple
+    of 32 (and of the group), and names under `skip`, stay as they are.  A
+    Linear reached under several names is quantized once and shared.  All
+    eligible weights must be on the GPU: nothing is replaced otherwise."""
     if bits != 4:
         raise ValueError(f"only 4-bit codes are built (bits={bits})")
+    if group_size is not None and group_size not in (32, 64, 128, 256):
+        raise ValueError(f"group_size must be 32, 64, 128 or 256, got {group_size}")
     alpha = _f32(alpha)
-    found = list(_targets(model, skip))
+    found = list(_targets(model, skip, group_size))
     for full, _, _, child in found:
         if not child.weight.is_cuda:
             raise ValueError(f"replace_with_opq: {full}.weight is not on the GPU "
@@ -142,7 +165,7 @@ def replace_with_opq(model: nn.Module, bits: int = 4, alpha: float = 0.73,
     made: Dict[int, OPQLinear] = {}
     for _, parent, cname, child in found:
         if id(child) not in made:
-            made[id(child)] = OPQLinear.from_linear(child, alpha)
+            made[id(child)] = OPQLinear.from_linear(child, alpha, group_size)
         setattr(parent, cname, made[id(child)])
     return [full for full, _, _, _ in found]
 
@@ -168,7 +191,7 @@ def save_opq(model: nn.Module, path: str) -> List[str]:
     layers = {}
     for name, mod in _opq_layers(model):
         layers[name] = {"in": mod.in_features, "out": mod.out_features, "alpha": mod.alpha,
-                        "bias": mod.bias is not None}
+                        "bias": mod.bias is not None, "group": mod.group_size or 0}
         for b in ("packed", "sign_packed", "mx") + (("bias",) if mod.bias is not None else ()):
             tensors[f"{name}.{b}"] = getattr(mod, b).detach().to("cpu").contiguous()
     meta = {_META_KEY: json.dumps({"format": FORMAT, "bits": 4, "layers": layers})}
@@ -204,7 +227,7 @@ def load_opq(model: nn.Module, path: str, device=None) -> List[str]:
                                  f"{old.out_features}x{old.in_features} in the model")
             dev = torch.device(device) if device is not None else ref_dev
             new = OPQLinear(info["in"], info["out"], bias=info["bias"], alpha=info["alpha"],
-                            device=dev)
+                            device=dev, group_size=info.get("group") or None)
             for b in ("packed", "sign_packed", "mx") + (("bias",) if info["bias"] else ()):
                 t = f.get_tensor(f"{name}.{b}")
                 dst = getattr(new, b)
