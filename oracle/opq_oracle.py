@@ -53,7 +53,8 @@ __all__ = [
     "encode", "pack", "unpack", "quantize", "reconstruct", "dequantize",
     "linear", "snr_db", "error_sums", "decision_thresholds_f32", "codes_of_u",
     "F16_MAX", "group_absmax_f16", "encode_grouped", "quantize_grouped",
-    "reconstruct_grouped", "dequantize_grouped",
+    "reconstruct_grouped", "dequantize_grouped", "levels_of", "encode_bits", "pack_bits",
+    "unpack_bits", "quantize_bits", "dequantize_bits", "error_sums_bits",
 ]
 
 
@@ -100,13 +101,13 @@ def row_absmax(w32: np.ndarray) -> np.ndarray:
     return np.max(np.abs(w32), axis=1).astype(np.float32)
 
 
-def _nearest_code_exact(u: float, alpha: float) -> int:
-    """round(15 u^alpha) at 200 bits; halves go up."""
+def _nearest_code_exact(u: float, alpha: float, levels: int = LEVELS) -> int:
+    """round(levels u^alpha) at 200 bits; halves go up."""
     with mpmath.workprec(200):
-        v = mpmath.mpf(LEVELS) * mpmath.power(mpmath.mpf(u), mpmath.mpf(alpha))
+        v = mpmath.mpf(levels) * mpmath.power(mpmath.mpf(u), mpmath.mpf(alpha))
         fl = mpmath.floor(v)
         q = int(fl) + (1 if v - fl >= mpmath.mpf(0.5) else 0)
-    return min(max(q, 0), LEVELS)
+    return min(max(q, 0), levels)
 
 
 def encode(w32: np.ndarray, alpha: float):
@@ -128,17 +129,17 @@ def encode(w32: np.ndarray, alpha: float):
     return q, s, m
 
 
-def codes_of_u(u: np.ndarray, alpha: float) -> np.ndarray:
-    """q = round(15 u^alpha) for binary32 u >= 0, halves up, limited to 15
-    (u above 1 only arises against a rounded group max)."""
+def codes_of_u(u: np.ndarray, alpha: float, levels: int = LEVELS) -> np.ndarray:
+    """q = round(levels u^alpha) for binary32 u >= 0, halves up, limited to
+    `levels` (u above 1 only arises against a rounded group max)."""
     a64 = alpha_f32(alpha)
-    v = LEVELS * np.power(u.astype(np.float64), a64)
+    v = levels * np.power(u.astype(np.float64), a64)
     q = np.floor(v + 0.5)
     # Values whose float64 v sits next to a half are settled exactly.
     frac = v - np.floor(v)
     for r, c in np.argwhere(np.abs(frac - 0.5) < 1e-9):
-        q[r, c] = _nearest_code_exact(float(u[r, c]), a64)
-    return np.clip(q, 0, LEVELS).astype(np.uint8)
+        q[r, c] = _nearest_code_exact(float(u[r, c]), a64, levels)
+    return np.clip(q, 0, levels).astype(np.uint8)
 
 
 def pack(q: np.ndarray, s: np.ndarray):
@@ -182,11 +183,13 @@ def quantize(w32: np.ndarray, alpha: float):
 
 # ---------------------------------------------------------------- dequantizer
 
-def reconstruct(q: np.ndarray, s: np.ndarray, scale: np.ndarray, alpha: float) -> np.ndarray:
-    """w' = sign (q/15)^(1/alpha) m in float64 (section "推理解码"); q = 0 gives +0."""
+def reconstruct(q: np.ndarray, s: np.ndarray, scale: np.ndarray, alpha: float,
+                levels: int = LEVELS) -> np.ndarray:
+    """w' = sign (q/15)^(1/alpha) m in float64 (section "推理解码"); q = 0 gives +0.
+    `levels` replaces 15 for other code widths."""
     a64 = alpha_f32(alpha)
     q64 = np.asarray(q, dtype=np.float64)
-    mag = np.power(q64 / LEVELS, 1.0 / a64) * np.asarray(scale, np.float64)[:, None]
+    mag = np.power(q64 / levels, 1.0 / a64) * np.asarray(scale, np.float64)[:, None]
     neg = (np.asarray(s) != 0) & (np.asarray(q) != 0)
     return np.where(neg, -mag, mag)
 
@@ -259,6 +262,92 @@ def dequantize_grouped(packed, sign, m16, alpha: float, gs: int) -> np.ndarray:
     return f64_to_bf16_bits(reconstruct_grouped(q, s, m16, alpha, gs))
 
 
+# ---------------------------------------------------------------- other code widths
+#
+# The card's configuration offers 3, 4, 5 or 6 bits ("OPQ_BITS"); its formulas
+# are written for 4 (x 15, 16 levels).  Reading: b bits give 2^b - 1 in place
+# of 15 everywhere (q = round((2^b - 1) u^alpha), w' = (q / (2^b - 1))^(1/alpha)
+# m); the sign plane and the per-row max are unchanged.  The card gives no
+# packing for b != 4; here the codes of a row form a little-endian bit stream
+# along K, code k in bits b k .. b k + b - 1, so 32 codes fill b uint32 words
+# (for b = 4 that is the nibble packing above).
+
+def levels_of(bits: int) -> int:
+    """Largest code of a b-bit magnitude: 2^b - 1 (15 for 4 bits)."""
+    assert bits in (3, 4, 5, 6)
+    return (1 << bits) - 1
+
+
+def encode_bits(w32: np.ndarray, alpha: float, bits: int):
+    """(q uint8 [N,K], s uint8 [N,K], scale float32 [N]) with b-bit codes."""
+    w32 = np.ascontiguousarray(w32, dtype=np.float32)
+    m = row_absmax(w32)
+    absw = np.abs(w32)
+    u = np.zeros_like(absw)
+    live = m > 0
+    with np.errstate(divide="ignore", invalid="ignore"):
+        u[live] = absw[live] / m[live, None]          # IEEE binary32 quotient
+    q = codes_of_u(u, alpha, levels_of(bits))
+    s = (w32 < 0).astype(np.uint8)
+    return q, s, m
+
+
+def pack_bits(q: np.ndarray, bits: int) -> np.ndarray:
+    """Codes [N, K] as a bit stream per row: uint32 [N, K*bits/32]."""
+    q = np.asarray(q, dtype=np.uint64)
+    n, k = q.shape
+    assert k % 32 == 0
+    out = np.zeros((n, k * bits // 32), np.uint64)
+    for i in range(k):
+        pos = bits * i
+        w, off = pos // 32, pos % 32
+        out[:, w] |= (q[:, i] << np.uint64(off)) & np.uint64(0xFFFFFFFF)
+        if off + bits > 32:
+            out[:, w + 1] |= q[:, i] >> np.uint64(32 - off)
+    return out.astype(np.uint32)
+
+
+def unpack_bits(packed: np.ndarray, bits: int, k: int) -> np.ndarray:
+    """Inverse of :func:`pack_bits`: codes uint8 [N, K]."""
+    p = np.asarray(packed, dtype=np.uint64)
+    n = p.shape[0]
+    q = np.zeros((n, k), np.uint8)
+    mask = np.uint64((1 << bits) - 1)
+    for i in range(k):
+        pos = bits * i
+        w, off = pos // 32, pos % 32
+        v = p[:, w] >> np.uint64(off)
+        if off + bits > 32:
+            v |= p[:, w + 1] << np.uint64(32 - off)
+        q[:, i] = (v & mask).astype(np.uint8)
+    return q
+
+
+def quantize_bits(w32: np.ndarray, alpha: float, bits: int):
+    """(packed [N, K*bits/32], sign [N, K/32], scale [N]) with b-bit codes."""
+    q, s, m = encode_bits(w32, alpha, bits)
+    _, sign = pack(np.zeros_like(q), s)
+    return pack_bits(q, bits), sign, m
+
+
+def dequantize_bits(packed, sign, scale, alpha: float, bits: int) -> np.ndarray:
+    """bfloat16 bit patterns [N, K] of the b-bit stored form, rounded once."""
+    k = np.asarray(sign).shape[1] * SIGNS_PER_WORD
+    q = unpack_bits(packed, bits, k)
+    _, s = unpack(np.zeros((q.shape[0], k // CODES_PER_WORD), np.uint32), sign)
+    return f64_to_bf16_bits(reconstruct(q, s, scale, alpha, levels_of(bits)))
+
+
+def error_sums_bits(w32: np.ndarray, alpha: float, bits: int) -> np.ndarray:
+    """Per row: (sum w^2, sum (w - w')^2) in float64 for b-bit codes."""
+    w32 = np.ascontiguousarray(w32, dtype=np.float32)
+    packed, sign, scale = quantize_bits(w32, alpha, bits)
+    w_rec = bf16_bits_to_f32(dequantize_bits(packed, sign, scale, alpha, bits)).astype(np.float64)
+    w64 = w32.astype(np.float64)
+    e = w64 - w_rec
+    return np.stack([np.sum(w64 * w64, axis=1), np.sum(e * e, axis=1)], axis=1)
+
+
 # ---------------------------------------------------------------- linear layer
 
 def linear(x_bf16: np.ndarray, wdq_bf16: np.ndarray, bias=None) -> np.ndarray:
@@ -300,8 +389,9 @@ def snr_db(w: np.ndarray, w_rec: np.ndarray) -> float:
 
 # ---------------------------------------------------------------- decision points
 
-def decision_thresholds_f32(alpha: float) -> np.ndarray:
-    """T_k = the smallest binary32 t with 15 t^alpha >= k - 1/2, k = 1..15.
+def decision_thresholds_f32(alpha: float, levels: int = LEVELS) -> np.ndarray:
+    """T_k = the smallest binary32 t with 15 t^alpha >= k - 1/2, k = 1..15
+    (`levels` in place of 15 for other code widths).
 
     For binary32 u in [0, 1], round(15 u^alpha) (halves up) equals the number
     of k with u >= T_k.  Computed with mpmath at 200 bits: the real boundary
@@ -309,16 +399,16 @@ def decision_thresholds_f32(alpha: float) -> np.ndarray:
     ulp until the condition holds at T_k and fails one ulp below.
     """
     a = alpha_f32(alpha)
-    out = np.zeros(LEVELS, np.float32)
+    out = np.zeros(levels, np.float32)
     with mpmath.workprec(200):
         A = mpmath.mpf(a)
 
         def ok(t: np.float32, k: int) -> bool:
-            v = LEVELS * mpmath.power(mpmath.mpf(float(t)), A)
+            v = levels * mpmath.power(mpmath.mpf(float(t)), A)
             return v >= k - mpmath.mpf(0.5)
 
-        for k in range(1, LEVELS + 1):
-            b = mpmath.power(mpmath.mpf(2 * k - 1) / 30, 1 / A)
+        for k in range(1, levels + 1):
+            b = mpmath.power(mpmath.mpf(2 * k - 1) / (2 * levels), 1 / A)
             t = np.float32(float(b))
             while not ok(t, k):
                 t = np.nextafter(t, np.float32(np.inf))

@@ -28,11 +28,11 @@ MUTATIONS = {
     # sign from the sign bit (-0.0 would give 1)
     "sign_bit": ("s = (w32 < 0).astype(np.uint8)", "s = (np.signbit(w32)).astype(np.uint8)"),
     # 14 levels instead of 15
-    "levels14": ("v = LEVELS * np.power", "v = 14 * np.power"),
+    "levels14": ("v = levels * np.power", "v = (levels - 1) * np.power"),
     # nibbles packed big-endian
     "pack_order": ("<< np.uint32(4 * i)", "<< np.uint32(28 - 4 * i)"),
     # reconstruction with alpha instead of 1/alpha
-    "deq_alpha": ("np.power(q64 / LEVELS, 1.0 / a64)", "np.power(q64 / LEVELS, a64)"),
+    "deq_alpha": ("np.power(q64 / levels, 1.0 / a64)", "np.power(q64 / levels, a64)"),
     # reconstruction rounded twice (through float32)
     "deq_double_round": ("return f64_to_bf16_bits(reconstruct(q, s, scale, alpha))",
                          "return f64_to_bf16_bits(reconstruct(q, s, scale, alpha)"
@@ -71,6 +71,11 @@ MUTATIONS = {
     # group scales spread over K in the wrong order when reconstructing
     "group_deq_tile": ("scale = np.repeat(np.asarray(m16, np.float16).astype(np.float64), gs, axis=1)",
                        "scale = np.tile(np.asarray(m16, np.float16).astype(np.float64), (1, gs))"),
+    # bit stream words in the wrong order
+    "bits_word_order": ("out[:, w] |= (q[:, i] << np.uint64(off)) & np.uint64(0xFFFFFFFF)",
+                        "out[:, -1 - w] |= (q[:, i] << np.uint64(off)) & np.uint64(0xFFFFFFFF)"),
+    # 2^b levels instead of 2^b - 1
+    "bits_levels": ("return (1 << bits) - 1", "return (1 << bits) - 1 + (bits != 4)"),
 }
 
 

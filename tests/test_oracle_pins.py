@@ -608,3 +608,87 @@ def test_group_quantize_dequantize_idempotent(gs):
     pk2, sg2, m2 = O.quantize_grouped(w1, 0.73, gs)
     assert np.array_equal(pk2, pk) and np.array_equal(m2, m16)
     assert np.array_equal(O.dequantize_grouped(pk2, sg2, m2, 0.73, gs), d1)
+
+
+# ------------------------------------------------------------------ other code widths
+#
+# The configuration section offers 3, 4, 5 or 6 bits; 2^b - 1 takes the place
+# of 15.  The packing for b != 4 is this build's (a little-endian bit stream).
+
+def test_bits4_is_the_nibble_form():
+    w = _to_bf16_values(_rand_rows(50, 5, 256))
+    for alpha in (0.45, 0.73):
+        pb, sb, mb = O.quantize_bits(w, alpha, 4)
+        p, s, m = O.quantize(w, alpha)
+        assert np.array_equal(pb, p) and np.array_equal(sb, s) and np.array_equal(mb, m)
+        assert np.array_equal(O.dequantize_bits(pb, sb, mb, alpha, 4), O.dequantize(p, s, m, alpha))
+
+
+@pytest.mark.parametrize("bits", [3, 4, 5, 6])
+def test_bit_stream_packing_by_big_integers(bits):
+    """Each row's codes as one Python integer, sum q_i 2^(b i), cut into
+    32-bit words from the bottom."""
+    rng = np.random.default_rng(51 + bits)
+    k = 96
+    q = rng.integers(0, 1 << bits, (3, k)).astype(np.uint8)
+    got = O.pack_bits(q, bits)
+    assert got.shape == (3, k * bits // 32)
+    for r in range(3):
+        big = sum(int(q[r, i]) << (bits * i) for i in range(k))
+        want = [(big >> (32 * j)) & 0xFFFFFFFF for j in range(k * bits // 32)]
+        assert got[r].tolist() == want
+    assert np.array_equal(O.unpack_bits(got, bits, k), q)
+
+
+@pytest.mark.parametrize("bits", [3, 5, 6])
+def test_bits_alpha_one_is_uniform_rounding(bits):
+    """alpha = 1: q = rint((2^b - 1) u), exact in float64."""
+    L = (1 << bits) - 1
+    w = _rand_rows(52, 6, 64)
+    w[0, 3] = np.float32(0.5) * np.abs(w[0]).max()   # u = 1/2: (2^b - 1)/2 is a half -> up
+    q, s, m = O.encode_bits(w, 1.0, bits)
+    assert np.array_equal(q, _codes_closed_form(w, lambda u: int(np.floor(L * float(u) + 0.5))))
+    assert q[0, 3] == (L + 1) // 2
+    assert np.array_equal(m, np.max(np.abs(w), axis=1))
+    assert np.array_equal(s, (w < 0).astype(np.uint8))
+
+
+@pytest.mark.parametrize("bits", [3, 5, 6])
+def test_bits_half_alpha_exact_rational_codes(bits):
+    """alpha = 1/2: L sqrt(u) >= k - 1/2  <=>  4 L^2 u >= (2k - 1)^2."""
+    L = (1 << bits) - 1
+    w = _rand_rows(53, 5, 64)
+    q, _, _ = O.encode_bits(w, 0.5, bits)
+    rule = lambda u: sum(1 for kk in range(1, L + 1) if 4 * L * L * u >= (2 * kk - 1) ** 2)
+    assert np.array_equal(q, _codes_closed_form(w, rule))
+
+
+@pytest.mark.parametrize("bits", [3, 5, 6])
+@pytest.mark.parametrize("alpha,level", [(1.0, lambda q, L: Fraction(q, L)),
+                                         (0.5, lambda q, L: Fraction(q, L) ** 2)])
+def test_bits_dequant_exact_rational(bits, alpha, level):
+    L = (1 << bits) - 1
+    w = _to_bf16_values(_rand_rows(54, 4, 64))
+    p, sg, m = O.quantize_bits(w, alpha, bits)
+    got = O.dequantize_bits(p, sg, m, alpha, bits)
+    q = O.unpack_bits(p, bits, 64)
+    _, s = O.unpack(np.zeros((4, 8), np.uint32), sg)
+    for r in range(4):
+        for c in range(64):
+            v = level(int(q[r, c]), L) * Fraction(float(m[r]))
+            if s[r, c] and q[r, c]:
+                v = -v
+            assert got[r, c] == bf16_bits_of(v), (r, c)
+
+
+@pytest.mark.parametrize("bits", [3, 6])
+def test_bits_error_sums_zero_on_reconstructions(bits):
+    w = _to_bf16_values(_rand_rows(55, 4, 128))
+    p, s, m = O.quantize_bits(w, 0.73, bits)
+    w1 = O.bf16_bits_to_f32(O.dequantize_bits(p, s, m, 0.73, bits))
+    sums = O.error_sums_bits(w1, 0.73, bits)
+    assert np.all(sums[:, 1] == 0.0)
+    assert np.allclose(sums[:, 0], np.sum(w1.astype(np.float64) ** 2, axis=1), rtol=0, atol=0)
+    # more bits, smaller error (same weights)
+    e = [O.error_sums_bits(w, 0.73, b)[:, 1].sum() for b in (3, 4, 5, 6)]
+    assert e[0] > e[1] > e[2] > e[3] > 0
