@@ -58,7 +58,7 @@
 extern "C" {
 #endif
 
-#define OPQ_ABI_VERSION 3
+#define OPQ_ABI_VERSION 4
 
 typedef enum {
   OPQ_OK = 0,
@@ -177,6 +177,50 @@ int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
                float alpha, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
                void* stream);
+
+/*
+ * Other code widths.  The configuration section of the card offers 3, 4, 5 or
+ * 6 bits ("OPQ_BITS"); its formulas are written for 4 (x 15).  Here b bits
+ * use 2^b - 1 in place of 15 everywhere: q = the integer nearest to
+ * (2^b - 1) u^alpha (halves up), reconstruction bf16(G_q m) with
+ * G_q = (q / (2^b - 1))^(1/alpha).  The sign plane and the per-row float32
+ * scale are as for 4 bits.  The card gives no packing for b != 4; here the
+ * codes of a row form a little-endian bit stream along k: code k occupies bits
+ * b*k .. b*k + b - 1 of the row, so 32 codes fill b uint32 words and packed is
+ * [n][k*b/32].  For b = 4 this is exactly the layout of opq_quantize, and
+ * these calls give the same results as the 4-bit ones.
+ *   bits     3, 4, 5 or 6 (OPQ_ERR_SHAPE otherwise)
+ * The linear layer runs on 4-bit codes only (the W4A16 path); the other
+ * widths are a storage format and an accuracy study (opq_error_sums_bits).
+ */
+
+/*
+ * Quantize with b-bit codes: w device [n][k] float32 or bfloat16; packed
+ * [n][k*bits/32], sign [n][k/32], scale [n] device outputs.  For bits != 4,
+ * k <= 16384 and alpha must have a separating bucket grid (every alpha in
+ * [0.1, 10] has one for 6 bits); otherwise OPQ_ERR_UNSUPPORTED.  Errors:
+ * OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN, OPQ_ERR_DTYPE,
+ * OPQ_ERR_UNSUPPORTED, OPQ_ERR_HIP.
+ */
+int opq_quantize_bits(const void* w, int w_dtype, int64_t n, int64_t k, int bits, float alpha,
+                      uint32_t* packed, uint32_t* sign, float* scale, void* stream);
+
+/*
+ * Dequantize b-bit codes to w_out device [n][k] bfloat16.  k <= 65536.
+ * Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN,
+ * OPQ_ERR_UNSUPPORTED, OPQ_ERR_HIP.
+ */
+int opq_dequantize_bits(const uint32_t* packed, const uint32_t* sign, const float* scale,
+                        int64_t n, int64_t k, int bits, float alpha, uint16_t* w_out,
+                        void* stream);
+
+/*
+ * opq_error_sums with b-bit codes (the same row_sums layout and precision):
+ * the reconstruction error per bit width, nothing stored.  Same limits as
+ * opq_quantize_bits (for bits = 4, those of opq_error_sums).
+ */
+int opq_error_sums_bits(const void* w, int w_dtype, int64_t n, int64_t k, int bits, float alpha,
+                        double* row_sums, void* stream);
 
 /*
  * Group-wise stored form: the card's own ("技术细节 / 存储格式": one float16

@@ -33,14 +33,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 15
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(opq._SIGNATURES)
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.opq_abi_version() == opq.ABI_VERSION == 3
+    assert lib.opq_abi_version() == opq.ABI_VERSION == 4
     for s in range(9):
         assert opq.status_str(s) and opq.status_str(s) != "unknown status"
     assert opq.status_str(99) == "unknown status"
@@ -143,6 +143,34 @@ def test_linear_argument_checks(lib):
     assert call(n=0) == OK
     assert call(m=0, yd=1) == OK
     assert lib.opq_linear_workspace_bytes(8, 16, 64) == opq.linear_workspace_bytes(8, 16, 64)
+
+
+def test_bits_argument_checks(lib):
+    q = lib.opq_quantize_bits
+    assert q(None, 1, 4, 64, 3, 0.73, FAKE, FAKE, FAKE, None) == NULL
+    for b in (0, 1, 2, 7, 8, -4):
+        assert q(FAKE, 1, 4, 64, b, 0.73, FAKE, FAKE, FAKE, None) == SHAPE, b
+    assert q(FAKE, 1, 4, 48, 5, 0.73, FAKE, FAKE, FAKE, None) == SHAPE
+    assert q(FAKE, 1, 4, 64, 6, 0.0, FAKE, FAKE, FAKE, None) == ALPHA
+    assert q(FAKE, 1, 4, 64, 6, 0.73, MISALIGNED, FAKE, FAKE, None) == ALIGN
+    assert q(FAKE, 4, 4, 64, 6, 0.73, FAKE, FAKE, FAKE, None) == DTYPE
+    assert q(FAKE, 1, 4, 16384 + 32, 6, 0.73, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert q(FAKE, 1, 4, 64, 6, 100.0, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    assert q(FAKE, 1, 0, 64, 3, 0.73, FAKE, FAKE, FAKE, None) == OK
+    # bits = 4 is opq_quantize itself (same checks, its own k limit)
+    assert q(FAKE, 1, 4, 65536 + 32, 4, 0.73, FAKE, FAKE, FAKE, None) == UNSUPPORTED
+    d = lib.opq_dequantize_bits
+    assert d(FAKE, None, FAKE, 4, 64, 5, 0.73, FAKE, None) == NULL
+    assert d(FAKE, FAKE, FAKE, 4, 64, 9, 0.73, FAKE, None) == SHAPE
+    assert d(FAKE, FAKE, FAKE, 4, 64, 5, -1.0, FAKE, None) == ALPHA
+    assert d(FAKE, FAKE, FAKE, 4, 64, 5, 0.73, MISALIGNED, None) == ALIGN
+    assert d(FAKE, FAKE, FAKE, 4, 65536 + 32, 5, 0.73, FAKE, None) == UNSUPPORTED
+    assert d(FAKE, FAKE, FAKE, 0, 64, 5, 0.73, FAKE, None) == OK
+    e = lib.opq_error_sums_bits
+    assert e(FAKE, 1, 4, 64, 3, 0.73, None, None) == NULL
+    assert e(FAKE, 1, 4, 64, 2, 0.73, FAKE, None) == SHAPE
+    assert e(FAKE, 1, 4, 16384 + 32, 5, 0.73, FAKE, None) == UNSUPPORTED
+    assert e(FAKE, 1, 0, 64, 6, 0.73, FAKE, None) == OK
 
 
 def test_grouped_argument_checks(lib):

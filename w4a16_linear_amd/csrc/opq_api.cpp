@@ -20,6 +20,19 @@ bool alpha_ok(float a) { return std::isfinite(a) && a > 0.0f; }
 
 bool shape_ok(int64_t n, int64_t k) { return n >= 0 && k >= 0 && k % 32 == 0; }
 
+bool bits_ok(int bits) { return bits >= 3 && bits <= 6; }
+
+// Decision points and levels of b-bit codes (2^b - 1 levels).
+bool bits_tables(float alpha, int bits, opq::DecisionPointsN& dp, opq::LevelsN& lv) {
+  const int L = (1 << bits) - 1;
+  dp.n = lv.n = L;
+  for (int i = L; i < opq::kMaxLevels; ++i) dp.t[i] = 2.0f;
+  for (int i = L + 1; i <= opq::kMaxLevels; ++i) lv.g[i] = 0.0;
+  if (!opq::decision_points_n(alpha, L, dp.t)) return false;
+  opq::levels_n(alpha, L, lv.g);
+  return true;
+}
+
 bool group_ok(int64_t k, int64_t gs) {
   return (gs == 32 || gs == 64 || gs == 128 || gs == 256) && k % gs == 0;
 }
@@ -38,7 +51,7 @@ const char* opq_status_str(int status) {
     case OPQ_ERR_NULL: return "a required pointer is NULL";
     case OPQ_ERR_SHAPE:
       return "bad shape: sizes must be >= 0, k a multiple of 32 (and of the group, which is "
-             "32, 64, 128 or 256)";
+             "32, 64, 128 or 256); bits 3, 4, 5 or 6";
     case OPQ_ERR_ALPHA: return "alpha must be finite and > 0";
     case OPQ_ERR_ALIGN: return "every array must be 16-byte aligned";
     case OPQ_ERR_DTYPE: return "unknown dtype code";
@@ -137,6 +150,62 @@ int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign, 
   return hip_status(opq::launch_linear(x, packed, sign, scale, bias, m, n, k, lv, y,
                                        y_dtype == OPQ_BF16, workspace,
                                        static_cast<hipStream_t>(stream)));
+}
+
+int opq_quantize_bits(const void* w, int w_dtype, int64_t n, int64_t k, int bits, float alpha,
+                      uint32_t* packed, uint32_t* sign, float* scale, void* stream) {
+  if (bits == 4) return opq_quantize(w, w_dtype, n, k, alpha, packed, sign, scale, stream);
+  const bool nk = n > 0 && k > 0;
+  if ((nk && (!w || !packed || !sign)) || (n > 0 && !scale)) return OPQ_ERR_NULL;
+  if (!shape_ok(n, k) || !bits_ok(bits)) return OPQ_ERR_SHAPE;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  if (!aligned16(w) || !aligned16(packed) || !aligned16(sign) || !aligned16(scale))
+    return OPQ_ERR_ALIGN;
+  if (w_dtype != OPQ_F32 && w_dtype != OPQ_BF16) return OPQ_ERR_DTYPE;
+  if (n == 0) return OPQ_OK;
+  opq::DecisionPointsN dp;
+  opq::LevelsN lv;
+  if (!bits_tables(alpha, bits, dp, lv)) return OPQ_ERR_ALPHA;
+  if (!opq::bits_supported(dp, k)) return OPQ_ERR_UNSUPPORTED;
+  return hip_status(opq::launch_quantize_bits(w, w_dtype == OPQ_BF16, n, k, bits, dp, lv, packed,
+                                              sign, scale, nullptr,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int opq_dequantize_bits(const uint32_t* packed, const uint32_t* sign, const float* scale,
+                        int64_t n, int64_t k, int bits, float alpha, uint16_t* w_out,
+                        void* stream) {
+  if (bits == 4) return opq_dequantize(packed, sign, scale, n, k, alpha, w_out, stream);
+  if (n > 0 && k > 0 && (!packed || !sign || !scale || !w_out)) return OPQ_ERR_NULL;
+  if (!shape_ok(n, k) || !bits_ok(bits)) return OPQ_ERR_SHAPE;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  if (!aligned16(packed) || !aligned16(sign) || !aligned16(scale) || !aligned16(w_out))
+    return OPQ_ERR_ALIGN;
+  if (n == 0 || k == 0) return OPQ_OK;
+  if (k > kMaxK) return OPQ_ERR_UNSUPPORTED;
+  opq::DecisionPointsN dp;
+  opq::LevelsN lv;
+  if (!bits_tables(alpha, bits, dp, lv)) return OPQ_ERR_ALPHA;
+  return hip_status(opq::launch_dequantize_bits(packed, sign, scale, n, k, bits, lv, w_out,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int opq_error_sums_bits(const void* w, int w_dtype, int64_t n, int64_t k, int bits, float alpha,
+                        double* row_sums, void* stream) {
+  if (bits == 4) return opq_error_sums(w, w_dtype, n, k, alpha, row_sums, stream);
+  if ((n > 0 && k > 0 && !w) || (n > 0 && !row_sums)) return OPQ_ERR_NULL;
+  if (!shape_ok(n, k) || !bits_ok(bits)) return OPQ_ERR_SHAPE;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  if (!aligned16(w) || !aligned16(row_sums)) return OPQ_ERR_ALIGN;
+  if (w_dtype != OPQ_F32 && w_dtype != OPQ_BF16) return OPQ_ERR_DTYPE;
+  if (n == 0) return OPQ_OK;
+  opq::DecisionPointsN dp;
+  opq::LevelsN lv;
+  if (!bits_tables(alpha, bits, dp, lv)) return OPQ_ERR_ALPHA;
+  if (!opq::bits_supported(dp, k)) return OPQ_ERR_UNSUPPORTED;
+  return hip_status(opq::launch_quantize_bits(w, w_dtype == OPQ_BF16, n, k, bits, dp, lv, nullptr,
+                                              nullptr, nullptr, row_sums,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int opq_quantize_grouped(const void* w, int w_dtype, int64_t n, int64_t k, int64_t group,

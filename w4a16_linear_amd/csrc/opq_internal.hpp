@@ -23,6 +23,19 @@ struct Levels {
 bool decision_points(float alpha, float out[kLevels]);
 void levels(float alpha, double out[kLevels + 1]);
 
+// Other code widths: b bits give L = 2^b - 1 levels (3 <= b <= 6).
+constexpr int kMaxLevels = 63;
+struct DecisionPointsN {
+  float t[kMaxLevels];
+  int n;  // L
+};
+struct LevelsN {
+  double g[kMaxLevels + 1];
+  int n;  // L
+};
+bool decision_points_n(float alpha, int L, float* out);  // out[L]
+void levels_n(float alpha, int L, double* out);          // out[L + 1]
+
 // quantize.hip
 hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, int64_t k,
                            const DecisionPoints& dp, uint32_t* packed, uint32_t* sign,
@@ -45,6 +58,18 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32
                          const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
                          const Levels& lv, void* y, bool y_bf16, void* workspace,
                          hipStream_t stream);
+
+// b-bit codes (3..6), codes of a row as a little-endian bit stream along k.
+// quantize.hip
+bool bits_supported(const DecisionPointsN& dp, int64_t k);
+hipError_t launch_quantize_bits(const void* w, bool w_is_bf16, int64_t n, int64_t k, int bits,
+                                const DecisionPointsN& dp, const LevelsN& lv, uint32_t* packed,
+                                uint32_t* sign, float* scale, double* row_sums,
+                                hipStream_t stream);
+// dequantize.hip
+hipError_t launch_dequantize_bits(const uint32_t* packed, const uint32_t* sign,
+                                  const float* scale, int64_t n, int64_t k, int bits,
+                                  const LevelsN& lv, uint16_t* out, hipStream_t stream);
 
 // Group-wise form (one float16 max per `gs` weights along k).
 // quantize.hip: alpha has a bucket grid and G_1 * 2^-24 is a normal binary32

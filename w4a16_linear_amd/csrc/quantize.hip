@@ -837,6 +837,308 @@ hipError_t dispatch_grouped(const T* w, int64_t total, int gs, const DecisionPoi
   }
 }
 
+// ---------------------------------------------------------------- other code widths
+//
+// b-bit codes (the configuration section's 3, 5 or 6 bits; 2^b - 1 levels in
+// place of 15).  Same structure as quantize_block_rows: a block owns a row at
+// a time, the row stays in registers, codes come from a bucket table over the
+// L = 2^b - 1 decision points (up to 4096 buckets: finer grids separate the
+// closer points of 63 levels).  A lane's eight codes make 8b bits of the row's
+// little-endian bit stream; the four lanes of a quad hold 32 codes = b words,
+// combined with quad broadcasts (DPP) and stored by the quad's lanes in turn.
+// kErr: the row's error sums instead of the stored form, as in the 4-bit
+// kernel, with the row table L[q] = bf16(G_q m) in the wave's LDS slot.
+constexpr int kMaxBucketsN = 4096;
+
+bool bucket_grid_n(const float* t, int L, BucketGrid& g) {
+  uint32_t c[kMaxLevels];
+  for (int j = 0; j < L; ++j) c[j] = float_bits(t[j]);
+  if (c[0] <= 2 * kGuard) return false;
+  for (int mbits = 3; mbits <= 12; ++mbits) {
+    const int shift = 23 - mbits;
+    const uint32_t b0 = (c[0] - kGuard) & ~((1u << shift) - 1u);
+    const int64_t nb = (int64_t)((kTop - b0) >> shift) + 1;
+    if (nb > kMaxBucketsN) return false;
+    bool ok = true;
+    for (int j = 0; j + 1 < L && ok; ++j)
+      ok = ((c[j] + kGuard - b0) >> shift) < ((c[j + 1] - kGuard - b0) >> shift);
+    if (ok) {
+      g.b0 = b0;
+      g.shift = shift;
+      g.nb = (int)nb;
+      return true;
+    }
+  }
+  return false;
+}
+
+// The table of build_table over L points held in LDS.
+__device__ void build_table_n(const float* pts, int L, BucketGrid g, uint2* tab) {
+  for (int b = threadIdx.x; b < g.nb; b += blockDim.x) {
+    const uint32_t lo = g.b0 + ((uint32_t)b << g.shift);
+    const uint32_t hi = lo + (1u << g.shift);
+    uint32_t below = 0u, next = kNoPoint;
+    for (int j = L - 1; j >= 0; --j) {
+      const uint32_t c = __float_as_uint(pts[j]);
+      const bool under = c + kGuard < lo;
+      below += under ? 1u : 0u;
+      next = under ? next : c;
+    }
+    const uint32_t x = (next != kNoPoint && next - kGuard < hi) ? kGuard - next : kGuard - kNoPoint;
+    tab[b] = make_uint2(x, below);
+  }
+}
+
+// Codes of a lane's eight elements (fast path, then exact where flagged).
+template <typename T>
+__device__ __forceinline__ void codes8(const Slot<T>& v, float mx, float r, bool fast,
+                                       const uint2* tab, int shift, uint32_t nbase, float ulo,
+                                       const float* pts, uint32_t (&q)[8]) {
+  uint32_t nr = 0u;
+  if (fast) {
+    nr = 0xFFFFFFFFu;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float up = __builtin_amdgcn_fmed3f(fabsf(v.at(i)) * r, ulo, 2.0f);
+      const uint32_t ub = __float_as_uint(up);
+      const uint2 e = table_at(tab, ub, shift, nbase);
+      const int d = (int)(ub + e.x);
+      q[i] = e.y + (d >= (int)kGuard ? 1u : 0u);
+      nr = min(nr, (uint32_t)d);
+    }
+  }
+  if (nr <= 2u * kGuard) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = code_exact(fabsf(v.at(i)), mx, tab, shift, nbase, ulo, pts);
+  }
+}
+
+// Word w of a 32-code block, the quad's fragments f[j] (8b bits each) laid
+// end to end from bit 0.
+template <int B>
+__device__ __forceinline__ uint32_t block_word(const uint64_t (&f)[4], int w) {
+  uint32_t out = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int s = 8 * B * j - 32 * w;  // where fragment j starts relative to word w
+    if (s >= 0 && s < 32) out |= (uint32_t)(f[j] << s);
+    if (s < 0 && s > -8 * B) out |= (uint32_t)(f[j] >> (-s));
+  }
+  return out;
+}
+
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t v, int j) {
+  switch (j) {
+    case 0: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x00, 0xF, 0xF, false);
+    case 1: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x55, 0xF, 0xF, false);
+    case 2: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xAA, 0xF, 0xF, false);
+    default: return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xFF, 0xF, 0xF, false);
+  }
+}
+
+// Stores a lane's eight codes (q) and sign byte: the quad's 32 codes make b
+// words at word index blk * b of the row; lane j of the quad stores words
+// j and j + 4.  `valid` is uniform over a quad.
+template <int B>
+__device__ __forceinline__ void store_bits(uint32_t* prow, uint32_t* srow, int blk, int lane,
+                                           bool valid, const uint32_t (&q)[8], uint32_t sbyte) {
+  uint64_t frag = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) frag |= (uint64_t)q[i] << (B * i);
+  uint64_t f[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    f[j] = (uint64_t)quad_bcast((uint32_t)frag, j) | ((uint64_t)quad_bcast((uint32_t)(frag >> 32), j) << 32);
+  uint32_t s32 = valid ? (sbyte << (8 * (lane & 3))) : 0u;
+  s32 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)s32, 0xB1, 0xF, 0xF, false);
+  s32 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)s32, 0x4E, 0xF, 0xF, false);
+  if (valid) {
+    const int j = lane & 3;
+#pragma unroll
+    for (int w = 0; w < B; ++w)
+      if ((w & 3) == j) prow[blk * B + w] = block_word<B>(f, w);
+    if (j == 0) srow[blk] = s32;
+  }
+}
+
+template <typename T, int NCT, int B, bool kErr>
+__global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
+    const T* __restrict__ w, int64_t n, int k, DecisionPointsN dp, BucketGrid g, LevelsN lv,
+    uint32_t* __restrict__ packed, uint32_t* __restrict__ sign, float* __restrict__ scale,
+    double* __restrict__ row_sums) {
+  constexpr int L = (1 << B) - 1;
+  constexpr int kWaves = kBlockThreads / kWave;
+  __shared__ uint2 s_tab[kMaxBucketsN];
+  __shared__ float s_pts[kMaxLevels + 1];
+  __shared__ double s_g[kMaxLevels + 1];
+  __shared__ float s_wmax[2][kWaves];
+  __shared__ uint32_t s_recw[kErr ? kWaves : 1][L + 1];
+  __shared__ double s_sum[2][kWaves][2];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int64_t stride = gridDim.x;
+
+  Slot<T> v[2][NCT];
+  auto load_row = [&](int64_t rr, int buf) __attribute__((always_inline)) {
+    const T* wr = w + rr * (int64_t)k;
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) {
+      const int e0 = c * kBlockChunk + tid * 8;
+      if (e0 < k) v[buf][c].load(wr + e0); else v[buf][c].zero();
+    }
+  };
+  int64_t row = blockIdx.x;
+  if (row < n) load_row(row, 0);
+
+  // decision points and levels to LDS (a lane-varying index into the argument
+  // struct reads it from memory; this happens once per block)
+  if (tid < L) s_pts[tid] = dp.t[tid];
+  if (tid == L) s_pts[L] = 2.0f;
+  if (kErr && tid <= L) s_g[tid] = lv.g[tid];
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  build_table_n(s_pts, L, g, s_tab);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  const int shift = g.shift;
+  const uint32_t nbase = (0u - (g.b0 >> g.shift)) << 3;
+  const float ulo = __uint_as_float(g.b0);
+
+  int64_t pend = -1;  // kErr: row whose partial sums wait in s_sum
+  auto flush_sums = [&](int slot) __attribute__((always_inline)) {
+    if (tid == 0 && pend >= 0) {
+      double a0 = 0.0, a1 = 0.0;
+#pragma unroll
+      for (int q = 0; q < kWaves; ++q) {
+        a0 += s_sum[slot][q][0];
+        a1 += s_sum[slot][q][1];
+      }
+      row_sums[2 * pend] = a0;
+      row_sums[2 * pend + 1] = a1;
+    }
+  };
+  auto process = [&](int64_t rr, int buf, int ms) __attribute__((always_inline)) {
+    typename Slot<T>::Acc acc = Slot<T>::acc0();
+#pragma unroll
+    for (int c = 0; c < NCT; ++c) v[buf][c].absmax(acc);
+    float mx = wave_max(Slot<T>::finish(acc));
+    if (lane == 0) s_wmax[ms][wave] = mx;
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    mx = fmaxf(fmaxf(s_wmax[ms][0], s_wmax[ms][1]), fmaxf(s_wmax[ms][2], s_wmax[ms][3]));
+    if constexpr (kErr) flush_sums(ms ^ 1);
+    const bool fast = mx >= 0x1p-125f && mx <= 0x1p125f;
+    const float r = 1.0f / mx;
+    if constexpr (!kErr) {
+      uint32_t* prow = packed + rr * (int64_t)(k / 32 * B);
+      uint32_t* srow = sign + rr * (int64_t)(k / 32);
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        const int e0 = c * kBlockChunk + tid * 8;
+        uint32_t q[8];
+        codes8(v[buf][c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts, q);
+        store_bits<B>(prow, srow, e0 >> 5, lane, e0 < k, q, sign_byte(v[buf][c]));
+      }
+      if (tid == 0) scale[rr] = mx;
+    } else {
+      if (lane <= L) s_recw[wave][lane] = bf16_rne_from_f64(s_g[lane] * (double)mx);
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // one wave's LDS ops complete in order
+      float sw2 = 0.0f, se2 = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NCT; ++c) {
+        uint32_t q[8];
+        codes8(v[buf][c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts, q);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float xv = v[buf][c].at(i);  // zero past k
+          const float e = fabsf(xv) - __uint_as_float(s_recw[wave][q[i]] << 16);
+          sw2 = fmaf(xv, xv, sw2);
+          se2 = fmaf(e, e, se2);
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        sw2 += __shfl_xor(sw2, off, kWave);
+        se2 += __shfl_xor(se2, off, kWave);
+      }
+      if (lane == 0) {
+        s_sum[ms][wave][0] = sw2;
+        s_sum[ms][wave][1] = se2;
+      }
+      pend = rr;
+    }
+  };
+
+  while (row < n) {
+    const int64_t r1 = row + stride;
+    if (r1 < n) load_row(r1, 1);
+    process(row, 0, 0);
+    if (r1 >= n) break;
+    const int64_t r2 = r1 + stride;
+    if (r2 < n) load_row(r2, 0);
+    process(r1, 1, 1);
+    row = r2;
+  }
+  if constexpr (kErr) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    const int64_t cnt = blockIdx.x < n ? (n - 1 - blockIdx.x) / stride + 1 : 0;
+    flush_sums((int)((cnt - 1) & 1));
+  }
+}
+
+template <typename T, int NCT, int B, bool kErr>
+hipError_t launch_bits_rows(const T* w, int64_t n, int64_t k, const DecisionPointsN& dp,
+                            const BucketGrid& g, const LevelsN& lv, uint32_t* packed,
+                            uint32_t* sign, float* scale, double* row_sums, hipStream_t stream) {
+  static const int per_cu = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, quantize_bits_rows<T, NCT, B, kErr>,
+                                                     kBlockThreads, 0) != hipSuccess || b < 1)
+      b = 1;
+    return b;
+  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 1;
+  int64_t blocks = std::min<int64_t>((int64_t)per_cu * cus, kPersistBlocks);
+  blocks = std::min<int64_t>(blocks, n);
+  hipLaunchKernelGGL((quantize_bits_rows<T, NCT, B, kErr>), dim3((unsigned)blocks),
+                     dim3(kBlockThreads), 0, stream, w, n, (int)k, dp, g, lv, packed, sign, scale,
+                     row_sums);
+  return hipGetLastError();
+}
+
+template <typename T, int B, bool kErr>
+hipError_t dispatch_bits_nct(const T* w, int64_t n, int64_t k, const DecisionPointsN& dp,
+                             const BucketGrid& g, const LevelsN& lv, uint32_t* packed,
+                             uint32_t* sign, float* scale, double* row_sums, hipStream_t stream) {
+  const int64_t nct = (k + kBlockChunk - 1) / kBlockChunk;
+  if (nct <= 1)
+    return launch_bits_rows<T, 1, B, kErr>(w, n, k, dp, g, lv, packed, sign, scale, row_sums, stream);
+  if (nct <= 2)
+    return launch_bits_rows<T, 2, B, kErr>(w, n, k, dp, g, lv, packed, sign, scale, row_sums, stream);
+  if (nct <= 4)
+    return launch_bits_rows<T, 4, B, kErr>(w, n, k, dp, g, lv, packed, sign, scale, row_sums, stream);
+  return launch_bits_rows<T, 8, B, kErr>(w, n, k, dp, g, lv, packed, sign, scale, row_sums, stream);
+}
+
+template <typename T, bool kErr>
+hipError_t dispatch_bits(const T* w, int64_t n, int64_t k, int bits, const DecisionPointsN& dp,
+                         const LevelsN& lv, uint32_t* packed, uint32_t* sign, float* scale,
+                         double* row_sums, hipStream_t stream) {
+  BucketGrid g;
+  if (!bucket_grid_n(dp.t, dp.n, g)) return hipErrorNotSupported;
+  switch (bits) {
+    case 3: return dispatch_bits_nct<T, 3, kErr>(w, n, k, dp, g, lv, packed, sign, scale, row_sums, stream);
+    case 5: return dispatch_bits_nct<T, 5, kErr>(w, n, k, dp, g, lv, packed, sign, scale, row_sums, stream);
+    case 6: return dispatch_bits_nct<T, 6, kErr>(w, n, k, dp, g, lv, packed, sign, scale, row_sums, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
 
 bool error_sums_supported(const DecisionPoints& dp, int64_t k) {
@@ -858,6 +1160,29 @@ hipError_t launch_quantize(const void* w, bool w_is_bf16, int64_t n, int64_t k,
   if (w_is_bf16)
     return dispatch(static_cast<const uint16_t*>(w), n, k, dp, packed, sign, scale, stream);
   return dispatch(static_cast<const float*>(w), n, k, dp, packed, sign, scale, stream);
+}
+
+bool bits_supported(const DecisionPointsN& dp, int64_t k) {
+  BucketGrid g;
+  return bucket_grid_n(dp.t, dp.n, g) && k <= 8 * kBlockChunk;
+}
+
+hipError_t launch_quantize_bits(const void* w, bool w_is_bf16, int64_t n, int64_t k, int bits,
+                                const DecisionPointsN& dp, const LevelsN& lv, uint32_t* packed,
+                                uint32_t* sign, float* scale, double* row_sums,
+                                hipStream_t stream) {
+  if (row_sums) {
+    if (w_is_bf16)
+      return dispatch_bits<uint16_t, true>(static_cast<const uint16_t*>(w), n, k, bits, dp, lv,
+                                           nullptr, nullptr, nullptr, row_sums, stream);
+    return dispatch_bits<float, true>(static_cast<const float*>(w), n, k, bits, dp, lv, nullptr,
+                                      nullptr, nullptr, row_sums, stream);
+  }
+  if (w_is_bf16)
+    return dispatch_bits<uint16_t, false>(static_cast<const uint16_t*>(w), n, k, bits, dp, lv,
+                                          packed, sign, scale, nullptr, stream);
+  return dispatch_bits<float, false>(static_cast<const float*>(w), n, k, bits, dp, lv, packed,
+                                     sign, scale, nullptr, stream);
 }
 
 bool grouped_supported(const DecisionPoints& dp, const Levels& lv) {

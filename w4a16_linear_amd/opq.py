@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libopq.so")
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 OPQ_F32 = 0
 OPQ_BF16 = 1
@@ -44,6 +44,16 @@ _SIGNATURES = {
                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                   ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                   ctypes.c_size_t, ctypes.c_void_p]),
+    "opq_quantize_bits": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                         ctypes.c_int64, ctypes.c_int, ctypes.c_float,
+                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p]),
+    "opq_dequantize_bits": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                           ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]),
+    "opq_error_sums_bits": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int, ctypes.c_float,
+                                           ctypes.c_void_p, ctypes.c_void_p]),
     "opq_quantize_grouped": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -142,6 +152,19 @@ class QuantizedWeight(NamedTuple):
         return (self.packed.shape[0], self.packed.shape[1] * 8)
 
 
+class BitsWeight(NamedTuple):
+    """b-bit codes (3..6) with one float32 max per row; codes of a row form a
+    little-endian bit stream along k (32 codes per `bits` words)."""
+    packed: torch.Tensor  # int32 [n, k*bits/32]
+    sign: torch.Tensor    # int32 [n, k/32]
+    scale: torch.Tensor   # float32 [n]
+    bits: int
+
+    @property
+    def shape(self):
+        return (self.packed.shape[0], self.sign.shape[1] * 32)
+
+
 class GroupedWeight(NamedTuple):
     """The group-wise stored form: one float16 max per `group` weights along k."""
     packed: torch.Tensor   # int32 [n, k/8]
@@ -170,6 +193,36 @@ def quantize(w: torch.Tensor, alpha: float, out: Optional[QuantizedWeight] = Non
                              _ptr(out.scale), _stream(w.device))
     _check("opq_quantize", st)
     return out
+
+
+def quantize_bits(w: torch.Tensor, alpha: float, bits: int,
+                  out: Optional[BitsWeight] = None) -> BitsWeight:
+    """Quantize a float32 or bfloat16 weight [n, k] with b-bit codes (3..6)."""
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("w must be float32 or bfloat16")
+    _need_cuda("w", w, w.dtype, 2)
+    n, k = w.shape
+    if bits not in (3, 4, 5, 6):
+        raise ValueError(f"bits must be 3, 4, 5 or 6, got {bits}")
+    if out is None:
+        out = BitsWeight(torch.empty((n, k * bits // 32), dtype=torch.int32, device=w.device),
+                         torch.empty((n, k // 32), dtype=torch.int32, device=w.device),
+                         torch.empty((n,), dtype=torch.float32, device=w.device), bits)
+    _check_bits(out, n, k)
+    dtype = OPQ_BF16 if w.dtype == torch.bfloat16 else OPQ_F32
+    st = load().opq_quantize_bits(_ptr(w), dtype, n, k, out.bits, alpha, _ptr(out.packed),
+                                  _ptr(out.sign), _ptr(out.scale), _stream(w.device))
+    _check("opq_quantize_bits", st)
+    return out
+
+
+def _check_bits(bw: BitsWeight, n: int, k: int) -> None:
+    for name, t, dt in (("packed", bw.packed, torch.int32), ("sign", bw.sign, torch.int32)):
+        _need_cuda(name, t, dt, 2)
+    _need_cuda("scale", bw.scale, torch.float32, 1)
+    if (bw.bits not in (3, 4, 5, 6) or tuple(bw.packed.shape) != (n, k * bw.bits // 32) or
+            tuple(bw.sign.shape) != (n, k // 32) or tuple(bw.scale.shape) != (n,)):
+        raise ValueError(f"b-bit weight buffers do not match n={n}, k={k}, bits={bw.bits}")
 
 
 def quantize_grouped(w: torch.Tensor, alpha: float, group: int = 128,
@@ -204,8 +257,18 @@ def _check_grouped(gw: GroupedWeight, n: int, k: int) -> None:
 
 
 def dequantize(qw, alpha: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """bfloat16 reconstruction [n, k] of a QuantizedWeight or GroupedWeight."""
+    """bfloat16 reconstruction [n, k] of a QuantizedWeight, GroupedWeight or
+    BitsWeight."""
     n, k = qw.shape
+    if isinstance(qw, BitsWeight):
+        _check_bits(qw, n, k)
+        if out is None:
+            out = torch.empty((n, k), dtype=torch.bfloat16, device=qw.packed.device)
+        _need_cuda("out", out, torch.bfloat16, 2)
+        st = load().opq_dequantize_bits(_ptr(qw.packed), _ptr(qw.sign), _ptr(qw.scale), n, k,
+                                        qw.bits, alpha, _ptr(out), _stream(qw.packed.device))
+        _check("opq_dequantize_bits", st)
+        return out
     if isinstance(qw, GroupedWeight):
         _check_grouped(qw, n, k)
         if out is None:
@@ -230,9 +293,11 @@ def linear_workspace_bytes(m: int, n: int, k: int) -> int:
     return int(load().opq_linear_workspace_bytes(m, n, k))
 
 
-def error_sums(w: torch.Tensor, alpha: float, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+def error_sums(w: torch.Tensor, alpha: float, out: Optional[torch.Tensor] = None,
+               bits: int = 4) -> torch.Tensor:
     """Per row of w: (sum w^2, sum (w - w')^2) as float64 [n, 2], w' the bf16
-    reconstruction opq_quantize + opq_dequantize would give (nothing stored)."""
+    reconstruction quantize + dequantize would give with b-bit codes (nothing
+    stored)."""
     _need_cuda("w", w, w.dtype, 2)
     if w.dtype == torch.float32:
         dt = OPQ_F32
@@ -244,18 +309,18 @@ def error_sums(w: torch.Tensor, alpha: float, out: Optional[torch.Tensor] = None
     if out is None:
         out = torch.empty((n, 2), dtype=torch.float64, device=w.device)
     _need_cuda("out", out, torch.float64, 2)
-    st = load().opq_error_sums(_ptr(w), dt, n, k, alpha, _ptr(out), _stream(w.device))
-    _check("opq_error_sums", st)
+    st = load().opq_error_sums_bits(_ptr(w), dt, n, k, bits, alpha, _ptr(out), _stream(w.device))
+    _check("opq_error_sums_bits", st)
     return out
 
 
-def snr_db(weights, alpha: float) -> float:
+def snr_db(weights, alpha: float, bits: int = 4) -> float:
     """10 log10(sum w^2 / sum (w - w')^2) over one tensor or a list of tensors."""
     if isinstance(weights, torch.Tensor):
         weights = [weights]
     tot = None
     for w in weights:
-        s = error_sums(w, alpha).sum(dim=0)
+        s = error_sums(w, alpha, bits=bits).sum(dim=0)
         tot = s if tot is None else tot + s
     num, den = (float(v) for v in tot.cpu())
     return float("inf") if den == 0.0 else 10.0 * float(np.log10(num / den))
