@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--group", type=int, default=0, choices=[0, 32, 64, 128, 256],
                     help="0: one float32 max per row; else the group-wise form (float16 max "
                          "per this many weights along k)")
+    ap.add_argument("--bits", type=int, default=4, choices=[3, 4, 5, 6],
+                    help="code width; other than 4 the step is quantize -> dequantize (the "
+                         "linear layer runs on 4-bit codes)")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for > 768 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -75,12 +78,14 @@ def workload(name):
     return L
 
 
-def algorithmic(m, n, k, w_bytes, group=0):
+def algorithmic(m, n, k, w_bytes, group=0, bits=4):
     """Per-launch algorithmic bytes / flops (what the method must move).  The
-    scales are 4 B per row, or 2 B per group of `group` weights."""
+    scales are 4 B per row, or 2 B per group of `group` weights; codes take
+    bits/8 B and signs 1/8 B per weight."""
     sc = 2 * n * (k // group) if group else 4 * n
-    quant = {"bytes": n * k * (w_bytes + 0.625) + sc, "flops": 0}
-    dequant = {"bytes": n * k * (0.625 + 2) + sc, "flops": 0}
+    st = (bits + 1) / 8.0
+    quant = {"bytes": n * k * (w_bytes + st) + sc, "flops": 0}
+    dequant = {"bytes": n * k * (st + 2) + sc, "flops": 0}
     lin = {"bytes": 0.625 * n * k + sc + 2 * m * k + 4 * m * n, "flops": 2 * m * n * k}
     return {"quantize": quant, "dequantize": dequant, "linear": lin}
 
@@ -197,17 +202,24 @@ def main():
         w_bytes = 4
     x_host = WL.to_bf16(L.make_x())
 
-    group = args.group
+    group, bits = args.group, args.bits
     if group and k % group:
         print(f"--group {group} does not divide k={k}", file=sys.stderr)
         sys.exit(2)
-    alg = algorithmic(m, n, k, w_bytes, group)
+    if group and bits != 4:
+        print("--group and --bits other than 4 do not combine", file=sys.stderr)
+        sys.exit(2)
+    alg = algorithmic(m, n, k, w_bytes, group, bits)
     per_set = (n * k * w_bytes + n * k * 0.625 + 4 * n + n * k * 2 + m * k * 2 + m * n * 4)
     rot = args.rotate or max(2, int(np.ceil(800e6 / per_set)))
     sets = []
     for _ in range(rot):
         w = w_host.to(dev)
-        if group:
+        if bits != 4:
+            qw = opq.BitsWeight(torch.empty((n, k * bits // 32), dtype=torch.int32, device=dev),
+                                torch.empty((n, k // 32), dtype=torch.int32, device=dev),
+                                torch.empty((n,), dtype=torch.float32, device=dev), bits)
+        elif group:
             qw = opq.GroupedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
                                    torch.empty((n, k // 32), dtype=torch.int32, device=dev),
                                    torch.empty((n, k // group), dtype=torch.float16, device=dev),
@@ -227,7 +239,9 @@ def main():
     def launch(kind, i):
         w, qw, d, x, y = sets[i % rot]
         if kind == "quantize":
-            if group:
+            if bits != 4:
+                opq.quantize_bits(w, alpha, bits, out=qw)
+            elif group:
                 opq.quantize_grouped(w, alpha, group, out=qw)
             else:
                 opq.quantize(w, alpha, out=qw)
@@ -236,7 +250,7 @@ def main():
         else:
             opq.linear(x, qw, alpha, out=y)
 
-    kinds = ["quantize", "dequantize", "linear"]
+    kinds = ["quantize", "dequantize", "linear"] if bits == 4 else ["quantize", "dequantize"]
 
     def step(i):
         for kind in kinds:
@@ -304,7 +318,8 @@ def main():
         roof = {"bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4)}
     roof["kernel"] = dom
-    wl_name = f"{args.workload}_g{group}" if group else args.workload
+    wl_name = (f"{args.workload}_g{group}" if group else
+               f"{args.workload}_b{bits}" if bits != 4 else args.workload)
     roof["traffic"] = measured_traffic(dom, wl_name)
 
     value = 100.0 * (ideal_total * 1e-3) / ms_step
@@ -325,13 +340,15 @@ def main():
         "config": {"workload": f"{args.workload}: {WL_title(args.workload)}", "m": m, "n": n,
                    "k": k, "w_dtype": L.w_dtype, "alpha": alpha, "rotating_sets": rot,
                    "scales": (f"float16 per group of {group}" if group else "float32 per row"),
-                   "step": "quantize -> dequantize -> linear"},
+                   "bits": bits,
+                   "step": ("quantize -> dequantize -> linear" if bits == 4
+                            else "quantize -> dequantize")},
         "roofline": roof,
         "kernels": kern,
         "kernels_sum_us": round(sum(kk["us"] for kk in kern.values()), 3),
         "wall_s": round(wall, 3),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and bits == 4:
         import oracle as O
         xb = WL.bf16_bits(x_host)
         wv = (O.bf16_bits_to_f32(WL.bf16_bits(w_host)) if L.w_dtype == "bf16"
@@ -480,6 +497,21 @@ def model_pass(args, dev):
              "algorithmic_bytes": int(alg_e), "launches": len(shapes),
              "stored_form_agrees_db": max(abs(sweep_snr[grid.index(a)] - snr[a])
                                           for a in (0.45, 1.0))}
+    # SNR per code width (3..6 bits) at three alphas, whole model, nothing stored
+    widths = {}
+    for b in (3, 4, 5, 6):
+        row = {}
+        for a in (0.45, 0.73, 1.0):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for w, s_ in zip(weights, sums):
+                opq.error_sums(w, a, out=s_, bits=b)
+            e1.record(stream)
+            tot = torch.stack([s_.sum(dim=0) for s_ in sums]).sum(dim=0).cpu()
+            row[str(a)] = {"snr_db": round(10.0 * float(np.log10(float(tot[0]) / float(tot[1]))), 3),
+                           "us": round(e0.elapsed_time(e1) * 1e3, 1)}
+        widths[str(b)] = row
     dom = max(kern, key=lambda kk: kern[kk]["us"])
     out = {
         "metric": METRIC,
@@ -505,6 +537,7 @@ def model_pass(args, dev):
         "snr_db": {str(a): round(v, 3) for a, v in snr.items()},
         "snr_gain_vs_alpha1_db": {str(a): round(v - snr[1.0], 3) for a, v in snr.items()},
         "alpha_sweep": sweep,
+        "snr_by_width": widths,
         "wall_s": round(wall, 3),
         "cpu_baseline": None,
     }
