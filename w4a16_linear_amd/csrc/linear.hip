@@ -249,25 +249,21 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
 
 // ---------------------------------------------------------------- tiled MFMA path
 //
-// Block tile 256 (x rows) x 256 (weight rows), k steps of 64, four waves.
-// Wave w owns weight rows [64w, 64w + 64) of the tile and all 256 x rows:
-// 8 x 2 accumulators of 32x32 (256 fp32 per lane, held in AGPRs).
+// Block tile 256 (x rows) x 256 (weight rows), k steps of 64,
+// v_mfma_f32_32x32x16_bf16, eight waves (two per SIMD).  Wave w owns weight
+// rows [32w, 32w + 32) of the tile (one B fragment) and all 256 x rows: 8
+// accumulators of 32x32 (128 fp32 per lane).
 //
-// Weights never pass through LDS: each lane loads the packed words of its two
-// weight rows straight into VGPRs, in the layout of the MFMA B operand (one
-// packed word = the eight k values a lane supplies), and dequantizes them with
-// its rows' tables held as byte planes in registers (v_perm lookups).  Lanes
+// Each weight row is decoded once per tile step, in registers: a lane
+// dequantizes one packed word (the eight k values it supplies to the B
+// operand) with its row's table held as byte planes (v_perm lookups).  Lanes
 // 0..31 take words 0..3 of the 8-word k step and lanes 32..63 words 4..7, so
 // sub-step s contracts k-blocks {s, 4 + s}; the x fragments read from LDS use
 // the same k-blocks.  Within a k-block the dequantizer emits bf16 pairs in the
-// order (k0,k2) (k4,k6) (k1,k3) (k5,k7); x is stored to LDS in that order too.
-// Only x is staged in LDS (two stages, rows XOR-swizzled by 16-byte chunk).
+// order (k0,k2) (k4,k6) (k1,k3) (k5,k7); x is stored to LDS in that order too
+// (two stages, rows XOR-swizzled by 16-byte chunk).
 
 constexpr int kTM = 256, kTN = 256, kTK = 64;
-constexpr int kMfmaWaves = 8;   // waves per 256x256 tile (8: two per SIMD)
-constexpr int kMfmaXSplit = 1;  // waves sharing a weight row, each with 256 / kMfmaXSplit x rows
-constexpr bool kWeightStage = true;  // linear_mfma_ws (weights through LDS) instead of linear_mfma
-constexpr int kAChunks = kTK / 8;                  // 16-byte chunks per LDS row
 constexpr int kAStage = kTM * kTK;                 // bf16 per stage
 
 // LDS element offset of 16-byte chunk c of tile row r.  A row is 128 bytes
@@ -276,228 +272,15 @@ constexpr int kAStage = kTM * kTK;                 // bf16 per stage
 // 16-lane passes of ds_read_b128 conflict-free.
 __device__ __forceinline__ int a_off(int r, int c) { return r * kTK + ((c ^ ((r >> 1) & 7)) << 3); }
 
-// Scheduling hint for one sub-step (N MFMAs): alternate each MFMA with V
-// VALU instructions so the dequantizer runs in the MFMAs' shadow, and spread
-// the x fragment reads (R), the x stage writes (W) and global loads (G) over
-// the first MFMAs.  V = 0 leaves the order to the compiler.  With one wave per
-// SIMD, V = 3 measured best; with two waves per SIMD (the default) the other
-// wave fills the MFMA shadow and the hints only cost registers (V = 3 spills).
-constexpr int kInterleaveV = 0;
-
-template <int I, int N, int V, int R, int W, int G>
-__device__ __forceinline__ void interleave_substep() {
-  if constexpr (V > 0 && I < N) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);          // MFMA
-    if constexpr (I < R) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    if constexpr (I < W) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-    if constexpr (I < G) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-    __builtin_amdgcn_sched_group_barrier(0x002, V, 0);          // VALU
-    interleave_substep<I + 1, N, V, R, W, G>();
-  }
-}
-
-template <bool kHalfTail, int WAVES, int XSPLIT>
-__global__ __launch_bounds__(WAVES * 64, 1) void linear_mfma(
-    const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
-    const uint32_t* __restrict__ sign, const float* __restrict__ scale,
-    const float* __restrict__ bias, int m, int n, int k, int tiles_m, Levels lv,
-    void* __restrict__ y, int y_bf16) {
-  constexpr int kThreads = WAVES * kWave;
-  constexpr int WG = WAVES / XSPLIT;                // weight groups (waves sharing x rows)
-  constexpr int NF = 8 / WG;                        // 32-row weight fragments per wave
-  constexpr int MI = 8 / XSPLIT;                    // 32-row x blocks per wave
-  constexpr int XCH = kTM * kTK / 8 / kThreads;     // x chunks each thread stages per step
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kAStage];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
-  // consecutive blocks share a weight tile and walk the x tiles
-  const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
-  const int m0 = tile_m * kTM;
-  const int wg = wave % WG, xh = wave / WG;
-  const int nw = tile_n * kTN + wg * 32 * NF;    // first weight row of this wave
-  const int mx0 = xh * 32 * MI;                   // first x row of this wave in the tile
-  const int g = lane >> 5;                        // which half of the k step
-  const int kwords = k / 8, swords = k / 32;
-  const int nsteps = (k + kTK - 1) / kTK;
-
-  // This lane's weight rows (B fragments f < NF).  Rows past n are clamped to
-  // row n - 1: their columns are computed and never stored.
-  int brow[NF];
-  RowLut lut[NF];
-  uint32_t pw_off[NF], sw_off[NF];  // byte offsets from the wave's first row
-  const int nw_c = min(nw, n - 1);
-  const char* pbase = reinterpret_cast<const char*>(packed + (int64_t)nw_c * kwords);
-  const char* sbase = reinterpret_cast<const char*>(sign + (int64_t)nw_c * swords);
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    brow[f] = nw + 32 * f + (lane & 31);
-    const int rc = min(brow[f], n - 1);
-    lut[f] = make_row_lut(lv, scale[rc]);
-    pw_off[f] = (uint32_t)(rc - nw_c) * (uint32_t)kwords * 4u;
-    sw_off[f] = (uint32_t)(rc - nw_c) * (uint32_t)swords * 4u;
-  }
-
-  // Weights of step kt: words 4g..4g+3 and sign word g of the step.  Steps past
-  // the end re-read the last one (every prefetch is issued unconditionally, so
-  // the wait counts stay static); in a final half step (k % 64 == 32) lanes
-  // g = 1 re-read the first half and the dequantizer zeroes their fragments.
-  auto load_b = [&](int kt, uint4 (&pw)[NF], uint32_t (&sw)[NF]) {
-    const int kc = min(min(kt, nsteps - 1) * kTK + 32 * g, k - 32);
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      pw[f] = *reinterpret_cast<const uint4*>(pbase + pw_off[f] + (uint32_t)kc / 2u);
-      sw[f] = *reinterpret_cast<const uint32_t*>(sbase + sw_off[f] + (uint32_t)kc / 8u);
-    }
-  };
-  // x of step kt: thread tid moves chunks tid + kThreads i (row c/8, chunk c%8).
-  // Rows past m read row m - 1 (never stored); chunks past k read the last
-  // chunk, which only meets zero weights.
-  const char* xbase = reinterpret_cast<const char*>(x + (int64_t)m0 * k);
-  uint32_t x_off[XCH];
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    const int c = tid + kThreads * i;
-    const int r = min(m0 + (c >> 3), m - 1) - m0;
-    x_off[i] = ((uint32_t)r * (uint32_t)k + 8u * (uint32_t)(c & 7)) * 2u;
-  }
-  auto load_a = [&](int kt, uint4 (&xa)[XCH]) {
-    const int kc = min(kt, nsteps - 1) * kTK;
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      uint32_t off = x_off[i] + (uint32_t)kc * 2u;
-      if constexpr (kHalfTail) {
-        const int c = tid + kThreads * i;
-        if (kc + 8 * (c & 7) >= k) off -= 64u;  // step back into the row
-      }
-      xa[i] = *reinterpret_cast<const uint4*>(xbase + off);
-    }
-  };
-  auto store_a = [&](int stage, const uint4 (&xa)[XCH]) {
-    uint16_t* base = s_a + stage * kAStage;
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int c = tid + kThreads * i;
-      *reinterpret_cast<uint4*>(base + a_off(c >> 3, c & 7)) = sigma_order(xa[i]);
-    }
-  };
-
-  floatx16_t acc[MI][NF];
-#pragma unroll
-  for (int i = 0; i < MI; ++i)
-#pragma unroll
-    for (int f = 0; f < NF; ++f)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][f][e] = 0.0f;
-
-  // Sub-step s of a k step: dequantize word s of both B fragments, read the
-  // eight x fragments of k-blocks {s, 4 + s}.
-  auto dequant_b = [&](int kt, int s, const uint4 (&pwv)[NF], const uint32_t (&swv)[NF],
-                       bf16x8_t (&b)[NF]) {
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const uint32_t words[4] = {pwv[f].x, pwv[f].y, pwv[f].z, pwv[f].w};
-      uint32_t o[4];
-      dequant_word(words[s], swv[f] >> (8 * s), lut[f], o);
-      if constexpr (kHalfTail) {
-        if (kt == nsteps - 1 && g == 1) o[0] = o[1] = o[2] = o[3] = 0u;
-      }
-      b[f] = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-    }
-  };
-  auto read_a = [&](const uint16_t* sa, int s, bf16x8_t (&a)[MI]) {
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-      a[mi] = *reinterpret_cast<const bf16x8_t*>(sa + a_off(mx0 + mi * 32 + (lane & 31), 4 * g + s));
-  };
-
-  // Pipeline per k step kt (x in LDS stage kt & 1); fragments of sub-step 0
-  // are ready when the step starts:
-  //   issue the weights of step kt + 1;
-  //   sub-steps s = 0..2: read x fragments and dequantize weights of s + 1,
-  //     MFMAs of s; after sub-step 0's MFMAs store x of step kt + 1 (loaded
-  //     during step kt - 1) into the other stage and issue the x loads of
-  //     step kt + 2;
-  //   sub-step 3: barrier, then read x fragments of step kt + 1 from the other
-  //     stage and dequantize its weights for sub-step 0, MFMAs of 3.
-  // The barrier orders every wave's store into the other stage (sub-step 0)
-  // before its reads, and every read of this stage (last issued in sub-step
-  // 2) before the next step's store into it.
-  uint4 pw[NF], pw_next[NF];
-  uint32_t sw[NF], sw_next[NF];
-  uint4 xa[XCH];
-  bf16x8_t a_buf[2][MI], b_buf[2][NF];
-  if (nsteps > 0) {
-    load_a(0, xa);
-    load_b(0, pw, sw);
-    store_a(0, xa);
-    load_a(1, xa);
-    __syncthreads();
-    read_a(s_a, 0, a_buf[0]);
-    dequant_b(0, 0, pw, sw, b_buf[0]);
-  }
-
-  for (int kt = 0; kt < nsteps; ++kt) {
-    const int stage = kt & 1;
-    load_b(kt + 1, pw_next, sw_next);
-    const uint16_t* sa = s_a + stage * kAStage;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int cur = s & 1, nxt = cur ^ 1;
-      if (s < 3) {
-        read_a(sa, s + 1, a_buf[nxt]);
-        dequant_b(kt, s + 1, pw, sw, b_buf[nxt]);
-      } else {
-        __syncthreads();
-        read_a(s_a + (stage ^ 1) * kAStage, 0, a_buf[nxt]);
-        dequant_b(kt + 1, 0, pw_next, sw_next, b_buf[nxt]);
-      }
-#pragma unroll
-      for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-          acc[mi][f] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_buf[cur][mi], b_buf[cur][f],
-                                                               acc[mi][f], 0, 0, 0);
-      if (s == 0) {
-        store_a(stage ^ 1, xa);
-        load_a(kt + 2, xa);
-        interleave_substep<0, MI * NF, kInterleaveV + 2, MI, XCH, XCH + NF * 2>();
-      } else {
-        interleave_substep<0, MI * NF, kInterleaveV, MI, 0, 0>();
-      }
-    }
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      pw[f] = pw_next[f];
-      sw[f] = sw_next[f];
-    }
-  }
-
-  // 32x32 accumulator layout: register e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
-  // column l%32.
-#pragma unroll
-  for (int f = 0; f < NF; ++f) {
-    const int col = brow[f];
-    const float bv = (bias && col < n) ? bias[col] : 0.0f;
-#pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = m0 + mx0 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-        if (row < m && col < n) store_y(y, y_bf16, (int64_t)row * n + col, acc[mi][f][e] + bv);
-      }
-  }
-}
-
-// Eight-wave tile with the weights staged through LDS.  Every two k steps the
-// block loads its 256 weight rows x 64 bytes of codes (and the two steps' sign
-// words) with loads in which each group of four lanes reads 64 contiguous
-// bytes, two steps before use, into one of two LDS stages of 80-byte row
-// records (codes of the two steps, then their sign words: a stride that keeps
-// the 32-row fragment reads below free of bank conflicts).  Wave w reads the
-// codes of its rows 32w .. 32w + 31 for a step with one ds_read_b128 and one
-// ds_read_b32 per lane.  Everything else is as in linear_mfma.
+// The weights are staged through LDS.  Every two k steps the block loads its
+// 256 weight rows x 64 bytes of codes (and the two steps' sign words) with
+// loads in which each group of four lanes reads 64 contiguous bytes, two steps
+// before use, into one of two LDS stages of 80-byte row records (codes of the
+// two steps, then their sign words: a stride that keeps the 32-row fragment
+// reads below free of bank conflicts).  Wave w reads the codes of its rows
+// 32w .. 32w + 31 for a step with one ds_read_b128 and one ds_read_b32 per
+// lane.  (Loading the B-operand layout straight from HBM made every dwordx4
+// touch 32 rows.)
 constexpr int kWRec = 20;  // uint32 per weight row record: 16 code words + 4 sign words
 
 //
@@ -747,18 +530,10 @@ hipError_t launch_linear_any(const uint16_t* x, const uint32_t* packed, const ui
                        sign, scale, scale16, bias, (int)m, (int)n, (int)k, lv, y, (int)y_bf16);
   } else {
     const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
-    if (GS > 0 || kWeightStage) {
-      auto kernel = (k % kTK) ? linear_mfma_ws<true, GS> : linear_mfma_ws<false, GS>;
-      hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream, x,
-                         packed, sign, scale, scale16, bias, (int)m, (int)n, (int)k,
-                         (int)tiles_m, lv, y, (int)y_bf16);
-    } else {
-      auto kernel = (k % kTK) ? linear_mfma<true, kMfmaWaves, kMfmaXSplit>
-                              : linear_mfma<false, kMfmaWaves, kMfmaXSplit>;
-      hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kMfmaWaves * kWave), 0,
-                         stream, x, packed, sign, scale, bias, (int)m, (int)n, (int)k,
-                         (int)tiles_m, lv, y, (int)y_bf16);
-    }
+    auto kernel = (k % kTK) ? linear_mfma_ws<true, GS> : linear_mfma_ws<false, GS>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream, x,
+                       packed, sign, scale, scale16, bias, (int)m, (int)n, (int)k, (int)tiles_m,
+                       lv, y, (int)y_bf16);
   }
   return hipGetLastError();
 }
