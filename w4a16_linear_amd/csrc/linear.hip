@@ -78,7 +78,9 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
     const uint16_t* __restrict__ scale16, const float* __restrict__ bias, int m, int n, int k,
     Levels lv, void* __restrict__ y, int y_bf16) {
   static_assert(GS == 0 || NMB <= 2, "the significand table and four x row blocks overfill LDS");
-  constexpr int CH = NMB == 4 ? 1 : 2;                  // k blocks per load batch
+  // One k block per load batch, two batches in flight: batches of two k
+  // blocks took 14 % longer at m = 32 (more registers, a later first MFMA).
+  constexpr int CH = 1;
   constexpr int kXRows = 16 * NMB;
   constexpr int kXLoads = kXRows / 4;                   // x loads per lane per k block
   constexpr int kStage = kXRows * kSkBlockK;            // bf16 per wave stage
