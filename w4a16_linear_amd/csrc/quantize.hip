@@ -372,14 +372,13 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
 // A block of 256 threads owns one row at a time: thread t holds elements
 // c*2048 + 8t .. c*2048 + 8t + 7 of chunk c (NCT chunks, k <= NCT * 2048), so a
 // wave's share of a row is a quarter of the one-wave-per-row kernel's and the
-// encode tail after the last load is short.  Blocks stay resident and stride
-// over rows; the next row's loads are issued before the current row is
-// encoded, into the other register buffer.  The row max meets in LDS behind a
+// encode tail after the last load is short.  Blocks stride over rows (the
+// grid is twice the resident count); the next row's loads are issued before
+// the current row is encoded, into the other register buffer.  The row max meets in LDS behind a
 // barrier that waits for LDS traffic only, so those loads stay in flight.
 
 constexpr int kBlockThreads = 256;
 constexpr int kBlockChunk = kBlockThreads * 8;  // elements per block-wide chunk
-constexpr int kPersistBlocks = 2048;
 
 // Store word `wi` of a row and, from the first lane of each quad, the sign word
 // wi / 4 made of the quad's four sign bytes.
@@ -660,8 +659,10 @@ hipError_t launch_block_rows(const T* w, int64_t n, int64_t k, const DecisionPoi
                              const BucketGrid& g, uint32_t* packed, uint32_t* sign, float* scale,
                              hipStream_t stream, const Levels* lv = nullptr,
                              double* row_sums = nullptr) {
-  int64_t blocks = resident_blocks<T, NCT, kErr>();
-  if (blocks > kPersistBlocks) blocks = kPersistBlocks;
+  // Twice the blocks that fit at once: the second half starts as the first
+  // finishes, which evens out the rows per block (15.8 -> 14.4 us for a
+  // 3840 x 3840 bf16 weight, no loss at 11520 rows).
+  int64_t blocks = 2 * resident_blocks<T, NCT, kErr>();
   if (blocks > n) blocks = n;
   Levels lvv{};
   if (lv) lvv = *lv;
@@ -1103,8 +1104,7 @@ hipError_t launch_bits_rows(const T* w, int64_t n, int64_t k, const DecisionPoin
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 1;
-  int64_t blocks = std::min<int64_t>((int64_t)per_cu * cus, kPersistBlocks);
-  blocks = std::min<int64_t>(blocks, n);
+  const int64_t blocks = std::min<int64_t>(2 * (int64_t)per_cu * cus, n);  // as launch_block_rows
   hipLaunchKernelGGL((quantize_bits_rows<T, NCT, B, kErr>), dim3((unsigned)blocks),
                      dim3(kBlockThreads), 0, stream, w, n, (int)k, dp, g, lv, packed, sign, scale,
                      row_sums);
