@@ -460,7 +460,9 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
     if (lane == 0) s_wmax[ms][wave] = mx;
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
-    mx = fmaxf(fmaxf(s_wmax[ms][0], s_wmax[ms][1]), fmaxf(s_wmax[ms][2], s_wmax[ms][3]));
+    mx = s_wmax[ms][0];
+#pragma unroll
+    for (int q = 1; q < kBlockThreads / kWave; ++q) mx = fmaxf(mx, s_wmax[ms][q]);
     if constexpr (kErr) flush_sums(ms ^ 1);
     const bool fast = mx >= 0x1p-125f && mx <= 0x1p125f;  // 1/m normal, u' <= 1 + ulps
     const float r = 1.0f / mx;
@@ -1027,7 +1029,9 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
     if (lane == 0) s_wmax[ms][wave] = mx;
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
-    mx = fmaxf(fmaxf(s_wmax[ms][0], s_wmax[ms][1]), fmaxf(s_wmax[ms][2], s_wmax[ms][3]));
+    mx = s_wmax[ms][0];
+#pragma unroll
+    for (int q = 1; q < kBlockThreads / kWave; ++q) mx = fmaxf(mx, s_wmax[ms][q]);
     if constexpr (kErr) flush_sums(ms ^ 1);
     const bool fast = mx >= 0x1p-125f && mx <= 0x1p125f;
     const float r = 1.0f / mx;
