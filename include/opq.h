@@ -11,7 +11,8 @@
  *   file list "opq_quantize.py (OPQLinear + replace_with_opq)": a linear layer
  *                                  that runs on the stored form.
  *
- * Format used by every call (the card leaves these open):
+ * Format of the main calls (the card leaves these open; the group-wise and
+ * other-width calls further down change only what they say they change):
  *   - one max per output row n, stored as float32 scale[n];
  *   - packed[n][k/8] (uint32): code of (n, k) in bits 4*(k%8) .. 4*(k%8)+3;
  *   - sign[n][k/32]  (uint32): bit k%32 is 1 exactly when w[n][k] < 0;

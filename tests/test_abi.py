@@ -229,3 +229,26 @@ def test_binding_refuses_host_tensors():
         opq.quantize(torch.zeros(4, 64), 0.73)
     with pytest.raises(ValueError):
         opq.quantize(torch.zeros(4, 64, dtype=torch.float16), 0.73)
+
+
+def test_host_tables_are_thread_safe():
+    """Many threads asking for many alphas at once (the per-alpha memo is the
+    library's only global state): every answer equals the single-threaded one."""
+    import threading
+    alphas = [0.3 + 0.05 * i for i in range(20)]
+    want = {a: opq.decision_points(a).tobytes() + opq.levels(a).tobytes() for a in alphas}
+    bad = []
+
+    def worker(seed):
+        rng = np.random.default_rng(seed)
+        for a in rng.choice(alphas, 200):
+            got = opq.decision_points(a).tobytes() + opq.levels(a).tobytes()
+            if got != want[a]:
+                bad.append(a)
+
+    threads = [threading.Thread(target=worker, args=(s,)) for s in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not bad

@@ -417,3 +417,34 @@ def test_error_sums_empty(gpu_lib):
     out = torch.full((7, 2), -1.0, dtype=torch.float64, device=DEV)
     assert np.all(opq.error_sums(z, 0.73, out=out).cpu().numpy() == 0.0)
     assert opq.error_sums(torch.empty((0, 64), dtype=torch.bfloat16, device=DEV), 0.73).shape == (0, 2)
+
+
+def test_concurrent_streams_different_alphas(gpu_lib):
+    """Calls with different alphas enqueued on two streams at once give the
+    results each gives alone (no state shared between calls)."""
+    opq = gpu_lib
+    _, w_dev = weight_tensor(WL.student_t(950, (512, 3840)), "bf16")
+    x = to_bf16(WL.normal(951, (200, 3840))).to(DEV)
+    ref = {}
+    for a in (0.45, 1.0):
+        qw = opq.quantize(w_dev, a)
+        ref[a] = (u32(qw.packed), opq.dequantize(qw, a).cpu(), opq.linear(x, qw, a).cpu(),
+                  opq.error_sums(w_dev, a).cpu())
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    outs = {}
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for a, s in zip((0.45, 1.0), streams):
+            with torch.cuda.stream(s):
+                qw = opq.quantize(w_dev, a)
+                ws = torch.zeros(max(opq.linear_workspace_bytes(200, 512, 3840), 16),
+                                 dtype=torch.uint8, device=DEV)
+                outs[a] = (qw, opq.dequantize(qw, a), opq.linear(x, qw, a, workspace=ws),
+                           opq.error_sums(w_dev, a))
+        torch.cuda.synchronize()
+        for a in (0.45, 1.0):
+            qw, d, y, e = outs[a]
+            assert np.array_equal(u32(qw.packed), ref[a][0])
+            assert torch.equal(d.cpu(), ref[a][1])
+            assert torch.equal(y.cpu(), ref[a][2])
+            assert torch.equal(e.cpu(), ref[a][3])
