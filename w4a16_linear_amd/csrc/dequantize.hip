@@ -62,21 +62,53 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void dequantize_rows(
 
 // Group-wise form.  The codes stream as one flat array; a lane decodes
 // kGWords consecutive packed words (8 kGWords codes, which lie in one group)
-// per chunk: it makes that group's table itself (make_row_lut with the
-// float16 max, the code index uniform so the levels stay in scalar
-// registers), then moves 4 kGWords bytes of codes and 16 kGWords of bf16.
-// Each wave takes kGUnroll chunks with all their loads in flight; there is no
-// LDS and no barrier, so the grid is simply one wave per kGUnroll chunks.
+// per chunk and moves 4 kGWords bytes of codes and 16 kGWords of bf16.  The
+// group's table bf16(G_q m16) is made by the group's lanes together: with
+// LG = GS / (8 kGWords) lanes per group, each makes 16 / LG entries (at least
+// a pair) from the levels in LDS, and the eight pair words are then gathered
+// to every lane of the group with ds_bpermute and cut into byte planes.  Each
+// wave takes kGUnroll chunks with all their loads in flight; the grid is one
+// wave per kGUnroll chunks.
 constexpr int kGThreads = 256;
 constexpr int kGUnroll = 2;
-constexpr int kGWords = 2;                   // packed words per lane per chunk
+constexpr int kGWords = 2;                    // packed words per lane per chunk
 constexpr int kGChunk = kWave * 8 * kGWords;  // elements per wave per chunk
+
+// Byte planes of the table of this lane's group: the group spans LG lanes
+// from `base`, its stored max is m16 (the same in all of them).
+template <int LG>
+__device__ __forceinline__ RowLut group_lut_shared(const double* s_g, float m16, int lane) {
+  constexpr int D = (16 / LG) / 2 > 0 ? (16 / LG) / 2 : 1;  // pair words per lane
+  constexpr int H = 8 / D;                                // lanes holding distinct words
+  const int j = lane % LG, base = lane - j;
+  const int slot = j % H;
+  const double m = (double)m16;
+  uint32_t mine[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    const int q = 2 * (D * slot + i);
+    mine[i] = bf16_rne_from_f64(s_g[q] * m) | (bf16_rne_from_f64(s_g[q + 1] * m) << 16);
+  }
+  uint32_t d[8];
+#pragma unroll
+  for (int w = 0; w < 8; ++w)
+    d[w] = (uint32_t)__builtin_amdgcn_ds_bpermute((base + w / D) * 4, (int)mine[w % D]);
+  RowLut t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t.lo[i] = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x06040200u);
+    t.hi[i] = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x07050301u);
+  }
+  return t;
+}
 
 template <int GS>
 __global__ __launch_bounds__(kGThreads) void dequantize_grouped_rows(
     const uint32_t* __restrict__ packed, const uint32_t* __restrict__ sign,
     const uint16_t* __restrict__ scale16, int64_t total, Levels lv, uint16_t* __restrict__ out) {
   static_assert(GS % (8 * kGWords) == 0, "a lane's codes lie in one group");
+  constexpr int LG = GS / (8 * kGWords);  // lanes per group
+  __shared__ double s_g[kLevels + 1];
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t wid = (int64_t)blockIdx.x * (kGThreads / kWave) + threadIdx.x / kWave;
   uint32_t wv[kGUnroll][kGWords], sv[kGUnroll], hv[kGUnroll];
@@ -96,11 +128,14 @@ __global__ __launch_bounds__(kGThreads) void dequantize_grouped_rows(
     sv[u] = valid ? sign[e0 >> 5] >> (kGWords == 4 ? 0 : 8 * ((e0 >> 3) & 3)) : 0u;
     hv[u] = valid ? scale16[e0 / GS] : 0u;
   }
+  if (threadIdx.x <= kLevels) s_g[threadIdx.x] = lv.g[threadIdx.x];
+  __syncthreads();
 #pragma unroll
   for (int u = 0; u < kGUnroll; ++u) {
     const int64_t e0 = (wid * kGUnroll + u) * kGChunk + lane * 8 * kGWords;
+    // every lane takes part in the gathers, valid or not
+    const RowLut t = group_lut_shared<LG>(s_g, f16_value(hv[u]), lane);
     if (e0 < total) {
-      const RowLut t = make_row_lut(lv, f16_value(hv[u]));
 #pragma unroll
       for (int j = 0; j < kGWords; ++j) {
         uint32_t o[4];
