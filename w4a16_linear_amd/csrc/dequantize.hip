@@ -11,6 +11,9 @@
 // the sign plane into 16 bytes of bfloat16 per 512-element chunk; the loads of
 // up to kGroup chunks are issued before any of them is decoded.  HBM traffic
 // is the algorithmic 0.625 B read + 2 B written per weight.
+//
+// Further down: the group-wise form (one float16 max per group of weights)
+// and 3/5/6-bit codes.
 #include "decode.hpp"
 #include "device_common.hpp"
 #include "group.hpp"

@@ -42,8 +42,10 @@ __device__ __forceinline__ void store_y(void* y, bool y_bf16, int64_t at, float 
 
 // ---------------------------------------------------------------- skinny path
 //
-// m <= 64: the product is bound by streaming the packed weights (0.625 bytes
-// per weight against 2 m flops).  A block owns 16 weight rows (one fragment of
+// m <= 64: few flops per weight byte (2 m flops against 0.625 bytes), so the
+// roofline is HBM; at these sizes the time goes to each wave's chain of k
+// blocks and the launch rather than to the loads.  A block owns 16 weight
+// rows (one fragment of
 // v_mfma_f32_16x16x32_bf16, W' the A operand, x^T the B operand) and all of k;
 // its eight waves take the 128-wide k blocks in turn and meet in LDS at the
 // end, so no partial sums leave the block.

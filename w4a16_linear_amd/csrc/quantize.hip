@@ -3,9 +3,14 @@
 //   m = max_k |w|;  u = fl32(|w| / m);  q = round(15 u^alpha);  s = [w < 0];
 //   packed nibbles eight per uint32, signs thirty-two per uint32.
 //
-// One wave owns one row.  The row is read from HBM once and held in VGPRs
-// while the wave reduces the max, so HBM traffic is the algorithmic
-// 2 B (bf16) read + 0.625 B written per weight.
+// A block of 256 threads owns one row at a time (one wave per row in the
+// kernels for rows longer than 16384).  The row is read from HBM once and held
+// in VGPRs while the max is reduced, so HBM traffic is the algorithmic 2 B
+// (bf16) read + 0.625 B written per weight.
+//
+// The file also holds the variants of the same encoder: the error sums of the
+// alpha sweep (codes reconstructed and compared instead of stored), the
+// group-wise form (a float16 max per group of weights) and 3/5/6-bit codes.
 //
 // Exact codes without a device pow: the host gives the binary32 decision
 // points T_k (code >= k  <=>  u >= T_k).  Positive binary32 values order like
