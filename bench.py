@@ -347,6 +347,7 @@ def main():
         "kernels": kern,
         "kernels_sum_us": round(sum(kk["us"] for kk in kern.values()), 3),
         "wall_s": round(wall, 3),
+        "env": run_env(dev),
     }
     if not args.no_cpu_baseline and bits == 4:
         import oracle as O
@@ -466,6 +467,17 @@ def model_pass(args, dev):
         return 10.0 * np.log10(num / den)
     snr = {a: snr_db(a) for a in (0.45, 0.73, 1.0)}
 
+    # the card's own stored form (a float16 max per 128 weights), same weights
+    def snr_grouped_db(a, gs=128):
+        num = den = 0.0
+        for w, (_, _, n, k) in zip(weights, shapes):
+            d = opq.dequantize(opq.quantize_grouped(w, a, gs), a, out=outs[(n, k)])
+            wf = w.float()
+            num += float(wf.double().square().sum())
+            den += float((wf - d.float()).double().square().sum())
+        return 10.0 * np.log10(num / den)
+    snr_g128 = {a: snr_grouped_db(a) for a in (0.45, 0.73, 1.0)}
+
     # alpha sweep: per-row error sums straight from the weights (nothing stored),
     # every layer at each alpha of the grid; timed per alpha.
     grid = [round(0.30 + 0.05 * i, 2) for i in range(15)]
@@ -536,12 +548,31 @@ def model_pass(args, dev):
         "kernels": kern,
         "snr_db": {str(a): round(v, 3) for a, v in snr.items()},
         "snr_gain_vs_alpha1_db": {str(a): round(v - snr[1.0], 3) for a, v in snr.items()},
+        "snr_db_groups_of_128": {str(a): round(v, 3) for a, v in snr_g128.items()},
+        "snr_gain_vs_alpha1_db_groups_of_128": {str(a): round(v - snr_g128[1.0], 3)
+                                                for a, v in snr_g128.items()},
         "alpha_sweep": sweep,
         "snr_by_width": widths,
         "wall_s": round(wall, 3),
+        "env": run_env(dev),
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
+
+
+def run_env(dev):
+    """What the numbers were measured on."""
+    import torch
+    prop = torch.cuda.get_device_properties(dev)
+    env = {"gpu": prop.name, "gcn_arch": getattr(prop, "gcnArchName", None),
+           "compute_units": prop.multi_processor_count,
+           "hip": torch.version.hip, "torch": torch.__version__}
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        env["rocm"] = None
+    return env
 
 
 def WL_title(name):
