@@ -128,39 +128,48 @@ def measured_traffic(kind, workload_name):
 
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(L, x_bits, w_vals, alpha, seconds, ideal_total_us, group=0):
+def cpu_baseline(L, x_bits, w_vals, alpha, seconds, ideal_total_us, group=0, threads=1):
     """The oracle, as it stands, over the whole workload, repeated until
-    `seconds` have passed (at least once); BLAS limited to one thread."""
+    `seconds` have passed (at least once).  threads = 1: one thread, BLAS
+    limited to one; threads > 1: the weight's rows split into that many
+    blocks run by a thread pool (NumPy releases the GIL), each block's BLAS
+    limited to one thread."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_limits
-        limiter = threadpool_limits(limits=1)
-    except Exception:  # pragma: no cover
-        limiter = None
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def block(rows):
+        w = w_vals[rows]
         if group:
-            p, s, m = O.quantize_grouped(w_vals, alpha, group)
+            p, s, m = O.quantize_grouped(w, alpha, group)
             d = O.dequantize_grouped(p, s, m, alpha, group)
         else:
-            p, s, m = O.quantize(w_vals, alpha)
+            p, s, m = O.quantize(w, alpha)
             d = O.dequantize(p, s, m, alpha)
-        O.linear(x_bits, d)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 20:
-            break
-    if limiter is not None:
-        limiter.unregister() if hasattr(limiter, "unregister") else None
+        return O.linear(x_bits, d)
+
+    blocks = [sl for sl in np.array_split(np.arange(L.n), threads) if len(sl)]
+    reps = 0
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=threads) as pool:
+        t0 = time.perf_counter()
+        while True:
+            list(pool.map(block, blocks))
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds or reps >= 20:
+                break
     per_step = el / reps
+    how = "one thread" if threads == 1 else f"{threads} threads over row blocks"
     return {
         "value": round(100.0 * ideal_total_us * 1e-6 / per_step, 6),
         "unit": "% of MI355X roofline",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
         "sample": f"{reps} full oracle step(s) (quantize, dequantize, linear) on the whole "
-                  f"{L.n}x{L.k} weight and x[{L.m},{L.k}], {el:.1f} s total, "
+                  f"{L.n}x{L.k} weight and x[{L.m},{L.k}], {how}, {el:.1f} s total, "
                   f"{per_step * 1e3:.1f} ms per step",
         "ms_per_step": round(per_step * 1e3, 3),
         "host_cpu": platform.processor() or platform.machine(),
@@ -356,6 +365,10 @@ def main():
               else w_host.numpy())
         out["cpu_baseline"] = cpu_baseline(L, xb, wv, alpha, args.cpu_seconds, ideal_total,
                                            group)
+        threads = min(os.cpu_count() or 1, 16)
+        if threads > 1:
+            out["cpu_baseline_pool"] = cpu_baseline(L, xb, wv, alpha, args.cpu_seconds,
+                                                    ideal_total, group, threads)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
