@@ -247,8 +247,13 @@ __device__ __forceinline__ uint32_t encode8_exact(const Slot<T>& s, float m, con
                                                   const float* pts) {
   uint32_t word = 0u;
 #pragma unroll
-  for (int i = 7; i >= 0; --i)
-    word = (word << 4) + code_exact(fabsf(s.at(i)), m, tab, shift, nbase, ulo, pts);
+  for (int i = 7; i >= 0; --i) {
+    // an opaque copy keeps |w| from being formed ahead of the branch (the fast
+    // path folds it into its multiply)
+    float v = s.at(i);
+    asm volatile("" : "+v"(v));
+    word = (word << 4) + code_exact(fabsf(v), m, tab, shift, nbase, ulo, pts);
+  }
   return word;
 }
 
@@ -278,12 +283,12 @@ template <typename T>
 __device__ __forceinline__ uint32_t encode_chunk(const Slot<T>& v, float mx, float r, bool fast,
                                                  const uint2* tab, int shift, uint32_t nbase,
                                                  float ulo, const float* pts) {
-  if (fast) {
-    uint32_t near;
-    const uint32_t word = encode8_fast(v, r, tab, shift, nbase, ulo, near);
-    if (near > 2u * kGuard) return word;
-  }
-  return encode8_exact(v, mx, tab, shift, nbase, ulo, pts);
+  // The fast encode runs on every chunk (with 1 standing in for 1/m where it
+  // does not apply), so the exact re-encode is the only branch.
+  uint32_t near;
+  uint32_t word = encode8_fast(v, fast ? r : 1.0f, tab, shift, nbase, ulo, near);
+  if (!fast || near <= 2u * kGuard) word = encode8_exact(v, mx, tab, shift, nbase, ulo, pts);
+  return word;
 }
 
 // Table kernel: blocks build the table, then each wave takes one row at a time
@@ -891,22 +896,25 @@ template <typename T>
 __device__ __forceinline__ void codes8(const Slot<T>& v, float mx, float r, bool fast,
                                        const uint2* tab, int shift, uint32_t nbase, float ulo,
                                        const float* pts, uint32_t (&q)[8]) {
-  uint32_t nr = 0u;
-  if (fast) {
-    nr = 0xFFFFFFFFu;
+  // As encode_chunk: the fast path runs everywhere, the exact one where flagged.
+  const float rf = fast ? r : 1.0f;
+  uint32_t nr = fast ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float up = __builtin_amdgcn_fmed3f(fabsf(v.at(i)) * r, ulo, 2.0f);
-      const uint32_t ub = __float_as_uint(up);
-      const uint2 e = table_at(tab, ub, shift, nbase);
-      const int d = (int)(ub + e.x);
-      q[i] = e.y + (d >= (int)kGuard ? 1u : 0u);
-      nr = min(nr, (uint32_t)d);
-    }
+  for (int i = 0; i < 8; ++i) {
+    const float up = __builtin_amdgcn_fmed3f(fabsf(v.at(i)) * rf, ulo, 2.0f);
+    const uint32_t ub = __float_as_uint(up);
+    const uint2 e = table_at(tab, ub, shift, nbase);
+    const int d = (int)(ub + e.x);
+    q[i] = e.y + (d >= (int)kGuard ? 1u : 0u);
+    nr = min(nr, (uint32_t)d);
   }
   if (nr <= 2u * kGuard) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = code_exact(fabsf(v.at(i)), mx, tab, shift, nbase, ulo, pts);
+    for (int i = 0; i < 8; ++i) {
+      float x = v.at(i);
+      asm volatile("" : "+v"(x));
+      q[i] = code_exact(fabsf(x), mx, tab, shift, nbase, ulo, pts);
+    }
   }
 }
 
