@@ -435,14 +435,14 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
   int64_t row = blockIdx.x;
   if (row < n) load_row(row, 0);
 
+  // No barrier here: the first row-max barrier below comes before any read
+  // of the table or the points.
   build_table(dp, g, s_tab);
   if (tid == 0) {
 #pragma unroll
     for (int j = 0; j < kLevels; ++j) s_pts[j] = dp.t[j];
     s_pts[kLevels] = 2.0f;
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the table is written
-  __builtin_amdgcn_s_barrier();
   const int shift = g.shift;
   const uint32_t nbase = (0u - (g.b0 >> g.shift)) << 3;
   const float ulo = __uint_as_float(g.b0);
@@ -1003,9 +1003,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
   if (kErr && tid <= L) s_g[tid] = lv.g[tid];
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
-  build_table_n(s_pts, L, g, s_tab);
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
+  build_table_n(s_pts, L, g, s_tab);  // read after the first row-max barrier
   const int shift = g.shift;
   const uint32_t nbase = (0u - (g.b0 >> g.shift)) << 3;
   const float ulo = __uint_as_float(g.b0);
