@@ -139,7 +139,11 @@ def test_grouped_near_decision_points(gpu_lib, alpha):
 @pytest.mark.parametrize("m,n,k,gs", [
     (1, 300, 512, 128), (8, 256, 256, 32), (16, 129, 96, 32), (32, 200, 768, 64),
     (33, 200, 768, 64), (64, 100, 1024, 256), (65, 96, 256, 128), (200, 300, 544, 32),
-    (256, 512, 1024, 128), (300, 260, 3840, 256), (130, 64, 192, 64)])
+    (256, 512, 1024, 128), (300, 260, 3840, 256), (130, 64, 192, 64),
+    # skinny blocks with 16 x k/gs group tables: one per thread of the block
+    # (made at block start), and more (rebuilt per k block)
+    (16, 50, 1024, 32), (40, 50, 8192, 256), (16, 50, 4096, 32), (8, 40, 8192, 128),
+    (33, 24, 4160, 32)])
 def test_grouped_linear_shapes(gpu_lib, m, n, k, gs):
     opq = gpu_lib
     w_vals, w_dev = weight_tensor(WL.student_t(1000 + n + gs, (n, k)), "bf16")

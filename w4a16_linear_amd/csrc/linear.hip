@@ -71,15 +71,22 @@ constexpr int kSkBlockK = 128;                  // k per wave step
 // banks.
 __device__ __forceinline__ int xs_off(int R, int c) { return R * kSkBlockK + ((c ^ (R & 15)) << 3); }
 
-// GS > 0: the group-wise form (group.hpp); the lane's table is rebuilt for
-// every k block from the LDS significand table and the group max of its part.
-template <int NMB, int GS>     // NMB: 16-row blocks of x (1, 2 or 4); GS: group or 0 (per row)
+// GS > 0: the group-wise form (group.hpp).  With kPre (the block's 16 x k/GS
+// groups are no more than its threads) each thread makes one group table at
+// block start, straight from the levels and the stored max, into LDS as byte
+// planes, group-major (a group's 16 rows adjacent, so a k block's reads hit 16
+// consecutive 32-byte records); a k block then costs a lane two ds_read_b128.
+// Otherwise the lane's table is rebuilt for every k block from the LDS
+// significand table and the group max of its part.
+constexpr int kSkPreGroups = kSkThreads;
+template <int NMB, int GS, bool kPre = false>  // NMB: 16-row blocks of x (1, 2 or 4); GS: group or 0 (per row)
 __global__ __launch_bounds__(kSkThreads) void linear_skinny(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
     const uint16_t* __restrict__ scale16, const float* __restrict__ bias, int m, int n, int k,
     Levels lv, void* __restrict__ y, int y_bf16) {
-  static_assert(GS == 0 || NMB <= 2, "the significand table and four x row blocks overfill LDS");
+  static_assert(GS == 0 || kPre || NMB <= 2, "the significand table and four x row blocks overfill LDS");
+  static_assert(!kPre || GS > 0, "tables made at block start are for the group-wise form");
   // One k block per load batch, two batches in flight: batches of two k
   // blocks took 14 % longer at m = 32 (more registers, a later first MFMA).
   constexpr int CH = 1;
@@ -90,7 +97,8 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   static_assert(kSkWaves * kOut * 4 <= kSkWaves * kStage * 2, "reduction fits the stages");
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kSkWaves * kStage];
   __shared__ uint32_t s_lut[GS ? 1 : kSkRows][8];
-  __shared__ __attribute__((aligned(16))) uint32_t s_mt[GS ? kMantissas * 8 : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t s_mt[(GS && !kPre) ? kMantissas * 8 : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t s_glut[kPre ? kSkPreGroups * 8 : 4];
   float* s_red = reinterpret_cast<float*>(s_x);         // after the k loop
 
   const int tid = threadIdx.x;
@@ -138,7 +146,7 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
       const uint32_t kx = (uint32_t)(kb + 8 * xc < k ? kb + 8 * xc : kb);
       wd[buf][j] = *reinterpret_cast<const uint4*>(pbase + p_off + kw / 2u);
       sw[buf][j] = *reinterpret_cast<const uint32_t*>(sbase + s_off + kw / 8u);
-      if constexpr (GS > 0) hv[buf][j] = hrow[min((kb + 32 * g) / GS, ngroups - 1)];
+      if constexpr (GS > 0 && !kPre) hv[buf][j] = hrow[min((kb + 32 * g) / GS, ngroups - 1)];
 #pragma unroll
       for (int i = 0; i < kXLoads; ++i)  // m <= 16: groups of 4 x rows wholly past m are skipped
         if (NMB > 1 || 4 * i < m) xv[buf][j][i] = *reinterpret_cast<const uint4*>(xbase + x_off[i] + kx * 2u);
@@ -152,7 +160,16 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   // Byte planes of the block's 16 row tables: wave w < 4 makes entries
   // 4w .. 4w+3 of row `lane` (a wave-uniform code, so the levels stay in
   // scalar registers).
-  if constexpr (GS > 0) build_mant_table(lv, s_mt);
+  if constexpr (GS > 0 && !kPre) build_mant_table(lv, s_mt);
+  if (kPre && tid < kSkRows * ngroups) {
+    // thread t: the table of group t / 16 of row n0 + t % 16 (all sixteen
+    // entries, each with a compile-time level index)
+    const float m16 = f16_value(scale16[(int64_t)min(n0 + (tid & (kSkRows - 1)), n - 1) * ngroups +
+                                        tid / kSkRows]);
+    const RowLut t = make_row_lut(lv, m16);
+    *reinterpret_cast<u32x4_t*>(&s_glut[8 * tid]) = u32x4_t{t.lo[0], t.lo[1], t.lo[2], t.lo[3]};
+    *reinterpret_cast<u32x4_t*>(&s_glut[8 * tid + 4]) = u32x4_t{t.hi[0], t.hi[1], t.hi[2], t.hi[3]};
+  }
   if (GS == 0 && wave < 4 && lane < kSkRows) {
     const float mr = scale[min(n0 + lane, n - 1)];
     uint32_t lo = 0u, hi = 0u;
@@ -202,7 +219,16 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
             (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)wd[buf][j].z),
             (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)wd[buf][j].w)};
         const uint32_t sb = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sw[buf][j]);
-        if constexpr (GS > 0) lut = group_lut(s_mt, hv[buf][j]);
+        if constexpr (kPre) {
+          // (the launcher picks kPre only when 16 * ngroups <= kSkPreGroups)
+          const int gidx = min(min((kb + 32 * g) / GS, ngroups - 1) * kSkRows + r, kSkPreGroups - 1);
+          const uint4 lo = *reinterpret_cast<const uint4*>(&s_glut[8 * gidx]);
+          const uint4 hi = *reinterpret_cast<const uint4*>(&s_glut[8 * gidx + 4]);
+          lut.lo[0] = lo.x; lut.lo[1] = lo.y; lut.lo[2] = lo.z; lut.lo[3] = lo.w;
+          lut.hi[0] = hi.x; lut.hi[1] = hi.y; lut.hi[2] = hi.z; lut.hi[3] = hi.w;
+        } else if constexpr (GS > 0) {
+          lut = group_lut(s_mt, hv[buf][j]);
+        }
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           uint32_t o[4];
@@ -515,21 +541,22 @@ hipError_t launch_linear_any(const uint16_t* x, const uint32_t* packed, const ui
                              bool y_bf16, hipStream_t stream) {
   if (m <= kSkinnyMaxM) {
     const int64_t blocks = (n + kSkRows - 1) / kSkRows;
-    if (GS > 0 && m > 32) {
+    // group tables made at block start when the block's groups fit
+    const bool pre = GS > 0 && kSkRows * (k / (GS ? GS : 1)) <= kSkPreGroups;
+    auto k2 = pre ? linear_skinny<2, GS, (GS > 0)> : linear_skinny<2, GS>;
+    if (GS > 0 && !pre && m > 32) {
       // The significand table leaves no room for four x row blocks: two
       // launches of up to 32 x rows each.
-      hipLaunchKernelGGL((linear_skinny<2, GS>), dim3((unsigned)blocks), dim3(kSkThreads), 0,
-                         stream, x, packed, sign, scale, scale16, bias, 32, (int)n, (int)k, lv, y,
-                         (int)y_bf16);
+      hipLaunchKernelGGL(k2, dim3((unsigned)blocks), dim3(kSkThreads), 0, stream, x, packed,
+                         sign, scale, scale16, bias, 32, (int)n, (int)k, lv, y, (int)y_bf16);
       const int64_t ybytes = y_bf16 ? 2 : 4;
-      hipLaunchKernelGGL((linear_skinny<2, GS>), dim3((unsigned)blocks), dim3(kSkThreads), 0,
-                         stream, x + 32 * k, packed, sign, scale, scale16, bias, (int)(m - 32),
-                         (int)n, (int)k, lv, static_cast<char*>(y) + 32 * n * ybytes,
-                         (int)y_bf16);
+      hipLaunchKernelGGL(k2, dim3((unsigned)blocks), dim3(kSkThreads), 0, stream, x + 32 * k,
+                         packed, sign, scale, scale16, bias, (int)(m - 32), (int)n, (int)k, lv,
+                         static_cast<char*>(y) + 32 * n * ybytes, (int)y_bf16);
       return hipGetLastError();
     }
-    auto kernel = m <= 16 ? linear_skinny<1, GS>
-                          : (m <= 32 ? linear_skinny<2, GS> : linear_skinny<(GS ? 2 : 4), GS>);
+    auto k1 = pre ? linear_skinny<1, GS, (GS > 0)> : linear_skinny<1, GS>;
+    auto kernel = m <= 16 ? k1 : (m <= 32 ? k2 : linear_skinny<4, GS, (GS > 0)>);
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kSkThreads), 0, stream, x, packed,
                        sign, scale, scale16, bias, (int)m, (int)n, (int)k, lv, y, (int)y_bf16);
   } else {
