@@ -408,7 +408,10 @@ __device__ __forceinline__ void store_word(uint32_t* prow, uint32_t* srow, int w
 // max is known) and write the row's (sum w^2, sum (w - w')^2): binary32 per lane
 // over its at most 64 elements and across the wave, then double across the
 // block's waves in a fixed order.
-template <typename T, int NCT, bool kErr>
+// kOne: the grid has a block per row, so there is no next row to prefetch and
+// one register buffer (8 fewer VGPRs for bfloat16 rows of two chunks, which
+// lets 8 instead of 7 blocks share a CU).
+template <typename T, int NCT, bool kErr, bool kOne = false>
 __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
     const T* __restrict__ w, int64_t n, int k, DecisionPoints dp, BucketGrid g,
     uint32_t* __restrict__ packed, uint32_t* __restrict__ sign, float* __restrict__ scale,
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
   const int wave = tid / kWave;
   const int64_t stride = gridDim.x;
 
-  Slot<T> v[2][NCT];
+  Slot<T> v[kOne ? 1 : 2][NCT];
   auto load_row = [&](int64_t rr, int buf) __attribute__((always_inline)) {
     const T* wr = w + rr * (int64_t)k;
 #pragma unroll
@@ -523,16 +526,20 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
     }
   };
 
-  // Rows alternate between the two buffers (register arrays need constant indices).
-  while (row < n) {
-    const int64_t r1 = row + stride;
-    if (r1 < n) load_row(r1, 1);
-    process(row, 0, 0);
-    if (r1 >= n) break;
-    const int64_t r2 = r1 + stride;
-    if (r2 < n) load_row(r2, 0);
-    process(r1, 1, 1);
-    row = r2;
+  if constexpr (kOne) {
+    if (row < n) process(row, 0, 0);
+  } else {
+    // Rows alternate between the two buffers (register arrays need constant indices).
+    while (row < n) {
+      const int64_t r1 = row + stride;
+      if (r1 < n) load_row(r1, 1);
+      process(row, 0, 0);
+      if (r1 >= n) break;
+      const int64_t r2 = r1 + stride;
+      if (r2 < n) load_row(r2, 0);
+      process(r1, 1, 1);
+      row = r2;
+    }
   }
   if constexpr (kErr) {
     // the last row's partials: which slot holds them follows the row count
@@ -650,11 +657,11 @@ hipError_t launch_rows(const T* w, int64_t n, int64_t k, const DecisionPoints& d
 // not exceed it: a block waiting for a slot would start only after another
 // block had finished all of its rows).  Per-CU occupancy is computed once per
 // kernel; the CU count is asked of the current device per call.
-template <typename T, int NCT, bool kErr>
+template <typename T, int NCT, bool kErr, bool kOne = false>
 int64_t resident_blocks() {
   static const int per_cu = [] {
     int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, quantize_block_rows<T, NCT, kErr>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, quantize_block_rows<T, NCT, kErr, kOne>,
                                                      kBlockThreads, 0) != hipSuccess || b < 1)
       b = 1;
     return b;
@@ -673,11 +680,17 @@ hipError_t launch_block_rows(const T* w, int64_t n, int64_t k, const DecisionPoi
                              double* row_sums = nullptr) {
   // Twice the blocks that fit at once: the second half starts as the first
   // finishes, which evens out the rows per block (15.8 -> 14.4 us for a
-  // 3840 x 3840 bf16 weight, no loss at 11520 rows).
-  int64_t blocks = 2 * resident_blocks<T, NCT, kErr>();
-  if (blocks > n) blocks = n;
+  // 3840 x 3840 bf16 weight, no loss at 11520 rows).  When that many blocks
+  // cover every row, a block per row without the prefetch buffer.
   Levels lvv{};
   if (lv) lvv = *lv;
+  if (n <= 2 * resident_blocks<T, NCT, kErr, true>()) {
+    hipLaunchKernelGGL((quantize_block_rows<T, NCT, kErr, true>), dim3((unsigned)n),
+                       dim3(kBlockThreads), 0, stream, w, n, (int)k, dp, g, packed, sign, scale,
+                       lvv, row_sums);
+    return hipGetLastError();
+  }
+  const int64_t blocks = 2 * resident_blocks<T, NCT, kErr>();
   hipLaunchKernelGGL((quantize_block_rows<T, NCT, kErr>), dim3((unsigned)blocks),
                      dim3(kBlockThreads), 0, stream, w, n, (int)k, dp, g, packed, sign, scale,
                      lvv, row_sums);
