@@ -170,7 +170,7 @@ size_t opq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *           one stream.  Calls that may run at the same time (other streams)
  *           need buffers of their own.
  * The sum order is fixed for a given shape, so results are reproducible bit
- * for bit.  k <= 65536.
+ * for bit.  k <= 65536 and n <= 2^26 (OPQ_ERR_UNSUPPORTED otherwise).
  * Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN,
  * OPQ_ERR_DTYPE, OPQ_ERR_WORKSPACE, OPQ_ERR_UNSUPPORTED, OPQ_ERR_HIP.
  */
@@ -268,7 +268,7 @@ int opq_dequantize_grouped(const uint32_t* packed, const uint32_t* sign, const u
  * The linear layer on the group-wise form: y = x W'^T (+ bias) with W' the
  * reconstruction opq_dequantize_grouped writes, made on chip; otherwise as
  * opq_linear (workspace sized by opq_linear_workspace_bytes, reproducible sum
- * order, k <= 65536).  Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA,
+ * order, k <= 65536, n <= 2^26).  Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA,
  * OPQ_ERR_ALIGN, OPQ_ERR_DTYPE, OPQ_ERR_WORKSPACE, OPQ_ERR_UNSUPPORTED,
  * OPQ_ERR_HIP.
  */

@@ -142,6 +142,8 @@ def test_linear_argument_checks(lib):
     assert call(m=0) == OK
     assert call(n=0) == OK
     assert call(m=0, yd=1) == OK
+    assert call(k=65536 + 32) == UNSUPPORTED
+    assert call(n=(1 << 26) + 1) == UNSUPPORTED   # past the skinny kernel's 32-bit grid
     assert lib.opq_linear_workspace_bytes(8, 16, 64) == opq.linear_workspace_bytes(8, 16, 64)
 
 
@@ -212,6 +214,7 @@ def test_grouped_argument_checks(lib):
     assert call(yd=2) == DTYPE
     assert call(a=100.0) == UNSUPPORTED
     assert call(k=65536 + 256, gs=256) == UNSUPPORTED
+    assert call(n=(1 << 26) + 1) == UNSUPPORTED
     assert call(m=0) == OK and call(n=0) == OK
 
 

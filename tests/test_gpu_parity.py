@@ -313,6 +313,37 @@ def test_linear_repeatable_and_bf16_out(gpu_lib, m, n, k):
     assert np.array_equal(bf16_bits(gb.t.cpu()), _bf16_rne_bits(y1))
 
 
+# ------------------------------------------------------------------ past one launch's grid
+
+def test_dequantize_rows_past_one_grid(gpu_lib):
+    """2^25 + 1000 rows of k = 32: the per-row and 3-bit dequantizers (a wave
+    per row segment) need two launches to stay within the 32-bit grid; rows on
+    both sides of the split against the oracle.  Weights drawn on the GPU."""
+    opq = gpu_lib
+    n, k = (1 << 25) + 1000, 32
+    g = torch.Generator(device=DEV)
+    g.manual_seed(2024)
+    w = (torch.randn((n, k), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    rows = np.array([0, 1, (1 << 25) - 2, (1 << 25) - 1, 1 << 25, (1 << 25) + 1, n - 1])
+    w_rows = bf16_bits(w[torch.from_numpy(rows).to(DEV)].cpu())
+    w_vals = (w_rows.astype(np.uint32) << 16).view(np.float32)
+    qw = opq.quantize(w, 0.73)
+    d = opq.dequantize(qw, 0.73)
+    idx = torch.from_numpy(rows).to(DEV)
+    ref = O.quantize(w_vals, 0.73)
+    torch.cuda.synchronize()
+    assert np.array_equal(u32(qw.packed[idx].cpu()), ref[0])
+    assert_dequant_close(bf16_bits(d[idx].cpu()), O.dequantize(*ref, 0.73), O.unpack(ref[0], ref[1])[0])
+    del qw, d
+    bw = opq.quantize_bits(w, 0.73, 3)
+    d = opq.dequantize(bw, 0.73)
+    ref = O.quantize_bits(w_vals, 0.73, 3)
+    torch.cuda.synchronize()
+    assert np.array_equal(u32(bw.packed[idx].cpu()), ref[0])
+    assert_dequant_close(bf16_bits(d[idx].cpu()), O.dequantize_bits(*ref, 0.73, 3),
+                         O.unpack_bits(ref[0], 3, k))
+
+
 # ------------------------------------------------------------------ full-size configs
 
 def _sample_rows(n, count, seed):

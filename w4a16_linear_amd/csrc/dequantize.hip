@@ -7,13 +7,17 @@
 // is then held as byte planes in registers and looked up with v_perm_b32
 // (decode.hpp).  Code 0 gives +0.0 whatever the sign bit.
 //
-// One wave per row.  A lane turns one packed word (eight codes) and a byte of
-// the sign plane into 16 bytes of bfloat16 per 512-element chunk; the loads of
-// up to kGroup chunks are issued before any of them is decoded.  HBM traffic
-// is the algorithmic 0.625 B read + 2 B written per weight.
+// One wave per row segment of up to kGroup 512-element chunks (a row of
+// k = 10240 is three segments), so every wave has all its loads in flight at
+// once and long rows still give many waves.  A lane turns one packed word
+// (eight codes) and a byte of the sign plane into 16 bytes of bfloat16 per
+// chunk; each wave makes its row's table.  HBM traffic is the algorithmic
+// 0.625 B read + 2 B written per weight.
 //
 // Further down: the group-wise form (one float16 max per group of weights)
 // and 3/5/6-bit codes.
+#include <algorithm>
+
 #include "decode.hpp"
 #include "device_common.hpp"
 #include "group.hpp"
@@ -25,40 +29,38 @@ constexpr int kRowsPerBlock = 4;
 constexpr int kChunk = kWave * 8;
 constexpr int kGroup = 8;  // chunks whose loads are in flight together
 
+// segs = segments per row (ceil(chunks / kGroup)); wave w of block b takes
+// segment (4b + w) % segs of row (4b + w) / segs.
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void dequantize_rows(
     const uint32_t* __restrict__ packed, const uint32_t* __restrict__ sign,
-    const float* __restrict__ scale, int64_t n, int k, Levels lv, uint16_t* __restrict__ out) {
+    const float* __restrict__ scale, int64_t n, int k, int segs, Levels lv,
+    uint16_t* __restrict__ out) {
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  const int64_t unit = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x / kWave);
+  const int64_t row = unit / segs;
   if (row >= n) return;  // whole waves leave; no block-wide barrier
+  const int c0 = (int)(unit - row * segs) * kGroup;  // first chunk of the segment
   const uint32_t* prow = packed + row * (int64_t)(k / 8);
   const uint32_t* srow = sign + row * (int64_t)(k / 32);
   uint16_t* orow = out + row * (int64_t)k;
-  const int nch = (k + kChunk - 1) / kChunk;
 
-  RowLut t;
-  for (int c0 = 0; c0 < nch; c0 += kGroup) {
-    uint32_t wv[kGroup], sv[kGroup];
+  uint32_t wv[kGroup], sv[kGroup];
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      const int e0 = (c0 + g) * kChunk + lane * 8;
-      const bool valid = e0 < k;
-      wv[g] = valid ? prow[e0 / 8] : 0u;
-      sv[g] = valid ? srow[e0 / 32] : 0u;
-    }
-    if (c0 == 0) {
-      // while the first loads are in flight: lane q makes L[q]
-      const uint32_t e = lut_entry(lv, lane & 15, scale[row]);
-      t = row_lut_from_lanes(e);
-    }
+  for (int g = 0; g < kGroup; ++g) {
+    const int e0 = (c0 + g) * kChunk + lane * 8;
+    const bool valid = e0 < k;
+    wv[g] = valid ? prow[e0 / 8] : 0u;
+    sv[g] = valid ? srow[e0 / 32] : 0u;
+  }
+  // while the loads are in flight: lane q makes L[q]
+  const RowLut t = row_lut_from_lanes(lut_entry(lv, lane & 15, scale[row]));
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      const int e0 = (c0 + g) * kChunk + lane * 8;
-      if (e0 < k) {
-        uint32_t o[4];
-        decode_word_ordered(wv[g], sv[g] >> (8 * (lane & 3)), t, o);
-        *reinterpret_cast<uint4*>(orow + e0) = make_uint4(o[0], o[1], o[2], o[3]);
-      }
+  for (int g = 0; g < kGroup; ++g) {
+    const int e0 = (c0 + g) * kChunk + lane * 8;
+    if (e0 < k) {
+      uint32_t o[4];
+      decode_word_ordered(wv[g], sv[g] >> (8 * (lane & 3)), t, o);
+      *reinterpret_cast<uint4*>(orow + e0) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }
@@ -151,11 +153,18 @@ __global__ __launch_bounds__(kGThreads) void dequantize_grouped_rows(
 
 template <int GS>
 hipError_t launch_grouped(const uint32_t* packed, const uint32_t* sign, const uint16_t* scale16,
-                          int64_t total, const Levels& lv, uint16_t* out, hipStream_t stream) {
+                          int64_t n, int64_t k, const Levels& lv, uint16_t* out,
+                          hipStream_t stream) {
   const int64_t per_block = (int64_t)kGChunk * kGUnroll * (kGThreads / kWave);
-  const int64_t blocks = (total + per_block - 1) / per_block;
-  hipLaunchKernelGGL((dequantize_grouped_rows<GS>), dim3((unsigned)blocks), dim3(kGThreads), 0,
-                     stream, packed, sign, scale16, total, lv, out);
+  const int64_t per_thread = per_block / kGThreads;
+  const int64_t max_rows = std::max<int64_t>(1, kMaxLaunchThreads * per_thread / k);
+  for (int64_t r0 = 0; r0 < n; r0 += max_rows) {  // groups never straddle rows
+    const int64_t total = std::min(max_rows, n - r0) * k;
+    const int64_t blocks = (total + per_block - 1) / per_block;
+    hipLaunchKernelGGL((dequantize_grouped_rows<GS>), dim3((unsigned)blocks), dim3(kGThreads), 0,
+                       stream, packed + r0 * (k / 8), sign + r0 * (k / 32),
+                       scale16 + r0 * (k / GS), total, lv, out + r0 * k);
+  }
   return hipGetLastError();
 }
 
@@ -222,22 +231,22 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void dequantize_bits_rows(
 hipError_t launch_dequantize_bits(const uint32_t* packed, const uint32_t* sign,
                                   const float* scale, int64_t n, int64_t k, int bits,
                                   const LevelsN& lv, uint16_t* out, hipStream_t stream) {
-  const int64_t blocks = (n + kRowsPerBlock - 1) / kRowsPerBlock;
-  switch (bits) {
-    case 3:
-      hipLaunchKernelGGL(dequantize_bits_rows<3>, dim3((unsigned)blocks), dim3(kRowsPerBlock * kWave),
-                         0, stream, packed, sign, scale, n, (int)k, lv, out);
-      break;
-    case 5:
-      hipLaunchKernelGGL(dequantize_bits_rows<5>, dim3((unsigned)blocks), dim3(kRowsPerBlock * kWave),
-                         0, stream, packed, sign, scale, n, (int)k, lv, out);
-      break;
-    case 6:
-      hipLaunchKernelGGL(dequantize_bits_rows<6>, dim3((unsigned)blocks), dim3(kRowsPerBlock * kWave),
-                         0, stream, packed, sign, scale, n, (int)k, lv, out);
-      break;
-    default:
-      return hipErrorInvalidValue;
+  if (bits != 3 && bits != 5 && bits != 6) return hipErrorInvalidValue;
+  const int64_t max_rows = kMaxLaunchThreads / kWave;  // a wave per row
+  for (int64_t r0 = 0; r0 < n; r0 += max_rows) {
+    const int64_t nr = std::min(max_rows, n - r0);
+    const int64_t blocks = (nr + kRowsPerBlock - 1) / kRowsPerBlock;
+    const uint32_t* p = packed + r0 * (k * bits / 32);
+    const uint32_t* sg = sign + r0 * (k / 32);
+    const float* sc = scale + r0;
+    uint16_t* o = out + r0 * k;
+    const dim3 grid((unsigned)blocks), block(kRowsPerBlock * kWave);
+    if (bits == 3)
+      hipLaunchKernelGGL(dequantize_bits_rows<3>, grid, block, 0, stream, p, sg, sc, nr, (int)k, lv, o);
+    else if (bits == 5)
+      hipLaunchKernelGGL(dequantize_bits_rows<5>, grid, block, 0, stream, p, sg, sc, nr, (int)k, lv, o);
+    else
+      hipLaunchKernelGGL(dequantize_bits_rows<6>, grid, block, 0, stream, p, sg, sc, nr, (int)k, lv, o);
   }
   return hipGetLastError();
 }
@@ -245,12 +254,11 @@ hipError_t launch_dequantize_bits(const uint32_t* packed, const uint32_t* sign,
 hipError_t launch_dequantize_grouped(const uint32_t* packed, const uint32_t* sign,
                                      const uint16_t* scale16, int64_t n, int64_t k, int gs,
                                      const Levels& lv, uint16_t* out, hipStream_t stream) {
-  const int64_t total = n * k;
   switch (gs) {
-    case 32: return launch_grouped<32>(packed, sign, scale16, total, lv, out, stream);
-    case 64: return launch_grouped<64>(packed, sign, scale16, total, lv, out, stream);
-    case 128: return launch_grouped<128>(packed, sign, scale16, total, lv, out, stream);
-    case 256: return launch_grouped<256>(packed, sign, scale16, total, lv, out, stream);
+    case 32: return launch_grouped<32>(packed, sign, scale16, n, k, lv, out, stream);
+    case 64: return launch_grouped<64>(packed, sign, scale16, n, k, lv, out, stream);
+    case 128: return launch_grouped<128>(packed, sign, scale16, n, k, lv, out, stream);
+    case 256: return launch_grouped<256>(packed, sign, scale16, n, k, lv, out, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -258,9 +266,16 @@ hipError_t launch_dequantize_grouped(const uint32_t* packed, const uint32_t* sig
 hipError_t launch_dequantize(const uint32_t* packed, const uint32_t* sign, const float* scale,
                              int64_t n, int64_t k, const Levels& lv, uint16_t* out,
                              hipStream_t stream) {
-  const int64_t blocks = (n + kRowsPerBlock - 1) / kRowsPerBlock;
-  hipLaunchKernelGGL(dequantize_rows, dim3((unsigned)blocks), dim3(kRowsPerBlock * kWave), 0,
-                     stream, packed, sign, scale, n, (int)k, lv, out);
+  const int64_t nch = (k + kChunk - 1) / kChunk;
+  const int64_t segs = nch > 0 ? (nch + kGroup - 1) / kGroup : 1;
+  const int64_t max_rows = kMaxLaunchThreads / kWave / segs;  // a wave per segment
+  for (int64_t r0 = 0; r0 < n; r0 += max_rows) {
+    const int64_t nr = std::min(max_rows, n - r0);
+    const int64_t blocks = (nr * segs + kRowsPerBlock - 1) / kRowsPerBlock;
+    hipLaunchKernelGGL(dequantize_rows, dim3((unsigned)blocks), dim3(kRowsPerBlock * kWave), 0,
+                       stream, packed + r0 * (k / 8), sign + r0 * (k / 32), scale + r0, nr,
+                       (int)k, (int)segs, lv, out + r0 * k);
+  }
   return hipGetLastError();
 }
 

@@ -12,6 +12,8 @@
 namespace {
 
 constexpr int64_t kMaxK = 65536;
+// the skinny linear kernel takes a block of 512 threads per 16 weight rows
+constexpr int64_t kMaxLinearN = int64_t(1) << 26;
 
 // NULL (allowed for an empty array) counts as aligned.
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -144,7 +146,7 @@ int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign, 
   const size_t need = opq::linear_workspace_bytes(m, n, k);
   if (workspace_bytes < need || (need > 0 && !workspace)) return OPQ_ERR_WORKSPACE;
   if (m == 0 || n == 0) return OPQ_OK;
-  if (k > kMaxK) return OPQ_ERR_UNSUPPORTED;
+  if (k > kMaxK || n > kMaxLinearN) return OPQ_ERR_UNSUPPORTED;
   opq::Levels lv;
   opq::levels(alpha, lv.g);
   return hip_status(opq::launch_linear(x, packed, sign, scale, bias, m, n, k, lv, y,
@@ -263,7 +265,7 @@ int opq_linear_grouped(const uint16_t* x, const uint32_t* packed, const uint32_t
   const size_t need = opq::linear_workspace_bytes(m, n, k);
   if (workspace_bytes < need || (need > 0 && !workspace)) return OPQ_ERR_WORKSPACE;
   if (m == 0 || n == 0) return OPQ_OK;
-  if (k > kMaxK) return OPQ_ERR_UNSUPPORTED;
+  if (k > kMaxK || n > kMaxLinearN) return OPQ_ERR_UNSUPPORTED;
   opq::DecisionPoints dp;
   if (!opq::decision_points(alpha, dp.t)) return OPQ_ERR_ALPHA;
   opq::Levels lv;

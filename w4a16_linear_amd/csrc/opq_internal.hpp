@@ -9,6 +9,10 @@ namespace opq {
 
 constexpr int kLevels = 15;  // 4-bit magnitude codes 0..15
 
+// A launch's grid counts work-items in 32 bits; launchers whose grid grows with
+// the rows split larger inputs into launches of at most this many.
+constexpr int64_t kMaxLaunchThreads = int64_t(1) << 31;
+
 // Decision points T_k (k = 1..15) of round(15 u^alpha), passed by value.
 struct DecisionPoints {
   float t[kLevels];

@@ -825,29 +825,37 @@ __global__ __launch_bounds__(kGThreads) void quantize_grouped_rows(
 }
 
 template <typename T, int GS>
-hipError_t launch_grouped_rows(const T* w, int64_t total, const DecisionPoints& dp,
+hipError_t launch_grouped_rows(const T* w, int64_t n, int64_t k, const DecisionPoints& dp,
                                const BucketGrid& g, uint32_t* packed, uint32_t* sign,
                                uint16_t* scale16, hipStream_t stream) {
   // One batch per wave: with the grid capped at the resident block count (and
   // the waves looping), a 11520 x 3840 weight took 35.9 us instead of 32.2.
-  const int64_t batches = (total + (int64_t)kChunk * kGUnroll - 1) / ((int64_t)kChunk * kGUnroll);
-  const int64_t blocks = (batches + kGWaves - 1) / kGWaves;
-  hipLaunchKernelGGL((quantize_grouped_rows<T, GS>), dim3((unsigned)blocks), dim3(kGThreads), 0,
-                     stream, w, total, dp, g, packed, sign, scale16);
+  // Inputs past the 32-bit grid go in several launches of whole rows (groups
+  // never straddle rows).
+  const int64_t per_batch = (int64_t)kChunk * kGUnroll;
+  const int64_t max_rows = std::max<int64_t>(1, kMaxLaunchThreads / kWave * per_batch / k);
+  for (int64_t r0 = 0; r0 < n; r0 += max_rows) {
+    const int64_t total = std::min(max_rows, n - r0) * k;
+    const int64_t batches = (total + per_batch - 1) / per_batch;
+    const int64_t blocks = (batches + kGWaves - 1) / kGWaves;
+    hipLaunchKernelGGL((quantize_grouped_rows<T, GS>), dim3((unsigned)blocks), dim3(kGThreads), 0,
+                       stream, w + r0 * k, total, dp, g, packed + r0 * (k / 8),
+                       sign + r0 * (k / 32), scale16 + r0 * (k / GS));
+  }
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t dispatch_grouped(const T* w, int64_t total, int gs, const DecisionPoints& dp,
+hipError_t dispatch_grouped(const T* w, int64_t n, int64_t k, int gs, const DecisionPoints& dp,
                             uint32_t* packed, uint32_t* sign, uint16_t* scale16,
                             hipStream_t stream) {
   BucketGrid g;
   if (!bucket_grid(dp, g)) return hipErrorNotSupported;
   switch (gs) {
-    case 32: return launch_grouped_rows<T, 32>(w, total, dp, g, packed, sign, scale16, stream);
-    case 64: return launch_grouped_rows<T, 64>(w, total, dp, g, packed, sign, scale16, stream);
-    case 128: return launch_grouped_rows<T, 128>(w, total, dp, g, packed, sign, scale16, stream);
-    case 256: return launch_grouped_rows<T, 256>(w, total, dp, g, packed, sign, scale16, stream);
+    case 32: return launch_grouped_rows<T, 32>(w, n, k, dp, g, packed, sign, scale16, stream);
+    case 64: return launch_grouped_rows<T, 64>(w, n, k, dp, g, packed, sign, scale16, stream);
+    case 128: return launch_grouped_rows<T, 128>(w, n, k, dp, g, packed, sign, scale16, stream);
+    case 256: return launch_grouped_rows<T, 256>(w, n, k, dp, g, packed, sign, scale16, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1212,9 +1220,9 @@ hipError_t launch_quantize_grouped(const void* w, bool w_is_bf16, int64_t n, int
                                    const DecisionPoints& dp, uint32_t* packed, uint32_t* sign,
                                    uint16_t* scale16, hipStream_t stream) {
   if (w_is_bf16)
-    return dispatch_grouped(static_cast<const uint16_t*>(w), n * k, gs, dp, packed, sign, scale16,
+    return dispatch_grouped(static_cast<const uint16_t*>(w), n, k, gs, dp, packed, sign, scale16,
                             stream);
-  return dispatch_grouped(static_cast<const float*>(w), n * k, gs, dp, packed, sign, scale16,
+  return dispatch_grouped(static_cast<const float*>(w), n, k, gs, dp, packed, sign, scale16,
                           stream);
 }
 
