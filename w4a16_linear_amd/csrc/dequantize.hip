@@ -168,8 +168,8 @@ hipError_t launch_grouped(const uint32_t* packed, const uint32_t* sign, const ui
   return hipGetLastError();
 }
 
-// b-bit codes (3, 5 or 6 bits; 2^b - 1 levels).  One wave per row as in
-// dequantize_rows; the row's table L[q] = bf16(G_q m), q = 0 .. 2^b - 1, sits
+// b-bit codes (3, 5 or 6 bits; 2^b - 1 levels).  One wave per row segment as
+// in dequantize_rows; the row's table L[q] = bf16(G_q m), q = 0 .. 2^b - 1, sits
 // in the wave's LDS slot (lane q makes entry q from the levels, which the block
 // copies to LDS once).  A lane decodes eight codes per 512-element chunk: its
 // 8b bits of the row's bit stream start at bit 8b (lane + 64 c), a multiple of
@@ -177,7 +177,8 @@ hipError_t launch_grouped(const uint32_t* packed, const uint32_t* sign, const ui
 template <int B>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void dequantize_bits_rows(
     const uint32_t* __restrict__ packed, const uint32_t* __restrict__ sign,
-    const float* __restrict__ scale, int64_t n, int k, LevelsN lv, uint16_t* __restrict__ out) {
+    const float* __restrict__ scale, int64_t n, int k, int segs, LevelsN lv,
+    uint16_t* __restrict__ out) {
   constexpr int L = (1 << B) - 1;
   __shared__ double s_g[L + 1];
   __shared__ uint32_t s_lut[kRowsPerBlock][L + 1];
@@ -185,43 +186,42 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void dequantize_bits_rows(
   const int wave = threadIdx.x / kWave;
   if (threadIdx.x <= L) s_g[threadIdx.x] = lv.g[threadIdx.x];
   __syncthreads();  // every wave passes here before any leaves
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + wave;
+  const int64_t unit = (int64_t)blockIdx.x * kRowsPerBlock + wave;  // row segment, as in dequantize_rows
+  const int64_t row = unit / segs;
   if (row >= n) return;
+  const int c0 = (int)(unit - row * segs) * kGroup;
   if (lane <= L) s_lut[wave][lane] = bf16_rne_from_f64(s_g[lane] * (double)scale[row]);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // one wave's LDS ops complete in order
   const int nwords = k / 32 * B;
   const uint32_t* prow = packed + row * (int64_t)nwords;
   const uint32_t* srow = sign + row * (int64_t)(k / 32);
   uint16_t* orow = out + row * (int64_t)k;
-  const int nch = (k + kChunk - 1) / kChunk;
-  for (int c0 = 0; c0 < nch; c0 += kGroup) {
-    uint32_t w0[kGroup], w1[kGroup], sv[kGroup];
+  uint32_t w0[kGroup], w1[kGroup], sv[kGroup];
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      const int e0 = (c0 + g) * kChunk + lane * 8;
-      const bool valid = e0 < k;
-      const int wi = (e0 * B) >> 5;
-      w0[g] = valid ? prow[wi] : 0u;
-      w1[g] = valid ? prow[min(wi + 1, nwords - 1)] : 0u;  // past the row only when unused
-      sv[g] = valid ? srow[e0 / 32] : 0u;
-    }
+  for (int g = 0; g < kGroup; ++g) {
+    const int e0 = (c0 + g) * kChunk + lane * 8;
+    const bool valid = e0 < k;
+    const int wi = (e0 * B) >> 5;
+    w0[g] = valid ? prow[wi] : 0u;
+    w1[g] = valid ? prow[min(wi + 1, nwords - 1)] : 0u;  // past the row only when unused
+    sv[g] = valid ? srow[e0 / 32] : 0u;
+  }
 #pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      const int e0 = (c0 + g) * kChunk + lane * 8;
-      if (e0 < k) {
-        const uint64_t f = (((uint64_t)w1[g] << 32) | w0[g]) >> ((e0 * B) & 31);
-        const uint32_t sb = sv[g] >> (8 * (lane & 3));
-        uint32_t o[4];
+  for (int g = 0; g < kGroup; ++g) {
+    const int e0 = (c0 + g) * kChunk + lane * 8;
+    if (e0 < k) {
+      const uint64_t f = (((uint64_t)w1[g] << 32) | w0[g]) >> ((e0 * B) & 31);
+      const uint32_t sb = sv[g] >> (8 * (lane & 3));
+      uint32_t o[4];
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          const uint32_t q0 = (uint32_t)(f >> (B * i)) & L, q1 = (uint32_t)(f >> (B * (i + 1))) & L;
-          uint32_t v0 = s_lut[wave][q0], v1 = s_lut[wave][q1];
-          if (((sb >> i) & 1u) && q0) v0 |= 0x8000u;
-          if (((sb >> (i + 1)) & 1u) && q1) v1 |= 0x8000u;
-          o[i / 2] = v0 | (v1 << 16);
-        }
-        *reinterpret_cast<uint4*>(orow + e0) = make_uint4(o[0], o[1], o[2], o[3]);
+      for (int i = 0; i < 8; i += 2) {
+        const uint32_t q0 = (uint32_t)(f >> (B * i)) & L, q1 = (uint32_t)(f >> (B * (i + 1))) & L;
+        uint32_t v0 = s_lut[wave][q0], v1 = s_lut[wave][q1];
+        if (((sb >> i) & 1u) && q0) v0 |= 0x8000u;
+        if (((sb >> (i + 1)) & 1u) && q1) v1 |= 0x8000u;
+        o[i / 2] = v0 | (v1 << 16);
       }
+      *reinterpret_cast<uint4*>(orow + e0) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }
@@ -232,21 +232,23 @@ hipError_t launch_dequantize_bits(const uint32_t* packed, const uint32_t* sign,
                                   const float* scale, int64_t n, int64_t k, int bits,
                                   const LevelsN& lv, uint16_t* out, hipStream_t stream) {
   if (bits != 3 && bits != 5 && bits != 6) return hipErrorInvalidValue;
-  const int64_t max_rows = kMaxLaunchThreads / kWave;  // a wave per row
+  const int64_t nch = (k + kChunk - 1) / kChunk;
+  const int segs = (int)(nch > 0 ? (nch + kGroup - 1) / kGroup : 1);
+  const int64_t max_rows = kMaxLaunchThreads / kWave / segs;  // a wave per row segment
   for (int64_t r0 = 0; r0 < n; r0 += max_rows) {
     const int64_t nr = std::min(max_rows, n - r0);
-    const int64_t blocks = (nr + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int64_t blocks = (nr * segs + kRowsPerBlock - 1) / kRowsPerBlock;
     const uint32_t* p = packed + r0 * (k * bits / 32);
     const uint32_t* sg = sign + r0 * (k / 32);
     const float* sc = scale + r0;
     uint16_t* o = out + r0 * k;
     const dim3 grid((unsigned)blocks), block(kRowsPerBlock * kWave);
     if (bits == 3)
-      hipLaunchKernelGGL(dequantize_bits_rows<3>, grid, block, 0, stream, p, sg, sc, nr, (int)k, lv, o);
+      hipLaunchKernelGGL(dequantize_bits_rows<3>, grid, block, 0, stream, p, sg, sc, nr, (int)k, segs, lv, o);
     else if (bits == 5)
-      hipLaunchKernelGGL(dequantize_bits_rows<5>, grid, block, 0, stream, p, sg, sc, nr, (int)k, lv, o);
+      hipLaunchKernelGGL(dequantize_bits_rows<5>, grid, block, 0, stream, p, sg, sc, nr, (int)k, segs, lv, o);
     else
-      hipLaunchKernelGGL(dequantize_bits_rows<6>, grid, block, 0, stream, p, sg, sc, nr, (int)k, lv, o);
+      hipLaunchKernelGGL(dequantize_bits_rows<6>, grid, block, 0, stream, p, sg, sc, nr, (int)k, segs, lv, o);
   }
   return hipGetLastError();
 }
