@@ -384,8 +384,10 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
 // wave's share of a row is a quarter of the one-wave-per-row kernel's and the
 // encode tail after the last load is short.  Blocks stride over rows (the
 // grid is twice the resident count); the next row's loads are issued before
-// the current row is encoded, into the other register buffer.  The row max meets in LDS behind a
-// barrier that waits for LDS traffic only, so those loads stay in flight.
+// the current row is encoded, into the other register buffer.  When that grid
+// covers every row, each block takes one row and keeps no second buffer.  The
+// row max meets in LDS behind a barrier that waits for LDS traffic only, so
+// those loads stay in flight.
 
 constexpr int kBlockThreads = 256;
 constexpr int kBlockChunk = kBlockThreads * 8;  // elements per block-wide chunk
