@@ -365,6 +365,8 @@ def main():
               else w_host.numpy())
         out["cpu_baseline"] = cpu_baseline(L, xb, wv, alpha, args.cpu_seconds, ideal_total,
                                            group)
+        # with the CPU baseline (the default run; profiled runs skip both)
+        out["env"]["gfx_clock_under_load"] = gfx_clock_under_load(step)
         threads = min(os.cpu_count() or 1, 16)
         if threads > 1:
             out["cpu_baseline_pool"] = cpu_baseline(L, xb, wv, alpha, args.cpu_seconds,
@@ -571,6 +573,53 @@ def model_pass(args, dev):
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
+
+
+def gfx_clock_under_load(step, seconds=1.0):
+    """Shader clock while the step repeats: the per-XCD gfx clocks from
+    `amd-smi metric --clock` (else rocm-smi's sclk), sampled once the load has
+    run for half the time.  None when neither tool answers."""
+    import subprocess
+    import threading
+
+    import torch
+    done = threading.Event()
+
+    def spin():
+        i = 0
+        while not done.is_set():
+            for _ in range(64):
+                step(i)
+                i += 1
+            torch.cuda.synchronize()
+
+    t = threading.Thread(target=spin, daemon=True)
+    t.start()
+    time.sleep(seconds / 2)
+    res = None
+    try:
+        r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        d = json.loads(r.stdout)
+        d = d["gpu_data"] if isinstance(d, dict) else d
+        mhz = [v["clk"]["value"] for kk, v in d[0]["clock"].items() if kk.startswith("gfx_")]
+        if mhz:
+            res = {"tool": "amd-smi", "gfx_mhz_mean": round(sum(mhz) / len(mhz), 1),
+                   "gfx_mhz_min": min(mhz), "gfx_mhz_max": max(mhz), "domains": len(mhz)}
+    except Exception:  # noqa: BLE001 - a missing or changed tool only loses this field
+        res = None
+    if res is None:
+        try:
+            r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                               text=True, timeout=30)
+            card = next(iter(json.loads(r.stdout).values()))
+            v = card.get("sclk clock speed:", "")
+            res = {"tool": "rocm-smi", "sclk_mhz": float(v.strip("()Mhz"))}
+        except Exception:  # noqa: BLE001
+            res = None
+    done.set()
+    t.join()
+    return res
 
 
 def run_env(dev):
