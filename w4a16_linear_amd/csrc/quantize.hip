@@ -784,18 +784,17 @@ __global__ __launch_bounds__(kGThreads) void quantize_grouped_rows(
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t nchunks = (total + kChunk - 1) / kChunk;
   const int64_t wid = (int64_t)blockIdx.x * kGWaves + threadIdx.x / kWave;
-  const int64_t step = (int64_t)gridDim.x * kGWaves * kGUnroll;
 
-  Slot<T> v[2][kGUnroll];
-  auto load = [&](int64_t cb, int buf) __attribute__((always_inline)) {
+  // The grid has one batch of kGUnroll chunks per wave.
+  Slot<T> v[kGUnroll];
+  const int64_t cb = wid * kGUnroll;  // first chunk of this wave's batch
+  if (cb < nchunks) {
 #pragma unroll
     for (int u = 0; u < kGUnroll; ++u) {
       const int64_t e0 = (cb + u) * kChunk + lane * 8;
-      if (e0 < total) v[buf][u].load(w + e0); else v[buf][u].zero();
+      if (e0 < total) v[u].load(w + e0); else v[u].zero();
     }
-  };
-  int64_t cb = wid * kGUnroll;  // first chunk of this wave's batch
-  if (cb < nchunks) load(cb, 0);
+  }
 
   build_table(dp, g, s_tab);
   if (threadIdx.x == 0) {
@@ -809,34 +808,22 @@ __global__ __launch_bounds__(kGThreads) void quantize_grouped_rows(
   const uint32_t nbase = (0u - (g.b0 >> g.shift)) << 3;
   const float ulo = __uint_as_float(g.b0);
 
-  auto process = [&](int64_t c, int buf) __attribute__((always_inline)) {
+  if (cb >= nchunks) return;  // after the barrier: the block's table is shared
 #pragma unroll
-    for (int u = 0; u < kGUnroll; ++u) {
-      const int64_t e0 = (c + u) * kChunk + lane * 8;
-      const bool valid = e0 < total;
-      float mx = slot_absmax(v[buf][u]);
+  for (int u = 0; u < kGUnroll; ++u) {
+    const int64_t e0 = (cb + u) * kChunk + lane * 8;
+    const bool valid = e0 < total;
+    float mx = slot_absmax(v[u]);
 #pragma unroll
-      for (int off = 1; off < kLanes; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
-      const uint32_t h = f16_bits_rn(mx);
-      const float m16 = f16_value(h);
-      const bool fast = m16 > 0.0f;
-      const float r = fast ? 1.0f / m16 : 0.0f;
-      const uint32_t word = encode_chunk(v[buf][u], m16, r, fast, s_tab, shift, nbase, ulo, s_pts);
-      const int64_t wi = valid ? (e0 >> 3) : 0;
-      store_word(packed + wi, sign + (wi >> 2), 0, lane, valid, word, sign_byte(v[buf][u]));
-      if (valid && lane % kLanes == 0) scale16[e0 / GS] = (uint16_t)h;
-    }
-  };
-
-  while (cb < nchunks) {
-    const int64_t c1 = cb + step;
-    if (c1 < nchunks) load(c1, 1);
-    process(cb, 0);
-    if (c1 >= nchunks) break;
-    const int64_t c2 = c1 + step;
-    if (c2 < nchunks) load(c2, 0);
-    process(c1, 1);
-    cb = c2;
+    for (int off = 1; off < kLanes; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off, kWave));
+    const uint32_t h = f16_bits_rn(mx);
+    const float m16 = f16_value(h);
+    const bool fast = m16 > 0.0f;
+    const float r = fast ? 1.0f / m16 : 0.0f;
+    const uint32_t word = encode_chunk(v[u], m16, r, fast, s_tab, shift, nbase, ulo, s_pts);
+    const int64_t wi = valid ? (e0 >> 3) : 0;
+    store_word(packed + wi, sign + (wi >> 2), 0, lane, valid, word, sign_byte(v[u]));
+    if (valid && lane % kLanes == 0) scale16[e0 / GS] = (uint16_t)h;
   }
 }
 
