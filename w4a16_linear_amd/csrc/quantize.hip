@@ -33,6 +33,7 @@
 #include "group.hpp"
 
 #include <algorithm>
+#include <atomic>
 
 namespace opq {
 namespace {
@@ -990,14 +991,19 @@ __device__ __forceinline__ void store_bits(uint32_t* prow, uint32_t* srow, int b
   }
 }
 
-template <typename T, int NCT, int B, bool kErr>
+// The bucket table sits in dynamic LDS sized to the grid's g.nb entries (for
+// alpha = 0.73: 52, 149 and 342 for 3, 5 and 6 bits, against kMaxBucketsN),
+// so the table does not cap the blocks per CU.  kOne as in quantize_block_rows.
+extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
+
+template <typename T, int NCT, int B, bool kErr, bool kOne = false>
 __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
     const T* __restrict__ w, int64_t n, int k, DecisionPointsN dp, BucketGrid g, LevelsN lv,
     uint32_t* __restrict__ packed, uint32_t* __restrict__ sign, float* __restrict__ scale,
     double* __restrict__ row_sums) {
   constexpr int L = (1 << B) - 1;
   constexpr int kWaves = kBlockThreads / kWave;
-  __shared__ uint2 s_tab[kMaxBucketsN];
+  uint2* s_tab = reinterpret_cast<uint2*>(dyn_lds);
   __shared__ float s_pts[kMaxLevels + 1];
   __shared__ double s_g[kMaxLevels + 1];
   __shared__ float s_wmax[2][kWaves];
@@ -1008,7 +1014,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
   const int wave = tid / kWave;
   const int64_t stride = gridDim.x;
 
-  Slot<T> v[2][NCT];
+  Slot<T> v[kOne ? 1 : 2][NCT];
   auto load_row = [&](int64_t rr, int buf) __attribute__((always_inline)) {
     const T* wr = w + rr * (int64_t)k;
 #pragma unroll
@@ -1099,15 +1105,19 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
     }
   };
 
-  while (row < n) {
-    const int64_t r1 = row + stride;
-    if (r1 < n) load_row(r1, 1);
-    process(row, 0, 0);
-    if (r1 >= n) break;
-    const int64_t r2 = r1 + stride;
-    if (r2 < n) load_row(r2, 0);
-    process(r1, 1, 1);
-    row = r2;
+  if constexpr (kOne) {
+    if (row < n) process(row, 0, 0);
+  } else {
+    while (row < n) {
+      const int64_t r1 = row + stride;
+      if (r1 < n) load_row(r1, 1);
+      process(row, 0, 0);
+      if (r1 >= n) break;
+      const int64_t r2 = r1 + stride;
+      if (r2 < n) load_row(r2, 0);
+      process(r1, 1, 1);
+      row = r2;
+    }
   }
   if constexpr (kErr) {
     __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -1117,25 +1127,44 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
   }
 }
 
+// Blocks of quantize_bits_rows<...> per CU with `dyn` bytes of table: computed
+// once per kernel and KiB of table (the memo holds a count, so a race only
+// computes it twice).
+template <typename T, int NCT, int B, bool kErr, bool kOne>
+int bits_blocks_per_cu(size_t dyn) {
+  static std::atomic<int> memo[kMaxBucketsN * 8 / 1024 + 1];
+  const size_t slot = (dyn + 1023) / 1024;
+  int b = memo[slot].load(std::memory_order_relaxed);
+  if (b == 0) {
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, quantize_bits_rows<T, NCT, B, kErr, kOne>,
+                                                     kBlockThreads, slot * 1024) != hipSuccess ||
+        b < 1)
+      b = 1;
+    memo[slot].store(b, std::memory_order_relaxed);
+  }
+  return b;
+}
+
 template <typename T, int NCT, int B, bool kErr>
 hipError_t launch_bits_rows(const T* w, int64_t n, int64_t k, const DecisionPointsN& dp,
                             const BucketGrid& g, const LevelsN& lv, uint32_t* packed,
                             uint32_t* sign, float* scale, double* row_sums, hipStream_t stream) {
-  static const int per_cu = [] {
-    int b = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&b, quantize_bits_rows<T, NCT, B, kErr>,
-                                                     kBlockThreads, 0) != hipSuccess || b < 1)
-      b = 1;
-    return b;
-  }();
+  const size_t dyn = (size_t)g.nb * sizeof(uint2);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
     cus = 1;
-  const int64_t blocks = std::min<int64_t>(2 * (int64_t)per_cu * cus, n);  // as launch_block_rows
+  // as launch_block_rows: twice the resident blocks, or a block per row
+  if (n <= 2 * (int64_t)bits_blocks_per_cu<T, NCT, B, kErr, true>(dyn) * cus) {
+    hipLaunchKernelGGL((quantize_bits_rows<T, NCT, B, kErr, true>), dim3((unsigned)n),
+                       dim3(kBlockThreads), dyn, stream, w, n, (int)k, dp, g, lv, packed, sign,
+                       scale, row_sums);
+    return hipGetLastError();
+  }
+  const int64_t blocks = 2 * (int64_t)bits_blocks_per_cu<T, NCT, B, kErr, false>(dyn) * cus;
   hipLaunchKernelGGL((quantize_bits_rows<T, NCT, B, kErr>), dim3((unsigned)blocks),
-                     dim3(kBlockThreads), 0, stream, w, n, (int)k, dp, g, lv, packed, sign, scale,
-                     row_sums);
+                     dim3(kBlockThreads), dyn, stream, w, n, (int)k, dp, g, lv, packed, sign,
+                     scale, row_sums);
   return hipGetLastError();
 }
 
