@@ -234,6 +234,21 @@ def test_decision_thresholds_rational_cases():
     assert t1[7] == np.float32(0.5)
 
 
+@pytest.mark.parametrize("alpha", [0.3, 0.45, 0.73, 1.0, 2.0])
+def test_decision_thresholds_are_least_in_class(alpha):
+    """T_k is the least binary32 t with 15 t^alpha >= k - 1/2 ("OPQ 原理":
+    code k from k - 1/2 up): T_k is in that class and the binary32 just below
+    it is not, in 200-bit arithmetic."""
+    al = mpmath.mpf(O.alpha_f32(alpha))
+    t = O.decision_thresholds_f32(alpha)
+    with mpmath.workprec(200):
+        for k in range(1, 16):
+            def in_class(x):
+                return 15 * mpmath.power(mpmath.mpf(float(x)), al) >= k - mpmath.mpf(0.5)
+            assert in_class(t[k - 1]), (alpha, k)
+            assert not in_class(np.nextafter(t[k - 1], np.float32(0))), (alpha, k)
+
+
 @pytest.mark.parametrize("alpha", [0.45, 0.73])
 def test_encode_equals_threshold_count(alpha):
     w = _rand_rows(7, 16, 256)
