@@ -309,6 +309,30 @@ def main():
             rec["TFLOPs"] = round(a["flops"] / (us * 1e-6) / 1e12, 2)
         kern[kind] = rec
 
+    # The practical ceiling at each kernel's size: a plain device copy that reads
+    # and writes the kernel's algorithmic bytes, over enough buffer pairs to
+    # defeat the 256 MB cache, timed the same way.  Left out of counter runs
+    # (--copy-mib), whose only copies calibrate the byte counters.
+    for kind in (kinds if not args.copy_mib else []):
+        half = int(alg[kind]["bytes"]) // 2
+        pairs = max(2, int(np.ceil(800e6 / (2 * half))))
+        bufs = [(torch.empty(half, dtype=torch.uint8, device=dev),
+                 torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(pairs)]
+        per = []
+        for b in range(7):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(args.steps):
+                dst, src = bufs[(b * args.steps + i) % pairs]
+                dst.copy_(src)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / args.steps * 1e3)
+        kern[kind]["same_bytes_copy_us"] = round(float(np.median(per)), 3)
+        del bufs
+    torch.cuda.synchronize()
+
     if args.copy_mib:
         # A plain device copy of known size, for scaling the HBM byte counters.
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
