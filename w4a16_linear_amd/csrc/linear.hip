@@ -64,6 +64,7 @@ constexpr int kSkRows = 16;                     // weight rows per block
 constexpr int kSkWaves = 8;
 constexpr int kSkThreads = kSkWaves * kWave;
 constexpr int kSkBlockK = 128;                  // k per wave step
+constexpr int kSkDepth = 2;                     // k blocks in flight per wave (m <= 32)
 
 // Element offset of 16-byte chunk c (0..15) of x row R in a wave's stage:
 // 256-byte rows, chunks XOR-swizzled by the row so that the sixteen rows of a
@@ -87,9 +88,11 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
     Levels lv, void* __restrict__ y, int y_bf16) {
   static_assert(GS == 0 || kPre || NMB <= 2, "the significand table and four x row blocks overfill LDS");
   static_assert(!kPre || GS > 0, "tables made at block start are for the group-wise form");
-  // One k block per load batch, two batches in flight: batches of two k
-  // blocks took 14 % longer at m = 32 (more registers, a later first MFMA).
+  // One k block per load batch, D batches in flight (a ring of register
+  // buffers): batches of two k blocks took 14 % longer at m = 32 (more
+  // registers, a later first MFMA).
   constexpr int CH = 1;
+  constexpr int D = NMB >= 4 ? 2 : kSkDepth;
   constexpr int kXRows = 16 * NMB;
   constexpr int kXLoads = kXRows / 4;                   // x loads per lane per k block
   constexpr int kStage = kXRows * kSkBlockK;            // bf16 per wave stage
@@ -129,10 +132,10 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   const int r = lane & 15, g = lane >> 4;
   const int src = (4 * r + g) * 4;
 
-  uint4 wd[2][CH];
-  uint32_t sw[2][CH];
-  uint32_t hv[2][CH];  // GS > 0: float16 max of the lane's group in each k block
-  uint4 xv[2][CH][kXLoads];
+  uint4 wd[D][CH];
+  uint32_t sw[D][CH];
+  uint32_t hv[D][CH];  // GS > 0: float16 max of the lane's group in each k block
+  uint4 xv[D][CH][kXLoads];
   const int ngroups = GS ? k / GS : 1;
   const uint16_t* hrow = GS ? scale16 + (int64_t)min(n0 + r, n - 1) * ngroups : nullptr;
   // Batch bi holds this wave's k blocks bi*CH .. bi*CH + CH - 1 (clamped to the
@@ -154,8 +157,9 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   };
 
   const int nbatch = (mine + CH - 1) / CH;
-  if (nbatch > 0) load_batch(0, 0);
-  if (nbatch > 1) load_batch(1, 1);
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (nbatch > d) load_batch(d, d);
 
   // Byte planes of the block's 16 row tables: wave w < 4 makes entries
   // 4w .. 4w+3 of row `lane` (a wave-uniform code, so the levels stay in
@@ -245,12 +249,13 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
     }
   };
 
-  for (int bi = 0; bi < nbatch; bi += 2) {
-    compute_batch(bi, 0);
-    if (bi + 2 < nbatch) load_batch(bi + 2, 0);
-    if (bi + 1 < nbatch) {
-      compute_batch(bi + 1, 1);
-      if (bi + 3 < nbatch) load_batch(bi + 3, 1);
+  for (int bi = 0; bi < nbatch; bi += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (bi + d < nbatch) {
+        compute_batch(bi + d, d);
+        if (bi + d + D < nbatch) load_batch(bi + d + D, d);
+      }
     }
   }
 
