@@ -154,7 +154,8 @@ def test_quantize_bf16_shapes(gpu_lib, n, k, alpha):
     full_roundtrip(gpu_lib, w_vals, w_dev, alpha)
 
 
-@pytest.mark.parametrize("n,k", [(3, 256), (4, 4096), (2, 8192), (2, 8224), (3, 12288)])
+@pytest.mark.parametrize("n,k", [(3, 256), (4, 4096), (2, 8192), (2, 8224), (3, 12288),
+                                 (2, 16416), (2, 20480)])
 def test_quantize_fp32_shapes(gpu_lib, n, k):
     w = WL.normal(200 + k, (n, k), 0.02)
     w_vals, w_dev = weight_tensor(w, "f32")
@@ -180,6 +181,19 @@ def _special_rows(k, dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_quantize_special_rows(gpu_lib, dtype, alpha):
     w = _special_rows(544, dtype)
+    w_vals, w_dev = weight_tensor(w, dtype)
+    full_roundtrip(gpu_lib, w_vals, w_dev, alpha)
+
+
+@pytest.mark.parametrize("alpha", [0.03, 100.0])
+@pytest.mark.parametrize("dtype,n,k", [("bf16", 5, 96), ("bf16", 7, 544), ("f32", 9, 3840),
+                                       ("bf16", 3, 8224), ("f32", 2, 16416), ("bf16", 2, 16416)])
+def test_quantize_alpha_without_bucket_grid(gpu_lib, alpha, dtype, n, k):
+    """Alphas whose decision points no bucket grid separates (at 0.03 the first
+    lies below the normal binary32 range, at 100 all crowd below 1): the
+    per-row threshold kernels, with the levels' subnormal reconstructions at
+    0.03, against the oracle; k > 16384 streams the row twice."""
+    w = WL.student_t(300 + n + k, (n, k))
     w_vals, w_dev = weight_tensor(w, dtype)
     full_roundtrip(gpu_lib, w_vals, w_dev, alpha)
 
