@@ -264,6 +264,27 @@ def test_linear_shapes(gpu_lib, m, n, k):
     assert_linear_close(gy.t.cpu().numpy(), y_ref)
 
 
+@pytest.mark.parametrize("alpha", [0.03, 100.0])
+@pytest.mark.parametrize("m", [8, 300])
+def test_linear_alpha_without_bucket_grid(gpu_lib, m, alpha):
+    """The linear layer's on-chip tables at alphas far from the usual range
+    (subnormal reconstructions at 0.03, levels crowded near 1 at 100): skinny
+    and tiled paths against the oracle's reconstruction."""
+    opq = gpu_lib
+    n, k = 200, 544
+    w_vals, w_dev = weight_tensor(WL.student_t(600 + n, (n, k)), "bf16")
+    qw = quantize_guarded(opq, w_dev, alpha)
+    ref = O.quantize(w_vals, alpha)
+    assert_quant_equal(qw, ref)
+    d_ref = O.dequantize(*ref, alpha)
+    xt = to_bf16(WL.normal(700 + m, (m, k)))
+    gy = Guarded((m, n), torch.float32)
+    opq.linear(xt.to(DEV), qw, alpha, out=gy.t)
+    torch.cuda.synchronize()
+    gy.check()
+    assert_linear_close(gy.t.cpu().numpy(), O.linear(bf16_bits(xt), d_ref))
+
+
 def test_linear_one_hot_rows_pick_weights(gpu_lib):
     """x = identity rows: y[:, n] is the reconstruction W'[n, :] itself."""
     opq = gpu_lib
