@@ -1,5 +1,6 @@
-"""Plain, slow CPU oracle for OPQ (Optimal Power Quantization), 4-bit, with one
-scale per output row or one float16 scale per group of weights.
+"""Plain, slow CPU oracle for OPQ (Optimal Power Quantization): 4-bit codes
+(and 3, 5 and 6-bit ones further down) with one scale per output row or one
+float16 scale per group of weights.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
 ``cpu_baseline`` leg of ``bench.py`` may import this module.  It shares no code,
