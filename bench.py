@@ -183,7 +183,7 @@ def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the OPQ hot path here has no multi-GPU "
-              "path (rows shard without exchange; see DESIGN.md)", file=sys.stderr)
+              "path (its rows would shard across GPUs with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
