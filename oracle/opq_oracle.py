@@ -16,7 +16,7 @@ Source of every step: the model card "OPQ INT4 Z-Image: 最优幂次量化扩散
 * section "技术细节 / 推理解码" (decode): q/15, raised to 1/alpha, times sign
   and the group max.
 
-Readings taken where the page is silent (each is listed in the design doc):
+Readings taken where the page is silent:
 
 * the max is taken per output row and kept as an fp32 scale (the card keeps an
   fp16 max per group of 128; the per-row form is the workload's);

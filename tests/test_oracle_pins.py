@@ -628,7 +628,7 @@ def test_group_quantize_dequantize_idempotent(gs):
 # ------------------------------------------------------------------ other code widths
 #
 # The configuration section offers 3, 4, 5 or 6 bits; 2^b - 1 takes the place
-# of 15.  The packing for b != 4 is this build's (a little-endian bit stream).
+# of 15.  The card gives no packing for b != 4; here it is a little-endian bit stream.
 
 def test_bits4_is_the_nibble_form():
     w = _to_bf16_values(_rand_rows(50, 5, 256))
