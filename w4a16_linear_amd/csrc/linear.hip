@@ -63,6 +63,16 @@ constexpr int kSkinnyMaxM = 64;
 constexpr int kSkRows = 16;                     // weight rows per block
 constexpr int kSkWaves = 8;
 constexpr int kSkThreads = kSkWaves * kWave;
+
+// Waves per block of an instance.  The two-m-block instance (17 <= m <= 32)
+// runs 16 waves with one k block in flight per wave: twice the waves over the
+// same 16 weight rows halve each wave's share of k, which hides more of the
+// load latency than a second buffer did (about 6% faster at m = 32); the
+// one-m-block instance was slower so (m = 16), and the four-m-block one has
+// no registers to spare.  The group-wise instance takes it only with the
+// block's tables prebuilt, which leaves it no per-k-block table build.
+template <int NMB, int GS, bool kPre>
+constexpr int sk_waves() { return (NMB == 2 && (GS == 0 || kPre)) ? 16 : kSkWaves; }
 constexpr int kSkBlockK = 128;                  // k per wave step
 constexpr int kSkDepth = 2;                     // k blocks in flight per wave (m <= 32)
 
@@ -81,7 +91,7 @@ __device__ __forceinline__ int xs_off(int R, int c) { return R * kSkBlockK + ((c
 // significand table and the group max of its part.
 constexpr int kSkPreGroups = kSkThreads;
 template <int NMB, int GS, bool kPre = false>  // NMB: 16-row blocks of x (1, 2 or 4); GS: group or 0 (per row)
-__global__ __launch_bounds__(kSkThreads) void linear_skinny(
+__global__ __launch_bounds__((sk_waves<NMB, GS, kPre>() * kWave)) void linear_skinny(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
     const uint16_t* __restrict__ scale16, const float* __restrict__ bias, int m, int n, int k,
@@ -92,13 +102,14 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   // buffers): batches of two k blocks took 14 % longer at m = 32 (more
   // registers, a later first MFMA).
   constexpr int CH = 1;
-  constexpr int D = NMB >= 4 ? 2 : kSkDepth;
+  constexpr int W = sk_waves<NMB, GS, kPre>();
+  constexpr int D = NMB >= 4 ? 2 : (W > kSkWaves && NMB == 2 ? 1 : kSkDepth);
   constexpr int kXRows = 16 * NMB;
   constexpr int kXLoads = kXRows / 4;                   // x loads per lane per k block
   constexpr int kStage = kXRows * kSkBlockK;            // bf16 per wave stage
   constexpr int kOut = NMB * 4 * kWave;                 // outputs per wave, accumulator order
-  static_assert(kSkWaves * kOut * 4 <= kSkWaves * kStage * 2, "reduction fits the stages");
-  __shared__ __attribute__((aligned(16))) uint16_t s_x[kSkWaves * kStage];
+  static_assert(W * kOut * 4 <= W * kStage * 2, "reduction fits the stages");
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[W * kStage];
   __shared__ uint32_t s_lut[GS ? 1 : kSkRows][8];
   __shared__ __attribute__((aligned(16))) uint32_t s_mt[(GS && !kPre) ? kMantissas * 8 : 4];
   __shared__ __attribute__((aligned(16))) uint32_t s_glut[kPre ? kSkPreGroups * 8 : 4];
@@ -110,9 +121,9 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   const int n0 = blockIdx.x * kSkRows;
   const int kwords = k / 8, swords = k / 32;
 
-  // This wave's k blocks: wave, wave + kSkWaves, ...
+  // This wave's k blocks: wave, wave + W, ...
   const int nkb = (k + kSkBlockK - 1) / kSkBlockK;
-  const int mine = nkb > wave ? (nkb - 1 - wave) / kSkWaves + 1 : 0;
+  const int mine = nkb > wave ? (nkb - 1 - wave) / W + 1 : 0;
 
   // Loader lanes.  Weight rows past n read row n - 1 and x rows past m read
   // row m - 1; neither is stored.
@@ -144,7 +155,7 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   auto load_batch = [&](int bi, int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-      const int kb = (wave + kSkWaves * min(bi * CH + j, mine - 1)) * kSkBlockK;
+      const int kb = (wave + W * min(bi * CH + j, mine - 1)) * kSkBlockK;
       const uint32_t kw = (uint32_t)(kb + 32 * lp < k ? kb + 32 * lp : kb);
       const uint32_t kx = (uint32_t)(kb + 8 * xc < k ? kb + 8 * xc : kb);
       wd[buf][j] = *reinterpret_cast<const uint4*>(pbase + p_off + kw / 2u);
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
     for (int j = 0; j < CH; ++j) {
       const int idx = bi * CH + j;
       if (idx < mine) {
-        const int kb = (wave + kSkWaves * idx) * kSkBlockK;
+        const int kb = (wave + W * idx) * kSkBlockK;
         const bool live = kb + 32 * g < k;
 #pragma unroll
         for (int i = 0; i < kXLoads; ++i) {
@@ -269,14 +280,14 @@ __global__ __launch_bounds__(kSkThreads) void linear_skinny(
   __syncthreads();
   // Output (x row mm, weight row i): register i % 4 of lane 16 * (i / 4) + mm % 16
   // in block mm / 16; waves summed in a fixed order.
-  for (int o = tid; o < kSkRows * kXRows; o += kSkThreads) {
+  for (int o = tid; o < kSkRows * kXRows; o += W * kWave) {
     const int i = o % kSkRows, mm = o / kSkRows;
     const int gcol = n0 + i;
     if (mm < m && gcol < n) {
       const int src_o = ((mm >> 4) * 4 + (i & 3)) * kWave + 16 * (i >> 2) + (mm & 15);
       float val = s_red[src_o];
 #pragma unroll
-      for (int w = 1; w < kSkWaves; ++w) val += s_red[w * kOut + src_o];
+      for (int w = 1; w < W; ++w) val += s_red[w * kOut + src_o];
       store_y(y, y_bf16, (int64_t)mm * n + gcol, val + (bias ? bias[gcol] : 0.0f));
     }
   }
@@ -549,20 +560,23 @@ hipError_t launch_linear_any(const uint16_t* x, const uint32_t* packed, const ui
     // group tables made at block start when the block's groups fit
     const bool pre = GS > 0 && kSkRows * (k / (GS ? GS : 1)) <= kSkPreGroups;
     auto k2 = pre ? linear_skinny<2, GS, (GS > 0)> : linear_skinny<2, GS>;
+    const unsigned t2 = (unsigned)(pre ? sk_waves<2, GS, (GS > 0)>() : sk_waves<2, GS, false>()) * kWave;
     if (GS > 0 && !pre && m > 32) {
       // The significand table leaves no room for four x row blocks: two
       // launches of up to 32 x rows each.
-      hipLaunchKernelGGL(k2, dim3((unsigned)blocks), dim3(kSkThreads), 0, stream, x, packed,
+      hipLaunchKernelGGL(k2, dim3((unsigned)blocks), dim3(t2), 0, stream, x, packed,
                          sign, scale, scale16, bias, 32, (int)n, (int)k, lv, y, (int)y_bf16);
       const int64_t ybytes = y_bf16 ? 2 : 4;
-      hipLaunchKernelGGL(k2, dim3((unsigned)blocks), dim3(kSkThreads), 0, stream, x + 32 * k,
+      hipLaunchKernelGGL(k2, dim3((unsigned)blocks), dim3(t2), 0, stream, x + 32 * k,
                          packed, sign, scale, scale16, bias, (int)(m - 32), (int)n, (int)k, lv,
                          static_cast<char*>(y) + 32 * n * ybytes, (int)y_bf16);
       return hipGetLastError();
     }
     auto k1 = pre ? linear_skinny<1, GS, (GS > 0)> : linear_skinny<1, GS>;
+    const unsigned t1 = (unsigned)(pre ? sk_waves<1, GS, (GS > 0)>() : sk_waves<1, GS, false>()) * kWave;
     auto kernel = m <= 16 ? k1 : (m <= 32 ? k2 : linear_skinny<4, GS, (GS > 0)>);
-    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kSkThreads), 0, stream, x, packed,
+    const unsigned th = m <= 16 ? t1 : (m <= 32 ? t2 : (unsigned)sk_waves<4, GS, (GS > 0)>() * kWave);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(th), 0, stream, x, packed,
                        sign, scale, scale16, bias, (int)m, (int)n, (int)k, lv, y, (int)y_bf16);
   } else {
     const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
