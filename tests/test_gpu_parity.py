@@ -143,7 +143,8 @@ def test_tiny_config_whole_path(gpu_lib):
 
 # ------------------------------------------------------------------ quantize / dequantize edge cases
 
-SHAPES = [(1, 32), (5, 96), (7, 544), (33, 3840), (3, 10240), (2, 16384), (2, 16416), (3, 20480)]
+SHAPES = [(1, 32), (5, 96), (7, 544), (3, 2048), (3, 2080), (33, 3840), (3, 10240), (2, 16384),
+          (2, 16416), (3, 20480)]
 
 
 @pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0])
@@ -154,11 +155,22 @@ def test_quantize_bf16_shapes(gpu_lib, n, k, alpha):
     full_roundtrip(gpu_lib, w_vals, w_dev, alpha)
 
 
-@pytest.mark.parametrize("n,k", [(3, 256), (4, 4096), (2, 8192), (2, 8224), (3, 12288),
-                                 (2, 16416), (2, 20480)])
+@pytest.mark.parametrize("n,k", [(3, 256), (5, 2048), (4, 2080), (4, 4096), (2, 8192), (2, 8224),
+                                 (3, 12288), (2, 16416), (2, 20480)])
 def test_quantize_fp32_shapes(gpu_lib, n, k):
     w = WL.normal(200 + k, (n, k), 0.02)
     w_vals, w_dev = weight_tensor(w, "f32")
+    full_roundtrip(gpu_lib, w_vals, w_dev, 0.73)
+
+
+@pytest.mark.parametrize("dtype,n,k", [("bf16", 9001, 96), ("f32", 8500, 544), ("bf16", 8200, 2048)])
+def test_quantize_short_rows_past_one_grid(gpu_lib, dtype, n, k):
+    """Rows of up to 2048 elements go one to a wave, on a grid of at most 8192
+    waves: more rows than that make waves take a second row (its loads issued
+    after the first row's stores)."""
+    w = WL.student_t(400 + n, (n, k))
+    w[n // 2] = 0.0
+    w_vals, w_dev = weight_tensor(w, dtype)
     full_roundtrip(gpu_lib, w_vals, w_dev, 0.73)
 
 

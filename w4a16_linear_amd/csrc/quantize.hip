@@ -4,7 +4,7 @@
 //   packed nibbles eight per uint32, signs thirty-two per uint32.
 //
 // A block of 256 threads owns one row at a time (one wave per row in the
-// kernels for rows longer than 16384).  The row is read from HBM once and held
+// kernels for rows of up to 2048 or more than 16384 elements).  The row is read from HBM once and held
 // in VGPRs while the max is reduced, so HBM traffic is the algorithmic 2 B
 // (bf16) read + 0.625 B written per weight.
 //
@@ -294,7 +294,9 @@ __device__ __forceinline__ uint32_t encode_chunk(const Slot<T>& v, float mx, flo
 
 // Table kernel: blocks build the table, then each wave takes one row at a time
 // (rows strided over the grid).  NCH > 0: the row (k <= NCH * 512) stays in
-// registers.  NCH == 0: any k, the row is streamed twice (max, then encode).
+// registers; this is the kernel for rows of up to 2048 elements.  NCH == 0:
+// any k, the row is streamed twice (max, then encode); it takes rows longer
+// than the block kernel's 16384.
 template <typename T, int NCH>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
     const T* __restrict__ w, int64_t n, int k, DecisionPoints dp, BucketGrid g,
@@ -733,10 +735,14 @@ hipError_t dispatch_error(const T* w, int64_t n, int64_t k, const DecisionPoints
 template <typename T>
 hipError_t dispatch(const T* w, int64_t n, int64_t k, const DecisionPoints& dp, uint32_t* packed,
                     uint32_t* sign, float* scale, hipStream_t stream) {
+  const int64_t nch = (k + kChunk - 1) / kChunk;
   BucketGrid g;
-  if (bucket_grid(dp, g)) {
+  // Rows of up to 2048 elements go one to a wave (below, through the table
+  // kernel): a 256-thread block would leave threads idle on them (11520 x 1024
+  // bf16: 18.2 -> 10.7 us); at k = 2560 the two measure the same, from 3840
+  // the block per row is faster.
+  if (nch > 4 && bucket_grid(dp, g)) {
     const int64_t nct = (k + kBlockChunk - 1) / kBlockChunk;
-    if (nct <= 1) return launch_block_rows<T, 1>(w, n, k, dp, g, packed, sign, scale, stream);
     if (nct <= 2) return launch_block_rows<T, 2>(w, n, k, dp, g, packed, sign, scale, stream);
     if (nct <= 3) return launch_block_rows<T, 3>(w, n, k, dp, g, packed, sign, scale, stream);
     if (nct <= 4) return launch_block_rows<T, 4>(w, n, k, dp, g, packed, sign, scale, stream);
@@ -744,7 +750,6 @@ hipError_t dispatch(const T* w, int64_t n, int64_t k, const DecisionPoints& dp, 
     if (nct <= 6) return launch_block_rows<T, 6>(w, n, k, dp, g, packed, sign, scale, stream);
     if (nct <= 8) return launch_block_rows<T, 8>(w, n, k, dp, g, packed, sign, scale, stream);
   }
-  const int64_t nch = (k + kChunk - 1) / kChunk;
   // bf16 slots take 4 VGPRs per chunk, fp32 slots 8: fp32 rows stay in
   // registers up to 16 chunks, bf16 rows up to 32.
   if (nch <= 1) return launch_rows<T, 1>(w, n, k, dp, packed, sign, scale, stream);
