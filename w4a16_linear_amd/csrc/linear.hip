@@ -64,17 +64,17 @@ constexpr int kSkRows = 16;                     // weight rows per block
 constexpr int kSkWaves = 8;
 constexpr int kSkThreads = kSkWaves * kWave;
 
-// Waves per block of an instance.  The two-m-block instance (17 <= m <= 32)
-// runs 16 waves with one k block in flight per wave: twice the waves over the
-// same 16 weight rows halve each wave's share of k, which hides more of the
-// load latency than a second buffer did (about 6% faster at m = 32); the
-// one-m-block instance was slower so (m = 16), and the four-m-block one has
-// no registers to spare.  The group-wise instance takes it only with the
-// block's tables prebuilt, which leaves it no per-k-block table build.
+// Waves per block of an instance.  Up to 32 x rows (one or two m blocks) a
+// block runs 16 waves with one k block in flight per wave: twice the waves
+// over the same 16 weight rows halve each wave's share of k, which hides more
+// of the load latency than a second buffer did (m = 32 about 6% faster, m = 8
+// and 16 4-7%).  The four-m-block instance has no registers or LDS to spare.
+// The group-wise instances take it only with the block's tables prebuilt,
+// which leaves them no per-k-block table build.
 template <int NMB, int GS, bool kPre>
-constexpr int sk_waves() { return (NMB == 2 && (GS == 0 || kPre)) ? 16 : kSkWaves; }
+constexpr int sk_waves() { return (NMB <= 2 && (GS == 0 || kPre)) ? 16 : kSkWaves; }
 constexpr int kSkBlockK = 128;                  // k per wave step
-constexpr int kSkDepth = 2;                     // k blocks in flight per wave (m <= 32)
+constexpr int kSkDepth = 2;                     // k blocks in flight per wave of an 8-wave block
 
 // Element offset of 16-byte chunk c (0..15) of x row R in a wave's stage:
 // 256-byte rows, chunks XOR-swizzled by the row so that the sixteen rows of a
@@ -103,7 +103,7 @@ __global__ __launch_bounds__((sk_waves<NMB, GS, kPre>() * kWave)) void linear_sk
   // registers, a later first MFMA).
   constexpr int CH = 1;
   constexpr int W = sk_waves<NMB, GS, kPre>();
-  constexpr int D = NMB >= 4 ? 2 : (W > kSkWaves && NMB == 2 ? 1 : kSkDepth);
+  constexpr int D = W > kSkWaves ? 1 : (NMB >= 4 ? 2 : kSkDepth);
   constexpr int kXRows = 16 * NMB;
   constexpr int kXLoads = kXRows / 4;                   // x loads per lane per k block
   constexpr int kStage = kXRows * kSkBlockK;            // bf16 per wave stage
