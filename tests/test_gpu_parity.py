@@ -424,6 +424,23 @@ def _check_layer(opq, L, alpha, with_linear, x_rows=64, q_rows=512):
     return None
 
 
+@pytest.mark.parametrize("dtype,n,k", [("bf16", 6007, 3840), ("bf16", 8200, 3840),
+                                       ("f32", 6100, 2080)])
+def test_quantize_rows_around_block_per_row_bound(gpu_lib, dtype, n, k):
+    """Row counts below and above the bound up to which each row gets a block
+    of its own (four times the blocks resident at once; past it blocks stride
+    over rows): codes, signs and scales at sampled rows equal the oracle's."""
+    opq = gpu_lib
+    w32 = WL.student_t(500 + n, (n, k))
+    w_vals, w_dev = weight_tensor(w32, dtype)
+    del w32
+    qw = opq.quantize(w_dev, WL.ALPHA)
+    rows = _sample_rows(n, 256, n + k)
+    ref_rows = O.quantize(w_vals[rows], WL.ALPHA)
+    torch.cuda.synchronize()
+    assert_quant_equal(qw, ref_rows, rows)
+
+
 @pytest.mark.parametrize("key", ["skinny", "qkv", "ffn"])
 def test_config_full_size(gpu_lib, key):
     cfg = WL.config(key)

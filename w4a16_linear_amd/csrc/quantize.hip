@@ -700,10 +700,12 @@ hipError_t launch_block_rows(const T* w, int64_t n, int64_t k, const DecisionPoi
   // Twice the blocks that fit at once: the second half starts as the first
   // finishes, which evens out the rows per block (15.8 -> 14.4 us for a
   // 3840 x 3840 bf16 weight, no loss at 11520 rows).  When that many blocks
-  // cover every row, a block per row without the prefetch buffer.
+  // cover every row, a block per row without the prefetch buffer; for the
+  // codes up to four times the resident count (7680 x 3840 bf16: 24.7 ->
+  // 23.0 us; equal at 11520 rows, 2% slower at 20480).
   Levels lvv{};
   if (lv) lvv = *lv;
-  if (n <= 2 * resident_blocks<T, NCT, kErr, true>()) {
+  if (n <= (kErr ? 2 : 4) * resident_blocks<T, NCT, kErr, true>()) {
     hipLaunchKernelGGL((quantize_block_rows<T, NCT, kErr, true>), dim3((unsigned)n),
                        dim3(kBlockThreads), 0, stream, w, n, (int)k, dp, g, packed, sign, scale,
                        lvv, row_sums);
