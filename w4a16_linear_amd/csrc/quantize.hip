@@ -161,12 +161,23 @@ constexpr uint32_t kTop = 0x40000000u;      // bits(2.0f): u' is clamped to [flo
 constexpr int kMaxBlocks = 2048;            // grid of the table kernel (rows are strided)
 
 // Buckets b = 0 .. nb-1 cover bit patterns [b0 + (b << shift), b0 + ((b + 1) << shift));
-// the last one reaches past bits(2.0f).
+// the last one reaches past bits(2.0f).  b0 is a multiple of 2^shift, and the
+// table has `size` slots (nb rounded up to a power of two) with bucket b in
+// slot ((b0 >> shift) + b) mod size, so a bit pattern's slot is
+// (bits >> shift) mod size: its byte offset (bits >> (shift - 3)) & mask8 is
+// two instructions, with no base to subtract.
 struct BucketGrid {
   uint32_t b0;
   int shift;
   int nb;
+  int size;
 };
+
+inline int table_slots(int64_t nb) {
+  int s = 1;
+  while (s < nb) s *= 2;
+  return s;
+}
 
 __host__ __device__ inline uint32_t float_bits(float t) {
   uint32_t b;
@@ -193,6 +204,7 @@ bool bucket_grid(const DecisionPoints& dp, BucketGrid& g) {
       g.b0 = b0;
       g.shift = shift;
       g.nb = (int)nb;
+      g.size = table_slots(nb);
       return true;
     }
   }
@@ -220,31 +232,31 @@ __device__ void build_table(const DecisionPoints& dp, BucketGrid g, uint2* tab) 
       next = under ? next : c;  // ends at the lowest point not wholly below
     }
     const uint32_t x = (next != kNoPoint && next - kGuard < hi) ? kGuard - next : kGuard - kNoPoint;
-    tab[b] = make_uint2(x, below);
+    tab[((g.b0 >> g.shift) + (uint32_t)b) & (uint32_t)(g.size - 1)] = make_uint2(x, below);
   }
 }
 
-// Table entry for a quotient already clamped to [floor, 2.0]; nbase8 is
-// -(b0 >> shift) * 8.
-__device__ __forceinline__ uint2 table_at(const uint2* tab, uint32_t ub, int shift, uint32_t nbase8) {
-  const uint32_t off = ((ub >> shift) << 3) + nbase8;
+// Table entry for a quotient already clamped to [floor, 2.0]; sh3 is the
+// grid's shift - 3 and mask8 is (size - 1) * 8.
+__device__ __forceinline__ uint2 table_at(const uint2* tab, uint32_t ub, int sh3, uint32_t mask8) {
+  const uint32_t off = (ub >> sh3) & mask8;
   return *reinterpret_cast<const uint2*>(reinterpret_cast<const char*>(tab) + off);
 }
 
 // Exact code of magnitude a in a row with max m (m >= a >= 0): the correctly
 // rounded quotient, its bucket, and one comparison with the next point
 // (pts[15] = 2 is never reached).
-__device__ __forceinline__ uint32_t code_exact(float a, float m, const uint2* tab, int shift,
-                                               uint32_t nbase, float ulo, const float* pts) {
+__device__ __forceinline__ uint32_t code_exact(float a, float m, const uint2* tab, int sh3,
+                                               uint32_t mask8, float ulo, const float* pts) {
   const float u = m > 0.0f ? a / m : 0.0f;
   const float uc = fminf(fmaxf(u, ulo), 2.0f);
-  const uint32_t below = table_at(tab, __float_as_uint(uc), shift, nbase).y;
+  const uint32_t below = table_at(tab, __float_as_uint(uc), sh3, mask8).y;
   return below + (u >= pts[below] ? 1u : 0u);
 }
 
 template <typename T>
 __device__ __forceinline__ uint32_t encode8_exact(const Slot<T>& s, float m, const uint2* tab,
-                                                  int shift, uint32_t nbase, float ulo,
+                                                  int sh3, uint32_t mask8, float ulo,
                                                   const float* pts) {
   uint32_t word = 0u;
 #pragma unroll
@@ -253,7 +265,7 @@ __device__ __forceinline__ uint32_t encode8_exact(const Slot<T>& s, float m, con
     // path folds it into its multiply)
     float v = s.at(i);
     asm volatile("" : "+v"(v));
-    word = (word << 4) + code_exact(fabsf(v), m, tab, shift, nbase, ulo, pts);
+    word = (word << 4) + code_exact(fabsf(v), m, tab, sh3, mask8, ulo, pts);
   }
   return word;
 }
@@ -263,7 +275,7 @@ __device__ __forceinline__ uint32_t encode8_exact(const Slot<T>& s, float m, con
 // caller re-encodes exactly when it is <= 2 kGuard.
 template <typename T>
 __device__ __forceinline__ uint32_t encode8_fast(const Slot<T>& s, float r, const uint2* tab,
-                                                 int shift, uint32_t nbase, float ulo,
+                                                 int sh3, uint32_t mask8, float ulo,
                                                  uint32_t& near) {
   uint32_t word = 0u, nr = 0xFFFFFFFFu;
 #pragma unroll
@@ -271,7 +283,7 @@ __device__ __forceinline__ uint32_t encode8_fast(const Slot<T>& s, float r, cons
     // finite here: the row max is normal and 1/m too
     const float up = __builtin_amdgcn_fmed3f(fabsf(s.at(i)) * r, ulo, 2.0f);
     const uint32_t ub = __float_as_uint(up);
-    const uint2 e = table_at(tab, ub, shift, nbase);
+    const uint2 e = table_at(tab, ub, sh3, mask8);
     const int d = (int)(ub + e.x);
     word = (word << 4) + e.y + (d >= (int)kGuard ? 1u : 0u);
     nr = min(nr, (uint32_t)d);
@@ -282,13 +294,13 @@ __device__ __forceinline__ uint32_t encode8_fast(const Slot<T>& s, float r, cons
 
 template <typename T>
 __device__ __forceinline__ uint32_t encode_chunk(const Slot<T>& v, float mx, float r, bool fast,
-                                                 const uint2* tab, int shift, uint32_t nbase,
+                                                 const uint2* tab, int sh3, uint32_t mask8,
                                                  float ulo, const float* pts) {
   // The fast encode runs on every chunk (with 1 standing in for 1/m where it
   // does not apply), so the exact re-encode is the only branch.
   uint32_t near;
-  uint32_t word = encode8_fast(v, fast ? r : 1.0f, tab, shift, nbase, ulo, near);
-  if (!fast || near <= 2u * kGuard) word = encode8_exact(v, mx, tab, shift, nbase, ulo, pts);
+  uint32_t word = encode8_fast(v, fast ? r : 1.0f, tab, sh3, mask8, ulo, near);
+  if (!fast || near <= 2u * kGuard) word = encode8_exact(v, mx, tab, sh3, mask8, ulo, pts);
   return word;
 }
 
@@ -331,8 +343,8 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
   // (a full __syncthreads would wait for them too).
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left open
   __builtin_amdgcn_s_barrier();
-  const int shift = g.shift;
-  const uint32_t nbase = (0u - (g.b0 >> g.shift)) << 3;
+  const int sh3 = g.shift - 3;
+  const uint32_t mask8 = (uint32_t)(g.size - 1) << 3;
   const float ulo = __uint_as_float(g.b0);
 
   for (; row < n; row += stride) {
@@ -348,7 +360,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         const int e0 = c * kChunk + lane * 8;
-        const uint32_t word = encode_chunk(v[c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts);
+        const uint32_t word = encode_chunk(v[c], mx, r, fast, s_tab, sh3, mask8, ulo, s_pts);
         store_chunk(prow, srow, c, lane, e0 < k, word, sign_byte(v[c]));
       }
       if (lane == 0) scale[row] = mx;
@@ -372,7 +384,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
         const int e0 = c * kChunk + lane * 8;
         Slot<T> sl;
         if (e0 < k) sl.load(wr + e0); else sl.zero();
-        const uint32_t word = encode_chunk(sl, mx, r, fast, s_tab, shift, nbase, ulo, s_pts);
+        const uint32_t word = encode_chunk(sl, mx, r, fast, s_tab, sh3, mask8, ulo, s_pts);
         store_chunk(prow, srow, c, lane, e0 < k, word, sign_byte(sl));
       }
       if (lane == 0) scale[row] = mx;
@@ -451,8 +463,8 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
     for (int j = 0; j < kLevels; ++j) s_pts[j] = dp.t[j];
     s_pts[kLevels] = 2.0f;
   }
-  const int shift = g.shift;
-  const uint32_t nbase = (0u - (g.b0 >> g.shift)) << 3;
+  const int sh3 = g.shift - 3;
+  const uint32_t mask8 = (uint32_t)(g.size - 1) << 3;
   const float ulo = __uint_as_float(g.b0);
 
   // Encode the row held in buffer `buf`; `ms` picks the LDS slot of its max
@@ -490,7 +502,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
         const int e0 = c * kBlockChunk + tid * 8;
-        const uint32_t word = encode_chunk(v[buf][c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts);
+        const uint32_t word = encode_chunk(v[buf][c], mx, r, fast, s_tab, sh3, mask8, ulo, s_pts);
         store_word(prow, srow, e0 >> 3, lane, e0 < k, word, sign_byte(v[buf][c]));
       }
       if (tid == 0) scale[rr] = mx;
@@ -503,7 +515,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
       float sw2 = 0.0f, se2 = 0.0f;
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        const uint32_t word = encode_chunk(v[buf][c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts);
+        const uint32_t word = encode_chunk(v[buf][c], mx, r, fast, s_tab, sh3, mask8, ulo, s_pts);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float xv = v[buf][c].at(i);  // zero past k
@@ -812,8 +824,8 @@ __global__ __launch_bounds__(kGThreads) void quantize_grouped_rows(
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the table is written
   __builtin_amdgcn_s_barrier();
-  const int shift = g.shift;
-  const uint32_t nbase = (0u - (g.b0 >> g.shift)) << 3;
+  const int sh3 = g.shift - 3;
+  const uint32_t mask8 = (uint32_t)(g.size - 1) << 3;
   const float ulo = __uint_as_float(g.b0);
 
   if (cb >= nchunks) return;  // after the barrier: the block's table is shared
@@ -828,7 +840,7 @@ __global__ __launch_bounds__(kGThreads) void quantize_grouped_rows(
     const float m16 = f16_value(h);
     const bool fast = m16 > 0.0f;
     const float r = fast ? 1.0f / m16 : 0.0f;
-    const uint32_t word = encode_chunk(v[u], m16, r, fast, s_tab, shift, nbase, ulo, s_pts);
+    const uint32_t word = encode_chunk(v[u], m16, r, fast, s_tab, sh3, mask8, ulo, s_pts);
     const int64_t wi = valid ? (e0 >> 3) : 0;
     store_word(packed + wi, sign + (wi >> 2), 0, lane, valid, word, sign_byte(v[u]));
     if (valid && lane % kLanes == 0) scale16[e0 / GS] = (uint16_t)h;
@@ -900,6 +912,7 @@ bool bucket_grid_n(const float* t, int L, BucketGrid& g) {
       g.b0 = b0;
       g.shift = shift;
       g.nb = (int)nb;
+      g.size = table_slots(nb);
       return true;
     }
   }
@@ -919,14 +932,14 @@ __device__ void build_table_n(const float* pts, int L, BucketGrid g, uint2* tab)
       next = under ? next : c;
     }
     const uint32_t x = (next != kNoPoint && next - kGuard < hi) ? kGuard - next : kGuard - kNoPoint;
-    tab[b] = make_uint2(x, below);
+    tab[((g.b0 >> g.shift) + (uint32_t)b) & (uint32_t)(g.size - 1)] = make_uint2(x, below);
   }
 }
 
 // Codes of a lane's eight elements (fast path, then exact where flagged).
 template <typename T>
 __device__ __forceinline__ void codes8(const Slot<T>& v, float mx, float r, bool fast,
-                                       const uint2* tab, int shift, uint32_t nbase, float ulo,
+                                       const uint2* tab, int sh3, uint32_t mask8, float ulo,
                                        const float* pts, uint32_t (&q)[8]) {
   // As encode_chunk: the fast path runs everywhere, the exact one where flagged.
   const float rf = fast ? r : 1.0f;
@@ -935,7 +948,7 @@ __device__ __forceinline__ void codes8(const Slot<T>& v, float mx, float r, bool
   for (int i = 0; i < 8; ++i) {
     const float up = __builtin_amdgcn_fmed3f(fabsf(v.at(i)) * rf, ulo, 2.0f);
     const uint32_t ub = __float_as_uint(up);
-    const uint2 e = table_at(tab, ub, shift, nbase);
+    const uint2 e = table_at(tab, ub, sh3, mask8);
     const int d = (int)(ub + e.x);
     q[i] = e.y + (d >= (int)kGuard ? 1u : 0u);
     nr = min(nr, (uint32_t)d);
@@ -945,7 +958,7 @@ __device__ __forceinline__ void codes8(const Slot<T>& v, float mx, float r, bool
     for (int i = 0; i < 8; ++i) {
       float x = v.at(i);
       asm volatile("" : "+v"(x));
-      q[i] = code_exact(fabsf(x), mx, tab, shift, nbase, ulo, pts);
+      q[i] = code_exact(fabsf(x), mx, tab, sh3, mask8, ulo, pts);
     }
   }
 }
@@ -998,8 +1011,9 @@ __device__ __forceinline__ void store_bits(uint32_t* prow, uint32_t* srow, int b
   }
 }
 
-// The bucket table sits in dynamic LDS sized to the grid's g.nb entries (for
-// alpha = 0.73: 52, 149 and 342 for 3, 5 and 6 bits, against kMaxBucketsN),
+// The bucket table sits in dynamic LDS sized to the grid's slots (for
+// alpha = 0.73: 52, 149 and 342 buckets for 3, 5 and 6 bits, in 64, 256 and
+// 512 slots, against kMaxBucketsN),
 // so the table does not cap the blocks per CU.  kOne as in quantize_block_rows.
 extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
 
@@ -1041,8 +1055,8 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
   __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
   build_table_n(s_pts, L, g, s_tab);  // read after the first row-max barrier
-  const int shift = g.shift;
-  const uint32_t nbase = (0u - (g.b0 >> g.shift)) << 3;
+  const int sh3 = g.shift - 3;
+  const uint32_t mask8 = (uint32_t)(g.size - 1) << 3;
   const float ulo = __uint_as_float(g.b0);
 
   int64_t pend = -1;  // kErr: row whose partial sums wait in s_sum
@@ -1079,7 +1093,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
       for (int c = 0; c < NCT; ++c) {
         const int e0 = c * kBlockChunk + tid * 8;
         uint32_t q[8];
-        codes8(v[buf][c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts, q);
+        codes8(v[buf][c], mx, r, fast, s_tab, sh3, mask8, ulo, s_pts, q);
         store_bits<B>(prow, srow, e0 >> 5, lane, e0 < k, q, sign_byte(v[buf][c]));
       }
       if (tid == 0) scale[rr] = mx;
@@ -1090,7 +1104,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
         uint32_t q[8];
-        codes8(v[buf][c], mx, r, fast, s_tab, shift, nbase, ulo, s_pts, q);
+        codes8(v[buf][c], mx, r, fast, s_tab, sh3, mask8, ulo, s_pts, q);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float xv = v[buf][c].at(i);  // zero past k
@@ -1156,7 +1170,7 @@ template <typename T, int NCT, int B, bool kErr>
 hipError_t launch_bits_rows(const T* w, int64_t n, int64_t k, const DecisionPointsN& dp,
                             const BucketGrid& g, const LevelsN& lv, uint32_t* packed,
                             uint32_t* sign, float* scale, double* row_sums, hipStream_t stream) {
-  const size_t dyn = (size_t)g.nb * sizeof(uint2);
+  const size_t dyn = (size_t)g.size * sizeof(uint2);
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
