@@ -47,8 +47,8 @@ __device__ __forceinline__ void store_y(void* y, bool y_bf16, int64_t at, float 
 // blocks and the launch rather than to the loads.  A block owns 16 weight
 // rows (one fragment of
 // v_mfma_f32_16x16x32_bf16, W' the A operand, x^T the B operand) and all of k;
-// its eight waves take the 128-wide k blocks in turn and meet in LDS at the
-// end, so no partial sums leave the block.
+// its waves (sixteen up to 32 x rows, eight above) take the 128-wide k blocks
+// in turn and meet in LDS at the end, so no partial sums leave the block.
 //
 // Loads are laid out for the memory system, not for the MFMA: in a load, each
 // group of four lanes reads 64 contiguous bytes (packed words: lane l reads
@@ -83,7 +83,7 @@ constexpr int kSkDepth = 2;                     // k blocks in flight per wave o
 __device__ __forceinline__ int xs_off(int R, int c) { return R * kSkBlockK + ((c ^ (R & 15)) << 3); }
 
 // GS > 0: the group-wise form (group.hpp).  With kPre (the block's 16 x k/GS
-// groups are no more than its threads) each thread makes one group table at
+// groups are at most kSkPreGroups = 512) each of the first threads makes one group table at
 // block start, straight from the levels and the stored max, into LDS as byte
 // planes, group-major (a group's 16 rows adjacent, so a k block's reads hit 16
 // consecutive 32-byte records); a k block then costs a lane two ds_read_b128.
