@@ -486,7 +486,8 @@ def test_error_sums_match_oracle(gpu_lib, alpha, dtype, n, k):
     assert np.all(got[0] == 0.0)
 
 
-@pytest.mark.parametrize("dtype,n,k", [("bf16", 6007, 3840), ("bf16", 4099, 10240), ("f32", 2500, 1056)])
+@pytest.mark.parametrize("dtype,n,k", [("bf16", 6007, 3840), ("bf16", 4099, 10240), ("f32", 2500, 1056),
+                                       ("bf16", 9001, 1024)])
 def test_error_sums_agree_with_stored_form(gpu_lib, dtype, n, k):
     """More rows than the persistent grid (each block takes several rows, odd
     and even counts): the fused sums equal those of the library's own quantize +

@@ -392,6 +392,84 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
   }
 }
 
+// Error sums over rows of up to 2048 elements, one wave per row (the row in
+// registers, rows strided over the grid), for the same reason as the table
+// kernel above: the codes as there, each element then reconstructed from the
+// row's table L[q] = bf16(G_q m) in the wave's own LDS slot (a wave's LDS
+// operations complete in order, so no block barrier), and the row's
+// (sum w^2, sum (w - w')^2) accumulated in binary32 per lane and across the
+// wave (at most 2048 nonnegative terms), written as doubles.  Elements past k
+// are zero and add nothing.
+template <typename T, int NCH>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void error_rows_table(
+    const T* __restrict__ w, int64_t n, int k, DecisionPoints dp, BucketGrid g, Levels lv,
+    double* __restrict__ row_sums) {
+  __shared__ uint2 s_tab[kMaxBuckets];
+  __shared__ float s_pts[kLevels + 1];
+  __shared__ uint32_t s_recw[kRowsPerBlock][16];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
+  int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + wave;
+
+  Slot<T> v[NCH];
+  auto load_row = [&](int64_t rr) {
+    const T* wr = w + rr * (int64_t)k;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int e0 = c * kChunk + lane * 8;
+      if (e0 < k) v[c].load(wr + e0); else v[c].zero();
+    }
+  };
+  if (row < n) load_row(row);
+
+  build_table(dp, g, s_tab);
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int j = 0; j < kLevels; ++j) s_pts[j] = dp.t[j];
+    s_pts[kLevels] = 2.0f;
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the row loads stay in flight
+  __builtin_amdgcn_s_barrier();
+  const int sh3 = g.shift - 3;
+  const uint32_t mask8 = (uint32_t)(g.size - 1) << 3;
+  const float ulo = __uint_as_float(g.b0);
+
+  for (; row < n; row += stride) {
+    typename Slot<T>::Acc acc = Slot<T>::acc0();
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) v[c].absmax(acc);
+    const float mx = wave_max(Slot<T>::finish(acc));
+    const bool fast = mx >= 0x1p-125f && mx <= 0x1p125f;  // 1/m normal, u' <= 1 + ulps
+    const float r = 1.0f / mx;
+    if (lane < 16) s_recw[wave][lane] = lut_entry(lv, lane, mx);
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    float sw2 = 0.0f, se2 = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const uint32_t word = encode_chunk(v[c], mx, r, fast, s_tab, sh3, mask8, ulo, s_pts);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float xv = v[c].at(i);
+        // a nonzero code carries the weight's sign, so |w - w'| = ||w| - L[q]|
+        const float e = fabsf(xv) - __uint_as_float(s_recw[wave][(word >> (4 * i)) & 15u] << 16);
+        sw2 = fmaf(xv, xv, sw2);
+        se2 = fmaf(e, e, se2);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      sw2 += __shfl_xor(sw2, off, kWave);
+      se2 += __shfl_xor(se2, off, kWave);
+    }
+    if (lane == 0) {
+      row_sums[2 * row] = (double)sw2;
+      row_sums[2 * row + 1] = (double)se2;
+    }
+    if (row + stride < n) load_row(row + stride);
+  }
+}
+
 // ---------------------------------------------------------------- block-per-row kernel
 //
 // A block of 256 threads owns one row at a time: thread t holds elements
@@ -735,12 +813,26 @@ hipError_t dispatch_error(const T* w, int64_t n, int64_t k, const DecisionPoints
                           const Levels& lv, double* row_sums, hipStream_t stream) {
   BucketGrid g;
   if (!bucket_grid(dp, g)) return hipErrorNotSupported;
+  // rows of up to 2048 elements one to a wave, as for the codes
+  const int64_t nch = (k + kChunk - 1) / kChunk;
+  if (nch <= 4) {
+    const int64_t groups = (n + kRowsPerBlock - 1) / kRowsPerBlock;
+    const dim3 grid((unsigned)(groups < kMaxBlocks ? groups : kMaxBlocks));
+    const dim3 block(kRowsPerBlock * kWave);
+    if (nch <= 1)
+      hipLaunchKernelGGL((error_rows_table<T, 1>), grid, block, 0, stream, w, n, (int)k, dp, g, lv, row_sums);
+    else if (nch <= 2)
+      hipLaunchKernelGGL((error_rows_table<T, 2>), grid, block, 0, stream, w, n, (int)k, dp, g, lv, row_sums);
+    else
+      hipLaunchKernelGGL((error_rows_table<T, 4>), grid, block, 0, stream, w, n, (int)k, dp, g, lv, row_sums);
+    return hipGetLastError();
+  }
   const int64_t nct = (k + kBlockChunk - 1) / kBlockChunk;
 #define OPQ_ERR_CASE(N)                                                                        \
   if (nct <= N)                                                                                \
     return launch_block_rows<T, N, true>(w, n, k, dp, g, nullptr, nullptr, nullptr, stream, &lv, \
                                          row_sums);
-  OPQ_ERR_CASE(1) OPQ_ERR_CASE(2) OPQ_ERR_CASE(3) OPQ_ERR_CASE(4) OPQ_ERR_CASE(5)
+  OPQ_ERR_CASE(2) OPQ_ERR_CASE(3) OPQ_ERR_CASE(4) OPQ_ERR_CASE(5)
   OPQ_ERR_CASE(6) OPQ_ERR_CASE(8)
 #undef OPQ_ERR_CASE
   return hipErrorNotSupported;
