@@ -74,6 +74,9 @@ MUTATIONS = {
     # bit stream words in the wrong order
     "bits_word_order": ("out[:, w] |= (q[:, i] << np.uint64(off)) & np.uint64(0xFFFFFFFF)",
                         "out[:, -1 - w] |= (q[:, i] << np.uint64(off)) & np.uint64(0xFFFFFFFF)"),
+    # SNR as a ratio of amplitudes, and with the ratio upside down
+    "snr_amplitude": ("return 10.0 * math.log10(num / den)", "return 10.0 * math.log10(math.sqrt(num / den))"),
+    "snr_swapped": ("return 10.0 * math.log10(num / den)", "return 10.0 * math.log10(den / num)"),
     # 2^b levels instead of 2^b - 1
     "bits_levels": ("return (1 << bits) - 1", "return (1 << bits) - 1 + (bits != 4)"),
 }

@@ -428,10 +428,19 @@ def test_snr_closed_form():
     assert d[0, 0] == float(round_fraction(mf, 8))
     assert d[0, 1] == float(round_fraction(Fraction(8, 15) * mf, 8))
     assert not d[0, 2:].any()
-    snr = O.snr_db(w, d)
-    e = w.astype(np.float64) - d.astype(np.float64)
-    assert math.isclose(snr, 10 * math.log10(np.sum(w.astype(np.float64) ** 2) / np.sum(e ** 2)))
     assert O.snr_db(d, d) == math.inf
+
+
+def test_snr_exact_cases():
+    """Signal and error energies picked by hand so the ratio is a power of ten:
+    w = (3, 4), w' = (3, 3.5): 25 / 0.25 = 100, 20 dB; w = (1, 3), w' = (0, 3):
+    10 / 1, 10 dB; a tensor whose every error equals its own value: 0 dB.  A
+    swapped ratio, an amplitude (not energy) ratio, a missing factor 10 or the
+    error taken as w + w' each miss one of these."""
+    assert O.snr_db(np.array([[3.0, 4.0]]), np.array([[3.0, 3.5]])) == 20.0
+    assert O.snr_db(np.array([[1.0, 3.0]]), np.array([[0.0, 3.0]])) == 10.0
+    assert O.snr_db(np.array([[1.0, 3.0], [0.0, 0.0]]), np.array([[0.0, 3.0], [0.0, 0.0]])) == 10.0
+    assert O.snr_db(np.array([[0.5, -2.0]]), np.zeros((1, 2))) == 0.0
 
 
 # ------------------------------------------------------------------ error sums (alpha sweep)

@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void dequantize_bits_rows(
   if (row >= n) return;
   const int c0 = (int)(unit - row * segs) * kGroup;
   if (lane <= L) s_lut[wave][lane] = bf16_rne_from_f64(s_g[lane] * (double)scale[row]);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // one wave's LDS ops complete in order
+  wave_lds_sync();  // one wave's LDS ops complete in order
   const int nwords = k / 32 * B;
   const uint32_t* prow = packed + row * (int64_t)nwords;
   const uint32_t* srow = sign + row * (int64_t)(k / 32);

@@ -52,6 +52,24 @@ __device__ __forceinline__ uint32_t lut_entry(const Levels& lv, int q, float m) 
   return bf16_rne_from_f64(level_of(lv, q) * (double)m);
 }
 
+// Block barrier for data exchanged through LDS only.  The release fence makes
+// the wave's LDS writes complete (lgkmcnt 0) and, with the acquire fence after
+// the barrier, keeps the compiler from moving any LDS access across it; global
+// loads in flight stay in flight, which a full __syncthreads would wait for.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// LDS written by some lanes of a wave and read by others of the same wave: the
+// wave's LDS operations are done in issue order, so the wait and the
+// wavefront-scope fence (which orders the accesses for the compiler) suffice.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));

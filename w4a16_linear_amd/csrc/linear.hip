@@ -198,8 +198,7 @@ __global__ __launch_bounds__((sk_waves<NMB, GS, kPre>() * kWave)) void linear_sk
     s_lut[lane][4 + wave] = hi;
   }
   // LDS writes done and visible; the loads stay in flight.
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
   RowLut lut;
   if constexpr (GS == 0) {
     const uint4 lo = *reinterpret_cast<const uint4*>(&s_lut[r][0]);

@@ -341,8 +341,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
   }
   // The table is in LDS once lgkmcnt drains; the row loads stay in flight
   // (a full __syncthreads would wait for them too).
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt and expcnt left open
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
   const int sh3 = g.shift - 3;
   const uint32_t mask8 = (uint32_t)(g.size - 1) << 3;
   const float ulo = __uint_as_float(g.b0);
@@ -429,8 +428,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void error_rows_table(
     for (int j = 0; j < kLevels; ++j) s_pts[j] = dp.t[j];
     s_pts[kLevels] = 2.0f;
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the row loads stay in flight
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
   const int sh3 = g.shift - 3;
   const uint32_t mask8 = (uint32_t)(g.size - 1) << 3;
   const float ulo = __uint_as_float(g.b0);
@@ -443,7 +441,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void error_rows_table(
     const bool fast = mx >= 0x1p-125f && mx <= 0x1p125f;  // 1/m normal, u' <= 1 + ulps
     const float r = 1.0f / mx;
     if (lane < 16) s_recw[wave][lane] = lut_entry(lv, lane, mx);
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+    wave_lds_sync();
     float sw2 = 0.0f, se2 = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
@@ -566,8 +564,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
     for (int c = 0; c < NCT; ++c) v[buf][c].absmax(acc);
     float mx = wave_max(Slot<T>::finish(acc));
     if (lane == 0) s_wmax[ms][wave] = mx;
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     mx = s_wmax[ms][0];
 #pragma unroll
     for (int q = 1; q < kBlockThreads / kWave; ++q) mx = fmaxf(mx, s_wmax[ms][q]);
@@ -589,7 +586,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
       // slot (lanes 0..15 one entry each): LDS ops of one wave complete in
       // order, so no block barrier is needed before the lookups.
       if (lane < 16) s_recw[wave][lane] = lut_entry(lv, lane, mx);
-      __builtin_amdgcn_s_waitcnt(0xC07F);
+      wave_lds_sync();
       float sw2 = 0.0f, se2 = 0.0f;
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
@@ -652,8 +649,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
   }
   if constexpr (kErr) {
     // the last row's partials: which slot holds them follows the row count
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     const int64_t cnt = blockIdx.x < n ? (n - 1 - blockIdx.x) / stride + 1 : 0;
     flush_sums((int)((cnt - 1) & 1));
   }
@@ -914,8 +910,7 @@ __global__ __launch_bounds__(kGThreads) void quantize_grouped_rows(
     for (int j = 0; j < kLevels; ++j) s_pts[j] = dp.t[j];
     s_pts[kLevels] = 2.0f;
   }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the table is written
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
   const int sh3 = g.shift - 3;
   const uint32_t mask8 = (uint32_t)(g.size - 1) << 3;
   const float ulo = __uint_as_float(g.b0);
@@ -1144,8 +1139,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
   if (tid < L) s_pts[tid] = dp.t[tid];
   if (tid == L) s_pts[L] = 2.0f;
   if (kErr && tid <= L) s_g[tid] = lv.g[tid];
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
   build_table_n(s_pts, L, g, s_tab);  // read after the first row-max barrier
   const int sh3 = g.shift - 3;
   const uint32_t mask8 = (uint32_t)(g.size - 1) << 3;
@@ -1170,8 +1164,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
     for (int c = 0; c < NCT; ++c) v[buf][c].absmax(acc);
     float mx = wave_max(Slot<T>::finish(acc));
     if (lane == 0) s_wmax[ms][wave] = mx;
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     mx = s_wmax[ms][0];
 #pragma unroll
     for (int q = 1; q < kBlockThreads / kWave; ++q) mx = fmaxf(mx, s_wmax[ms][q]);
@@ -1191,7 +1184,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
       if (tid == 0) scale[rr] = mx;
     } else {
       if (lane <= L) s_recw[wave][lane] = bf16_rne_from_f64(s_g[lane] * (double)mx);
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // one wave's LDS ops complete in order
+      wave_lds_sync();  // one wave's LDS ops complete in order
       float sw2 = 0.0f, se2 = 0.0f;
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
@@ -1233,8 +1226,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
     }
   }
   if constexpr (kErr) {
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
+    lds_barrier();
     const int64_t cnt = blockIdx.x < n ? (n - 1 - blockIdx.x) / stride + 1 : 0;
     flush_sums((int)((cnt - 1) & 1));
   }

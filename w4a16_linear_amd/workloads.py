@@ -2,9 +2,9 @@
 
 These generators only draw numbers: they hold none of the quantizer's
 arithmetic, and both the tests' oracle side and the GPU side get their inputs
-from here.  Every tensor is drawn with numpy's PCG64 ``default_rng(seed)`` in
-float64, cast to float32, and (for bf16 tensors) rounded to bfloat16 by torch's
-cast.  Hidden size 3840, fused QKV 11520, FFN 10240 (up and gate fused to
+from here.  Every host tensor is drawn with numpy's PCG64 ``default_rng(seed)``
+in float64, cast to float32, and (for bf16 tensors) rounded to bfloat16 by
+torch's cast; ``student_t_device`` draws the whole-model weights on the GPU.  Hidden size 3840, fused QKV 11520, FFN 10240 (up and gate fused to
 20480), 30 blocks: the model card's Z-Image transformer is a 6.02B-parameter DiT
 but the card gives no layer shapes, so these shapes stand in for it.
 """
@@ -54,6 +54,23 @@ def normal_laplace(seed: int, shape, std: float = 0.02, p_tail: float = 0.01,
     tail = rng.random(shape) < p_tail
     w[tail] = rng.laplace(0.0, b, size=int(tail.sum()))
     return w.astype(np.float32)
+
+
+def student_t_device(seed: int, shape, device, std: float = 0.02, nu: int = 4) -> torch.Tensor:
+    """Student-t(nu) at standard deviation std drawn on `device` as bfloat16:
+    z / sqrt(chi2_nu / nu), with z and the nu squared normals of chi2 from
+    torch's generator seeded with `seed` (Philox on the GPU).  The same
+    distribution as ``student_t`` but other numbers; it serves the whole-model
+    workload, whose 5.3 B values would take minutes to draw on the host."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    z = torch.randn(shape, device=device, generator=g)
+    chi2 = torch.zeros(shape, device=device)
+    for _ in range(nu):
+        chi2.add_(torch.randn(shape, device=device, generator=g).square_())
+    w = z.mul_(torch.rsqrt(chi2.div_(nu))).mul_(std / math.sqrt(nu / (nu - 2.0)))
+    del chi2
+    return w.to(torch.bfloat16)
 
 
 def normal(seed: int, shape, std: float = 1.0) -> np.ndarray:
@@ -140,11 +157,16 @@ BLOCK_LAYERS = (("qkv", QKV, HIDDEN), ("o", HIDDEN, HIDDEN), ("up_gate", FFN_UPG
                 ("down", HIDDEN, FFN))
 
 
+def model_seed(block: int, layer: int) -> int:
+    """Seed of layer `layer` (0..3: QKV, O, up/gate, down) of block `block`."""
+    return 5000 + 4 * block + layer
+
+
 def _c5(blocks: int = BLOCKS) -> Config:
     layers = []
     for b in range(blocks):
         for i, (nm, n, k) in enumerate(BLOCK_LAYERS):
-            seed = 5000 + 4 * b + i
+            seed = model_seed(b, i)
             layers.append(Layer(f"block{b}.{nm}", n, k,
                                 (lambda s=seed, n=n, k=k: student_t(s, (n, k))), "bf16"))
     return Config("model", f"whole-model quantize/dequant pass: {blocks} DiT blocks "
