@@ -1,20 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the OPQ W4A16 hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic input:
-    opq_quantize(W bf16) -> opq_dequantize -> opq_linear(x, stored W)
-on the skinny DiT-shaped workload (W 3840x3840 Student-t(4) std 0.02,
-x bf16 [32, 3840], alpha 0.73) unless --workload names another.
+One step = one pass of the whole path over one batch of synthetic input.  By
+default the workload is the DiT FFN pair, the largest configuration that runs
+all three kernels on one GPU:
+
+    up/gate: opq_quantize(W 20480x3840 bf16) -> opq_dequantize -> opq_linear(x [4096, 3840])
+    down:    opq_quantize(W 3840x10240 bf16) -> opq_dequantize -> opq_linear(x [4096, 10240])
+
+(weights N(0, 0.02^2) with 1% Laplace(0, 0.02) tails, alpha 0.73).
+--workload skinny|qkv|tiny|ffn_up|ffn_down selects one of the other shapes.
 
 Prints ONE JSON line.  `value` is the step's fraction of the MI355X roofline
 in percent: the sum of each kernel's ideal time (algorithmic bytes / 8 TB/s,
-or flops / 2.5 PFLOP/s for MFMA-bound shapes) over the measured step time.
+or flops / 2.5 PFLOP/s for the MFMA-bound linear) over the measured step time.
 The timed region is exactly --steps steps between two HIP events.  Per-kernel
-durations (under "kernels", with absolute GB/s and TFLOP/s) come from a
-second pass: 7 batches of --steps back-to-back launches of one kernel, median
-batch; the "roofline" object is the slowest kernel's.  Inputs are resident in
-HBM before timing starts; every launch rotates to another set of input/output
-buffers so that the 256 MB Infinity Cache cannot serve repeats.
+durations (under "kernels", with absolute GB/s and TFLOP/s) come from a second
+pass: 7 batches of --steps back-to-back launches of one kernel on the same
+stream, median batch; the "roofline" object is the slowest kernel's (the
+up/gate linear layer by default).  Inputs are resident in HBM before timing
+starts; every launch rotates to another set of input/output buffers so that
+the 256 MB Infinity Cache cannot serve repeats.  The default run also times
+the whole-model quantize/dequantize pass ("model_pass") and the CPU oracle on
+the same workload ("cpu_baseline").
 """
 from __future__ import annotations
 
@@ -22,7 +30,6 @@ import argparse
 import hashlib
 import json
 import os
-import platform
 import sys
 import time
 
@@ -37,15 +44,15 @@ PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "w4a16_linear_amd", "csrc")
 KERNEL_SOURCE = {"quantize": "quantize.hip", "dequantize": "dequantize.hip",
                  "linear": "linear.hip"}
+WORKLOADS = ["ffn", "skinny", "qkv", "ffn_up", "ffn_down", "tiny", "model"]
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="skinny",
-                    choices=["skinny", "qkv", "ffn_up", "ffn_down", "tiny", "model"])
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="ffn", choices=WORKLOADS)
     ap.add_argument("--alpha", type=float, default=0.73)
     ap.add_argument("--group", type=int, default=0, choices=[0, 32, 64, 128, 256],
                     help="0: one float32 max per row; else the group-wise form (float16 max "
@@ -55,7 +62,9 @@ def parse():
                          "linear layer runs on 4-bit codes)")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for > 768 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-model-pass", action="store_true",
+                    help="leave out the whole-model quantize/dequantize pass")
+    ap.add_argument("--no-copy", action="store_true", help="leave out the same-bytes copies")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, 5 plain device copies of this many MiB (counter scaling)")
     return ap.parse_args()
@@ -63,19 +72,26 @@ def parse():
 
 # ------------------------------------------------------------------ workload
 
-def workload(name):
+def workload_layers(name):
+    """[(tag, Layer)]: the layers one step runs, tagged as the counter
+    summaries in profiles/ are named."""
     from w4a16_linear_amd import workloads as WL
-    if name == "skinny":
-        L = WL.config("skinny").layers[0]
-    elif name == "qkv":
-        L = WL.config("qkv").layers[0]
-    elif name == "ffn_up":
-        L = WL.config("ffn").layers[0]
-    elif name == "ffn_down":
-        L = WL.config("ffn").layers[1]
-    else:
-        L = WL.config("tiny").layers[0]
-    return L
+    if name == "ffn":
+        up, down = WL.config("ffn").layers
+        return [("ffn_up", up), ("ffn_down", down)]
+    if name == "ffn_up":
+        return [("ffn_up", WL.config("ffn").layers[0])]
+    if name == "ffn_down":
+        return [("ffn_down", WL.config("ffn").layers[1])]
+    return [(name, WL.config(name).layers[0])]
+
+
+def workload_title(name):
+    from w4a16_linear_amd import workloads as WL
+    return {"ffn": WL.config("ffn").title, "skinny": WL.config("skinny").title,
+            "qkv": WL.config("qkv").title, "tiny": WL.config("tiny").title,
+            "ffn_up": "FFN up/gate: x bf16 [4096, 3840] x W 20480x3840",
+            "ffn_down": "FFN down: x bf16 [4096, 10240] x W 3840x10240"}[name]
 
 
 def algorithmic(m, n, k, w_bytes, group=0, bits=4):
@@ -106,11 +122,11 @@ def source_hash(kind):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kind, workload_name):
-    """HBM bytes per launch from the committed counter summary, or None when
-    there is none or the kernel source changed since it was taken.  Grouped
-    runs are named <workload>_g<group>."""
-    path = os.path.join(PROFILES, f"{kind}_{workload_name}_traffic.txt")
+def measured_traffic(kind, tag):
+    """HBM bytes per launch from the committed counter summary
+    profiles/<kernel>_<tag>_traffic.txt, or None when there is none or the
+    kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kind}_{tag}_traffic.txt")
     if not os.path.exists(path):
         return None
     vals = {}
@@ -126,54 +142,95 @@ def measured_traffic(kind, workload_name):
         return None
 
 
+# ------------------------------------------------------------------ host description
+
+def host_description():
+    """CPU model, thread count, numpy and BLAS of the host the oracle runs on."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas = [{"api": d.get("internal_api"), "version": d.get("version"),
+             "threads": d.get("num_threads")}
+            for d in threadpool_info() if d.get("user_api") == "blas"]
+    return {"cpu_model": model, "nproc": os.cpu_count(), "numpy": np.__version__,
+            "blas": blas}
+
+
 # ------------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(L, x_bits, w_vals, alpha, seconds, ideal_total_us, group=0, threads=1):
-    """The oracle, as it stands, over the whole workload, repeated until
-    `seconds` have passed (at least once).  threads = 1: one thread, BLAS
-    limited to one; threads > 1: the weight's rows split into that many
-    blocks run by a thread pool (NumPy releases the GIL), each block's BLAS
-    limited to one thread."""
+def cpu_baseline(layers, alpha, ideal_total_us, group=0, threads=1, x_rows=512):
+    """The oracle, as it stands, on the same workload.  Per layer: quantize and
+    dequantize of the whole weight, and the linear layer on a seeded subset of
+    `x_rows` activation rows (all rows when there are fewer), scaled to the
+    full row count.  threads = 1: one thread, BLAS limited to one; threads >
+    1: the weight's rows split into that many blocks run by a thread pool
+    (NumPy releases the GIL), each block's BLAS limited to one thread."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     import oracle as O
+    from w4a16_linear_amd import workloads as WL
 
-    def block(rows):
-        w = w_vals[rows]
-        if group:
-            p, s, m = O.quantize_grouped(w, alpha, group)
-            d = O.dequantize_grouped(p, s, m, alpha, group)
-        else:
-            p, s, m = O.quantize(w, alpha)
-            d = O.dequantize(p, s, m, alpha)
-        return O.linear(x_bits, d)
-
-    blocks = [sl for sl in np.array_split(np.arange(L.n), threads) if len(sl)]
-    reps = 0
+    t_step = 0.0
+    parts = []
     with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=threads) as pool:
-        t0 = time.perf_counter()
-        while True:
-            list(pool.map(block, blocks))
-            reps += 1
-            el = time.perf_counter() - t0
-            if el >= seconds or reps >= 20:
-                break
-    per_step = el / reps
+        for tag, L in layers:
+            w32 = L.make_w()
+            if L.w_dtype == "bf16":
+                w_vals = O.bf16_bits_to_f32(WL.bf16_bits(WL.to_bf16(w32)))
+            else:
+                w_vals = np.ascontiguousarray(w32, np.float32)
+            del w32
+            rows_x = np.sort(np.random.default_rng(L.m + L.k).choice(L.m, min(x_rows, L.m),
+                                                                     replace=False))
+            xb = WL.bf16_bits(WL.to_bf16(L.make_x()))[rows_x]
+
+            def block(rows):
+                w = w_vals[rows]
+                t0 = time.perf_counter()
+                if group:
+                    p, s, m = O.quantize_grouped(w, alpha, group)
+                    d = O.dequantize_grouped(p, s, m, alpha, group)
+                else:
+                    p, s, m = O.quantize(w, alpha)
+                    d = O.dequantize(p, s, m, alpha)
+                t1 = time.perf_counter()
+                O.linear(xb, d)
+                return t1 - t0, time.perf_counter() - t1
+
+            blocks = [sl for sl in np.array_split(np.arange(L.n), threads) if len(sl)]
+            t0 = time.perf_counter()
+            res = list(pool.map(block, blocks))
+            wall = time.perf_counter() - t0
+            # wall time of the pool, split between the two phases in the
+            # proportion the blocks measured, the linear part scaled to every x row
+            qd = sum(r[0] for r in res)
+            lin = sum(r[1] for r in res)
+            frac_lin = lin / (qd + lin) if qd + lin > 0 else 0.0
+            scale_x = L.m / len(rows_x)
+            t_layer = wall * (1.0 - frac_lin) + wall * frac_lin * scale_x
+            t_step += t_layer
+            parts.append(f"{tag}: quantize+dequantize of all {L.n}x{L.k} weights, linear on "
+                         f"{len(rows_x)} of {L.m} x rows (x{scale_x:g}), {wall:.1f} s measured")
     how = "one thread" if threads == 1 else f"{threads} threads over row blocks"
     return {
-        "value": round(100.0 * ideal_total_us * 1e-6 / per_step, 6),
+        "value": round(100.0 * ideal_total_us * 1e-6 / t_step, 6),
         "unit": "% of MI355X roofline",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{reps} full oracle step(s) (quantize, dequantize, linear) on the whole "
-                  f"{L.n}x{L.k} weight and x[{L.m},{L.k}], {how}, {el:.1f} s total, "
-                  f"{per_step * 1e3:.1f} ms per step",
-        "ms_per_step": round(per_step * 1e3, 3),
-        "host_cpu": platform.processor() or platform.machine(),
-        "host_threads_available": os.cpu_count(),
+        "sample": f"{how}; " + "; ".join(parts) + f"; {t_step:.1f} s per step",
+        "ms_per_step": round(t_step * 1e3, 1),
+        "host": host_description(),
     }
 
 
@@ -196,57 +253,67 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.workload == "model":
-        return model_pass(args, dev)
-    L = workload(args.workload)
-    m, n, k = L.m, L.n, L.k
+        out = model_pass(args, dev)
+        out.update({"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                    "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                    "dtype": "bf16", "cpu_baseline": None, "env": run_env(dev)})
+        print(json.dumps(out), flush=True)
+        return
+
     alpha = args.alpha
-
-    w32 = L.make_w()
-    if L.w_dtype == "bf16":
-        w_host = WL.to_bf16(w32)
-        w_vals = None
-        w_bytes = 2
-    else:
-        w_host = torch.from_numpy(w32)
-        w_bytes = 4
-    x_host = WL.to_bf16(L.make_x())
-
     group, bits = args.group, args.bits
-    if group and k % group:
-        print(f"--group {group} does not divide k={k}", file=sys.stderr)
-        sys.exit(2)
     if group and bits != 4:
         print("--group and --bits other than 4 do not combine", file=sys.stderr)
         sys.exit(2)
-    alg = algorithmic(m, n, k, w_bytes, group, bits)
-    per_set = (n * k * w_bytes + n * k * 0.625 + 4 * n + n * k * 2 + m * k * 2 + m * n * 4)
-    rot = args.rotate or max(2, int(np.ceil(800e6 / per_set)))
-    sets = []
-    for _ in range(rot):
-        w = w_host.to(dev)
-        if bits != 4:
-            qw = opq.BitsWeight(torch.empty((n, k * bits // 32), dtype=torch.int32, device=dev),
-                                torch.empty((n, k // 32), dtype=torch.int32, device=dev),
-                                torch.empty((n,), dtype=torch.float32, device=dev), bits)
-        elif group:
-            qw = opq.GroupedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
-                                   torch.empty((n, k // 32), dtype=torch.int32, device=dev),
-                                   torch.empty((n, k // group), dtype=torch.float16, device=dev),
-                                   group)
-        else:
-            qw = opq.QuantizedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
-                                     torch.empty((n, k // 32), dtype=torch.int32, device=dev),
-                                     torch.empty((n,), dtype=torch.float32, device=dev))
-        d = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
-        x = x_host.to(dev)
-        y = torch.empty((m, n), dtype=torch.float32, device=dev)
-        sets.append((w, qw, d, x, y))
-    torch.cuda.synchronize()
-
+    layers = workload_layers(args.workload)
+    kinds = ["quantize", "dequantize", "linear"] if bits == 4 else ["quantize", "dequantize"]
     stream = torch.cuda.current_stream(dev)
 
-    def launch(kind, i):
-        w, qw, d, x, y = sets[i % rot]
+    # Per layer: host tensors once, then `rot` device sets of every buffer.
+    plan = []
+    for tag, L in layers:
+        m, n, k = L.m, L.n, L.k
+        if group and k % group:
+            print(f"--group {group} does not divide k={k}", file=sys.stderr)
+            sys.exit(2)
+        w32 = L.make_w()
+        if L.w_dtype == "bf16":
+            w_host, w_bytes = WL.to_bf16(w32), 2
+        else:
+            w_host, w_bytes = torch.from_numpy(w32), 4
+        del w32
+        x_host = WL.to_bf16(L.make_x())
+        alg = algorithmic(m, n, k, w_bytes, group, bits)
+        # enough sets that every HBM-bound kernel's buffers exceed 768 MB between repeats
+        least = min(alg["quantize"]["bytes"], alg["dequantize"]["bytes"],
+                    alg["linear"]["bytes"])
+        rot = args.rotate or max(2, int(np.ceil(800e6 / least)))
+        sets = []
+        for _ in range(rot):
+            w = w_host.to(dev)
+            if bits != 4:
+                qw = opq.BitsWeight(torch.empty((n, k * bits // 32), dtype=torch.int32, device=dev),
+                                    torch.empty((n, k // 32), dtype=torch.int32, device=dev),
+                                    torch.empty((n,), dtype=torch.float32, device=dev), bits)
+            elif group:
+                qw = opq.GroupedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
+                                       torch.empty((n, k // 32), dtype=torch.int32, device=dev),
+                                       torch.empty((n, k // group), dtype=torch.float16,
+                                                   device=dev), group)
+            else:
+                qw = opq.QuantizedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
+                                         torch.empty((n, k // 32), dtype=torch.int32, device=dev),
+                                         torch.empty((n,), dtype=torch.float32, device=dev))
+            d = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+            x = x_host.to(dev)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            sets.append((w, qw, d, x, y))
+        plan.append({"tag": tag, "L": L, "alg": alg, "rot": rot, "sets": sets,
+                     "w_bytes": w_bytes})
+    torch.cuda.synchronize()
+
+    def launch(p, kind, i):
+        w, qw, d, x, y = p["sets"][i % p["rot"]]
         if kind == "quantize":
             if bits != 4:
                 opq.quantize_bits(w, alpha, bits, out=qw)
@@ -259,11 +326,10 @@ def main():
         else:
             opq.linear(x, qw, alpha, out=y)
 
-    kinds = ["quantize", "dequantize", "linear"] if bits == 4 else ["quantize", "dequantize"]
-
     def step(i):
-        for kind in kinds:
-            launch(kind, i)
+        for p in plan:
+            for kind in kinds:
+                launch(p, kind, i)
 
     for i in range(args.warmup):
         step(i)
@@ -282,56 +348,61 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(stop) / args.steps
 
+    def timed(fn, reps):
+        """Median over 7 batches of `reps` back-to-back calls, microseconds per call."""
+        per = []
+        for b in range(7):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(reps):
+                fn(b * reps + i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            per.append(e0.elapsed_time(e1) / reps * 1e3)
+        return float(np.median(per))
+
     # Per-kernel duration: batches of K back-to-back launches of one kernel
     # (same rotation of buffers), median over 7 batches.
     kern = {}
     ideal_total = 0.0
-    for kind in kinds:
-        per = []
-        for b in range(7):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(args.steps):
-                launch(kind, b * args.steps + i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            per.append(e0.elapsed_time(e1) / args.steps * 1e3)
-        us = float(np.median(per))
-        ideal, bound = ideal_us(kind, alg[kind], m)
-        ideal_total += ideal
-        a = alg[kind]
-        rec = {"us": round(us, 3), "bound": bound, "ideal_us": round(ideal, 3),
-               "frac": round(ideal / us, 4),
-               "GBps": round(a["bytes"] / (us * 1e-6) / 1e9, 1),
-               "algorithmic_bytes": int(a["bytes"])}
-        if a["flops"]:
-            rec["TFLOPs"] = round(a["flops"] / (us * 1e-6) / 1e12, 2)
-        kern[kind] = rec
+    single = len(plan) == 1
+    for p in plan:
+        L = p["L"]
+        for kind in kinds:
+            us = timed(lambda i, p=p, kind=kind: launch(p, kind, i), args.steps)
+            ideal, bound = ideal_us(kind, p["alg"][kind], L.m)
+            ideal_total += ideal
+            a = p["alg"][kind]
+            rec = {"us": round(us, 3), "bound": bound, "ideal_us": round(ideal, 3),
+                   "frac": round(ideal / us, 4),
+                   "GBps": round(a["bytes"] / (us * 1e-6) / 1e9, 1),
+                   "algorithmic_bytes": int(a["bytes"]), "shape": [L.m, L.n, L.k]}
+            if a["flops"]:
+                rec["TFLOPs"] = round(a["flops"] / (us * 1e-6) / 1e12, 2)
+                rec["algorithmic_flops"] = int(a["flops"])
+            rec["tag"] = p["tag"]
+            kern[kind if single else f"{p['tag']}.{kind}"] = rec
 
-    # The practical ceiling at each kernel's size: a plain device copy that reads
-    # and writes the kernel's algorithmic bytes, over enough buffer pairs to
-    # defeat the 256 MB cache, timed the same way.  Left out of counter runs
-    # (--copy-mib), whose only copies calibrate the byte counters.
-    for kind in (kinds if not args.copy_mib else []):
-        half = int(alg[kind]["bytes"]) // 2
-        pairs = max(2, int(np.ceil(800e6 / (2 * half))))
-        bufs = [(torch.empty(half, dtype=torch.uint8, device=dev),
-                 torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(pairs)]
-        per = []
-        for b in range(7):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(args.steps):
-                dst, src = bufs[(b * args.steps + i) % pairs]
+    # The practical ceiling at each HBM-bound kernel's size: a plain device copy
+    # that reads and writes the kernel's algorithmic bytes, over enough buffer
+    # pairs to defeat the 256 MB cache, timed the same way.  Left out of counter
+    # runs (--copy-mib), whose only copies calibrate the byte counters.
+    if not (args.copy_mib or args.no_copy):
+        for name, rec in kern.items():
+            if rec["bound"] != "hbm":
+                continue
+            half = rec["algorithmic_bytes"] // 2
+            pairs = max(2, int(np.ceil(800e6 / (2 * half))))
+            bufs = [(torch.empty(half, dtype=torch.uint8, device=dev),
+                     torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(pairs)]
+
+            def cp(i):
+                dst, src = bufs[i % pairs]
                 dst.copy_(src)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            per.append(e0.elapsed_time(e1) / args.steps * 1e3)
-        kern[kind]["same_bytes_copy_us"] = round(float(np.median(per)), 3)
-        del bufs
-    torch.cuda.synchronize()
+            rec["same_bytes_copy_us"] = round(timed(cp, args.steps), 3)
+            del bufs
+        torch.cuda.synchronize()
 
     if args.copy_mib:
         # A plain device copy of known size, for scaling the HBM byte counters.
@@ -342,7 +413,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    dom = max(kinds, key=lambda kk: kern[kk]["us"])
+    dom = max(kern, key=lambda kk: kern[kk]["us"])
     dk = kern[dom]
     if dk["bound"] == "mfma":
         roof = {"bound": "mfma", "achieved": dk["TFLOPs"], "peak": BF16_PEAK_TFLOPS,
@@ -350,13 +421,17 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": dk["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dk["GBps"] / HBM_PEAK_GBS, 4)}
-    roof["kernel"] = dom
-    wl_name = (f"{args.workload}_g{group}" if group else
-               f"{args.workload}_b{bits}" if bits != 4 else args.workload)
-    roof["traffic"] = measured_traffic(dom, wl_name)
+    kind_dom = dom.split(".")[-1]
+    roof["kernel"] = f"{dk['tag']}.{kind_dom}"
+    suffix = f"_g{group}" if group else (f"_b{bits}" if bits != 4 else "")
+    roof["traffic"] = measured_traffic(kind_dom, dk["tag"] + suffix)
+    roof["per_launch"] = ({"flops": dk.get("algorithmic_flops"), "us": dk["us"]}
+                          if dk["bound"] == "mfma" else
+                          {"bytes": dk["algorithmic_bytes"], "us": dk["us"]})
 
     value = 100.0 * (ideal_total * 1e-3) / ms_step
-
+    shapes = {p["tag"]: {"m": p["L"].m, "n": p["L"].n, "k": p["L"].k, "w_dtype": p["L"].w_dtype,
+                         "rotating_sets": p["rot"]} for p in plan}
     out = {
         "metric": METRIC,
         "value": round(value, 3),
@@ -370,31 +445,32 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{args.workload}: {WL_title(args.workload)}", "m": m, "n": n,
-                   "k": k, "w_dtype": L.w_dtype, "alpha": alpha, "rotating_sets": rot,
+        "config": {"workload": f"{args.workload}: {workload_title(args.workload)}",
+                   "layers": shapes, "alpha": alpha,
                    "scales": (f"float16 per group of {group}" if group else "float32 per row"),
                    "bits": bits,
-                   "step": ("quantize -> dequantize -> linear" if bits == 4
-                            else "quantize -> dequantize")},
+                   "step": ("per layer: quantize -> dequantize -> linear" if bits == 4
+                            else "per layer: quantize -> dequantize")},
         "roofline": roof,
         "kernels": kern,
         "kernels_sum_us": round(sum(kk["us"] for kk in kern.values()), 3),
         "wall_s": round(wall, 3),
         "env": run_env(dev),
     }
-    if not args.no_cpu_baseline and bits == 4:
-        import oracle as O
-        xb = WL.bf16_bits(x_host)
-        wv = (O.bf16_bits_to_f32(WL.bf16_bits(w_host)) if L.w_dtype == "bf16"
-              else w_host.numpy())
-        out["cpu_baseline"] = cpu_baseline(L, xb, wv, alpha, args.cpu_seconds, ideal_total,
-                                           group)
+    default_run = not (args.no_cpu_baseline or args.copy_mib)
+    if default_run:
         # with the CPU baseline (the default run; profiled runs skip both)
         out["env"]["gfx_clock_under_load"] = gfx_clock_under_load(step)
+    del plan
+    torch.cuda.empty_cache()
+    if not (args.no_model_pass or args.copy_mib) and group == 0 and bits == 4:
+        out["model_pass"] = model_pass(args, dev)
+        torch.cuda.empty_cache()
+    if default_run and bits == 4:
+        out["cpu_baseline"] = cpu_baseline(layers, alpha, ideal_total, group)
         threads = min(os.cpu_count() or 1, 16)
         if threads > 1:
-            out["cpu_baseline_pool"] = cpu_baseline(L, xb, wv, alpha, args.cpu_seconds,
-                                                    ideal_total, group, threads)
+            out["cpu_baseline_pool"] = cpu_baseline(layers, alpha, ideal_total, group, threads)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
@@ -402,45 +478,23 @@ def main():
 
 # ------------------------------------------------------------------ whole-model pass
 
-def student_t_gpu(seed, shape, dev, std=0.02, nu=4):
-    """Student-t(4) at std 0.02 drawn on the GPU (z / sqrt(chi2_4 / 4)), as bf16.
-
-    Same distribution and per-layer seed as the host recipe of the parity
-    tests, drawn with torch's Philox generator so that 5.3 B values take well
-    under a second."""
-    g = torch_gen(dev, seed)
-    import torch
-    z = torch.randn(shape, device=dev, generator=g)
-    chi2 = torch.zeros(shape, device=dev)
-    for _ in range(nu):
-        chi2.add_(torch.randn(shape, device=dev, generator=g).square_())
-    w = z.mul_(torch.rsqrt(chi2.div_(nu))).mul_(std / (nu / (nu - 2)) ** 0.5)
-    del chi2
-    return w.to(torch.bfloat16)
-
-
-def torch_gen(dev, seed):
-    import torch
-    g = torch.Generator(device=dev)
-    g.manual_seed(seed)
-    return g
-
-
 def model_pass(args, dev):
-    """One step = quantize + dequantize of every layer of 30 synthetic DiT
+    """One pass = quantize + dequantize of every layer of 30 synthetic DiT
     blocks (QKV 11520x3840, O 3840x3840, FFN 20480x3840 and 3840x10240): 5.308 B
-    bf16 weights.  Also reports SNR(alpha) - SNR(1) over the whole model."""
+    bf16 weights, drawn on the device per layer seed.  Also SNR(alpha) - SNR(1)
+    over the whole model, an alpha sweep of the error sums, and SNR by code
+    width.  Returns a dict (reporting, not the headline)."""
     import numpy as np
     import torch
     from w4a16_linear_amd import opq
     from w4a16_linear_amd import workloads as WL
 
     alpha = args.alpha
-    shapes = [(f"block{b}.{nm}", 5000 + 4 * b + i, n, k)
+    shapes = [(f"block{b}.{nm}", WL.model_seed(b, i), n, k)
               for b in range(WL.BLOCKS) for i, (nm, n, k) in enumerate(WL.BLOCK_LAYERS)]
     weights, qws, outs = [], [], {}
     for _, seed, n, k in shapes:
-        weights.append(student_t_gpu(seed, (n, k), dev))
+        weights.append(WL.student_t_device(seed, (n, k), dev))
         qws.append(opq.QuantizedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
                                        torch.empty((n, k // 32), dtype=torch.int32, device=dev),
                                        torch.empty((n,), dtype=torch.float32, device=dev)))
@@ -460,26 +514,25 @@ def model_pass(args, dev):
         for qw, (_, _, n, k) in zip(qws, shapes):
             opq.dequantize(qw, a, out=outs[(n, k)])
 
-    for _ in range(args.warmup):
+    reps = max(1, min(args.steps, 10))
+    for _ in range(max(1, min(args.warmup, 3))):
         quant_all(alpha)
         dequant_all(alpha)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
+    for _ in range(reps):
         quant_all(alpha)
         dequant_all(alpha)
     stop.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(stop) / args.steps
+    ms_pass = start.elapsed_time(stop) / reps
 
     kern = {}
     for name, fn, alg in (("quantize", quant_all, alg_q), ("dequantize", dequant_all, alg_d)):
         per = []
-        for _ in range(3):
+        for _ in range(5):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -564,23 +617,17 @@ def model_pass(args, dev):
                            "us": round(e0.elapsed_time(e1) * 1e3, 1)}
         widths[str(b)] = row
     dom = max(kern, key=lambda kk: kern[kk]["us"])
-    out = {
-        "metric": METRIC,
-        "value": round(100.0 * (ideal_total * 1e-3) / ms_step, 3),
+    del weights, qws, outs, sums
+    return {
+        "value": round(100.0 * (ideal_total * 1e-3) / ms_pass, 3),
         "unit": "% of MI355X roofline",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
+        "ms_per_step": round(ms_pass, 4),
         "data": "synthetic (drawn on the GPU)",
         "config": {"workload": "model: 30 DiT blocks (QKV 11520x3840, O 3840x3840, FFN "
                                "20480x3840 + 3840x10240), Student-t(4) std 0.02",
                    "weights": nweights, "layers": len(shapes), "alpha": alpha,
-                   "step": "quantize every layer -> dequantize every layer"},
+                   "step": "quantize every layer -> dequantize every layer",
+                   "passes_timed": reps},
         "roofline": {"bound": "hbm", "achieved": kern[dom]["GBps"], "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(kern[dom]["GBps"] / HBM_PEAK_GBS, 4),
                      "kernel": dom, "traffic": None},
@@ -592,11 +639,7 @@ def model_pass(args, dev):
                                                 for a, v in snr_g128.items()},
         "alpha_sweep": sweep,
         "snr_by_width": widths,
-        "wall_s": round(wall, 3),
-        "env": run_env(dev),
-        "cpu_baseline": None,
     }
-    print(json.dumps(out), flush=True)
 
 
 def gfx_clock_under_load(step, seconds=1.0):
@@ -612,7 +655,7 @@ def gfx_clock_under_load(step, seconds=1.0):
     def spin():
         i = 0
         while not done.is_set():
-            for _ in range(64):
+            for _ in range(8):
                 step(i)
                 i += 1
             torch.cuda.synchronize()
@@ -659,14 +702,6 @@ def run_env(dev):
     except OSError:
         env["rocm"] = None
     return env
-
-
-def WL_title(name):
-    from w4a16_linear_amd import workloads as WL
-    return {"skinny": WL.config("skinny").title, "qkv": WL.config("qkv").title,
-            "ffn_up": "FFN up/gate: x bf16 [4096, 3840] x W 20480x3840",
-            "ffn_down": "FFN down: x bf16 [4096, 10240] x W 3840x10240",
-            "tiny": WL.config("tiny").title}[name]
 
 
 if __name__ == "__main__":

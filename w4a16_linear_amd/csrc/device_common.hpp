@@ -62,6 +62,19 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The same barrier for kernels that also fill LDS with direct-to-LDS loads
+// (global_load_lds).  The release fence above would wait for every such load
+// still in flight (they write LDS too); here the caller waits (vmcnt) for the
+// loads whose data the barrier publishes, this wave's own LDS accesses complete
+// (lgkmcnt 0), and empty asm statements that clobber memory keep the compiler
+// from moving any memory access across the barrier.
+__device__ __forceinline__ void lds_barrier_dma() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // LDS written by some lanes of a wave and read by others of the same wave: the
 // wave's LDS operations are done in issue order, so the wait and the
 // wavefront-scope fence (which orders the accesses for the compiler) suffice.

@@ -20,17 +20,7 @@
 namespace opq {
 namespace {
 
-// ---------------------------------------------------------------- operand order
-
-// x chunk (8 bf16, natural k order) -> the dequantizer's pair order.
-__device__ __forceinline__ uint4 sigma_order(uint4 v) {
-  uint4 r;
-  r.x = __builtin_amdgcn_perm(v.y, v.x, 0x05040100u);  // (k0, k2)
-  r.y = __builtin_amdgcn_perm(v.w, v.z, 0x05040100u);  // (k4, k6)
-  r.z = __builtin_amdgcn_perm(v.y, v.x, 0x07060302u);  // (k1, k3)
-  r.w = __builtin_amdgcn_perm(v.w, v.z, 0x07060302u);  // (k5, k7)
-  return r;
-}
+// ---------------------------------------------------------------- output
 
 // Output element (row i of a 16-row weight fragment, column c of a 16-column x
 // fragment) of v_mfma_f32_16x16x32_bf16 sits in lane 16 * (i / 4) + c,
@@ -296,53 +286,133 @@ __global__ __launch_bounds__((sk_waves<NMB, GS, kPre>() * kWave)) void linear_sk
 //
 // Block tile 256 (x rows) x 256 (weight rows), k steps of 64,
 // v_mfma_f32_32x32x16_bf16, eight waves (two per SIMD).  Wave w owns weight
-// rows [32w, 32w + 32) of the tile (one B fragment) and all 256 x rows: 8
-// accumulators of 32x32 (128 fp32 per lane).
+// rows [32w, 32w + 32) of the tile (one B fragment per 16-wide k block) and all
+// 256 x rows: 8 accumulators of 32x32 (128 fp32 per lane).
 //
-// Each weight row is decoded once per tile step, in registers: a lane
-// dequantizes one packed word (the eight k values it supplies to the B
-// operand) with its row's table held as byte planes (v_perm lookups).  Lanes
-// 0..31 take words 0..3 of the 8-word k step and lanes 32..63 words 4..7, so
-// sub-step s contracts k-blocks {s, 4 + s}; the x fragments read from LDS use
-// the same k-blocks.  Within a k-block the dequantizer emits bf16 pairs in the
-// order (k0,k2) (k4,k6) (k1,k3) (k5,k7); x is stored to LDS in that order too
-// (two stages, rows XOR-swizzled by 16-byte chunk).
+// Both operands reach LDS without passing through registers (buffer loads
+// with the lds bit: lane i of a request writes 16 bytes, or 4, at the wave's
+// LDS base + 16 i, from any offset it likes; the descriptor's range check
+// returns zeros past the operand):
+//  * x: NXS stages of 256 rows x 64 k (32 KB).  Row r is 128 bytes; its 16-byte
+//    chunk c (k order) sits at chunk c ^ ((r >> 1) & 7), which keeps the
+//    fragment reads below free of bank conflicts.  The lane that fills a slot
+//    fetches the chunk that belongs there, so the four lanes of a quad still
+//    read 64 contiguous bytes of one row.
+//  * weights: NWS stages of a step pair (128 k): the 64 code bytes of each of
+//    the 256 rows (16-byte chunk c of row r at chunk c ^ ((r >> 2) & 3)), then
+//    each row's four sign words.
+// A lane's offsets are fixed for the whole tile; the step's part goes in the
+// scalar offset.
+//
+// Each weight row is decoded once per tile, in registers: lane (r, h) of wave w
+// (row 32w + r, half h of the step) takes the four code words of k
+// 64 kt + 32 h ... + 31 and turns word s into the eight bf16 values of sub-step
+// s with its row's table held as byte planes (v_perm lookups, k order), so
+// sub-step s contracts the 8-wide k blocks {s, 4 + s}; the x fragments are read
+// for the same blocks.
+//
+// Pipeline, one barrier per k step:
+//  * x of step kt + NXS - 1 is requested right after the barrier that ends step
+//    kt - 1 (its stage last served step kt - 1), and waited for (vmcnt) before
+//    the barrier that ends step kt + NXS - 2, which publishes it;
+//  * the weights of pair q are requested in step 2q + 1 - 2 NWS (their stage
+//    last served pair q - NWS) and are complete long before their first use;
+//  * the code words and the first decode of step kt + 1 are done before the
+//    barrier that ends step kt (their pair was published steps earlier), so after
+//    the barrier a wave only waits for its first x fragments.
+// Requests past the last step read whatever lies there (never used), which keeps
+// the wait counts static.  A final half step (k % 64 = 32) zeroes the dead half
+// of the weight fragment; its x slots re-read the step's first half.
+//
+// Within a sub-step each MFMA is followed by one x fragment read of the next
+// sub-step and a share of the decode (and, in sub-step 0, of the step's
+// requests): the decode's VALU work then runs while the wave's own MFMAs
+// execute instead of alternating with them.  Each stage is an LDS array of its
+// own and the main loop is unrolled over the stages' common period, so every
+// access names its stage at compile time; the compiler then tells a read of one
+// stage from the loads in flight to another and inserts no wait for them.  The
+// barrier is the one for direct-to-LDS kernels (lds_barrier_dma): a workgroup
+// release fence on LDS would wait for every load in flight.
+//
+// GS > 0: the group-wise form (group.hpp).  The lane's table is rebuilt from the
+// LDS significand table when its group changes; the float16 group maxima are
+// loaded two steps ahead.  That table takes 32 KB of LDS, so these instances run
+// two x stages and two weight stages.
 
 constexpr int kTM = 256, kTN = 256, kTK = 64;
-constexpr int kAStage = kTM * kTK;                 // bf16 per stage
+constexpr int kTVALUPerMFMA = 6;  // VALU slots after each MFMA in the forced interleave
+constexpr int kTThreads = 512;
+constexpr int kXStageBytes = kTM * kTK * 2;        // 32 KB
+constexpr int kWCodeBytes = kTN * 64;              // codes of a step pair, 16 KB
+constexpr int kWStageBytes = kWCodeBytes + kTN * 16;  // + four sign words per row, 20 KB
+constexpr int kXLoads = kXStageBytes / 1024 / (kTThreads / kWave);     // 4 per wave per step
+constexpr int kWCodeLoads = kWCodeBytes / 1024 / (kTThreads / kWave);  // 2 per wave per pair
+constexpr int kWSignLoads = kTN * 16 / 256 / (kTThreads / kWave);      // 2 per wave per pair
+constexpr int kWLoads = kWCodeLoads + kWSignLoads;
 
-// LDS element offset of 16-byte chunk c of tile row r.  A row is 128 bytes
-// (32 banks), so rows alternate bank halves; XOR-ing the chunk with bits 1..3
-// of the row spreads any 16 consecutive rows over all 64 banks, which keeps the
-// 16-lane passes of ds_read_b128 conflict-free.
-__device__ __forceinline__ int a_off(int r, int c) { return r * kTK + ((c ^ ((r >> 1) & 7)) << 3); }
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+// Fourth word of a raw buffer descriptor: 32-bit data format, no swizzle or stride.
+constexpr int kBufferFlags = 0x00020000;
 
-// The weights are staged through LDS.  Every two k steps the block loads its
-// 256 weight rows x 64 bytes of codes (and the two steps' sign words) with
-// loads in which each group of four lanes reads 64 contiguous bytes, two steps
-// before use, into one of two LDS stages of 80-byte row records (codes of the
-// two steps, then their sign words: a stride that keeps the 32-row fragment
-// reads below free of bank conflicts).  Wave w reads the codes of its rows
-// 32w .. 32w + 31 for a step with one ds_read_b128 and one ds_read_b32 per
-// lane.  (Loading the B-operand layout straight from HBM made every dwordx4
-// touch 32 rows.)
-constexpr int kWRec = 20;  // uint32 per weight row record: 16 code words + 4 sign words
+// LDS byte offset of 16-byte chunk c of x row r within a stage.
+__device__ __forceinline__ uint32_t x_slot(int r, int c) {
+  return (uint32_t)(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+}
 
-//
-// GS > 0: the group-wise form (group.hpp).  The lane's table is rebuilt from
-// the LDS significand table before the first sub-step of every k step; the
-// float16 group maxima are loaded two steps ahead.
+// A step's position in the unrolled main loop (its stages are then known at
+// compile time), or kDynamic: stages chosen at run time.
+template <int I> struct StepPos { static constexpr int value = I; };
+constexpr int kDynamic = -1;
+
+template <int U, typename F>
+__device__ __forceinline__ void unroll_steps(F&& f) {
+  if constexpr (U > 0) {
+    unroll_steps<U - 1>(f);
+    f(StepPos<U - 1>{});
+  }
+}
+
+template <int GS> constexpr int tiled_x_stages() { return GS ? 2 : 3; }
+template <int GS> constexpr int tiled_w_stages() { return GS ? 2 : 3; }
+template <int GS>
+constexpr int tiled_lds_bytes() {
+  return tiled_x_stages<GS>() * kXStageBytes + tiled_w_stages<GS>() * kWStageBytes +
+         (GS ? kMantissas * 32 : 0);
+}
+static_assert(tiled_lds_bytes<0>() <= 160 * 1024 && tiled_lds_bytes<32>() <= 160 * 1024,
+              "the stages fit the 160 KB of LDS");
+
+// s_waitcnt vmcnt(N) for N < 64, every other counter left open.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
 template <bool kHalfTail, int GS>
-__global__ __launch_bounds__(512, 1) void linear_mfma_ws(
+__global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
     const uint16_t* __restrict__ scale16, const float* __restrict__ bias, int m, int n, int k,
     int tiles_m, Levels lv, void* __restrict__ y, int y_bf16) {
-  constexpr int kThreads = 512;
-  constexpr int XCH = kTM * kTK / 8 / kThreads;     // x chunks each thread stages per step (4)
-  __shared__ __attribute__((aligned(16))) uint16_t s_a[2 * kAStage];
-  __shared__ __attribute__((aligned(16))) uint32_t s_w[2][kTN][kWRec];
+  constexpr int NXS = tiled_x_stages<GS>(), NWS = tiled_w_stages<GS>();
+  constexpr int LX = NXS - 1;  // x of step kt + LX is requested in step kt
+  // One array per stage: with the stage of every access known at compile time
+  // the compiler can tell an LDS read from the direct-to-LDS writes in flight
+  // to other stages, and does not wait for them.
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x0[kXStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x1[kXStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x2[NXS > 2 ? kXStageBytes : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w0[kWStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w1[kWStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w2[NWS > 2 ? kWStageBytes : 16];
   __shared__ __attribute__((aligned(16))) uint32_t s_mt[GS ? kMantissas * 8 : 4];
+  auto x_stage = [&](int i) __attribute__((always_inline)) -> uint8_t* {
+    return i == 0 ? s_x0 : (i == 1 ? s_x1 : s_x2);
+  };
+  auto w_stage = [&](int i) __attribute__((always_inline)) -> uint8_t* {
+    return i == 0 ? s_w0 : (i == 1 ? s_w1 : s_w2);
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -350,90 +420,117 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
   const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
   const int m0 = tile_m * kTM;
   const int n0 = tile_n * kTN;
-  const int nw = n0 + wave * 32;                  // first weight row of this wave
-  const int g = lane >> 5;                        // which half of the k step
+  const int h = lane >> 5;                         // which half of the k step
+  const int rr = wave * 32 + (lane & 31);          // this lane's weight row in the tile
+  const int brow = n0 + rr;
   const int kwords = k / 8, swords = k / 32;
   const int nsteps = (k + kTK - 1) / kTK;
-  const int npairs = (nsteps + 1) / 2;
 
-  const int brow = nw + (lane & 31);
+  // ---- loads.  x: load i of wave w fills 1 KB block 4w + i of a stage, i.e.
+  // rows 8(4w + i) .. + 7; lane l the slot (row 8(4w + i) + l/8, chunk l%8).
+  const char* xbase = reinterpret_cast<const char*>(x + (int64_t)m0 * k);
+  uint32_t x_off[kXLoads];   // byte offset of the lane's chunk, step 0
+  int x_chunk[kXLoads];      // its chunk (k / 8 within the step)
+#pragma unroll
+  for (int i = 0; i < kXLoads; ++i) {
+    const int r = 8 * (kXLoads * wave + i) + (lane >> 3);
+    x_chunk[i] = (lane & 7) ^ ((r >> 1) & 7);
+    const uint32_t rowc = (uint32_t)(min(m0 + r, m - 1) - m0);
+    x_off[i] = rowc * (uint32_t)k * 2u + (uint32_t)x_chunk[i] * 16u;
+  }
+  // The requests go through buffer descriptors (base and size in scalar
+  // registers, a 32-bit offset per lane), whose range check turns any offset
+  // past the end into zeros; offsets stay below 2^31 (a tile's rows).
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)xbase, (short)0, (int)min((int64_t)(m - m0) * k * 2, (int64_t)0x7FFFFFFF), kBufferFlags);
+  // The step's offset goes in the scalar offset; requests for steps past the
+  // last read whatever lies there (never used).  In a final half step the
+  // chunks past k re-read the step's first half, so only values of the same x
+  // row ever meet the zeroed half of the weight fragment.
+  auto load_x = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)kt * (kTK * 2);
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) {
+      uint32_t off = x_off[i];
+      if constexpr (kHalfTail) {
+        if (kt == nsteps - 1 && x_chunk[i] >= 4) off -= 64u;
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (lds_ptr_t)(st + (kXLoads * wave + i) * 1024),
+                                               16, off, soff, 0, 0);
+    }
+  };
+  // weights of pair q: code load i of wave w fills 1 KB block 2w + i of the code
+  // region (rows 16(2w + i) + l/4, chunk slot l%4); sign load i fills 256 B block
+  // 2w + i (rows 16(2w + i) + l/4, word l%4).
+  const int n0c = min(n0, n - 1);
+  const char* pbase = reinterpret_cast<const char*>(packed + (int64_t)n0c * kwords);
+  const char* sbase = reinterpret_cast<const char*>(sign + (int64_t)n0c * swords);
+  // byte offsets of the lane's code chunk and sign word in pair 0
+  uint32_t wc_off[kWCodeLoads], ws_off[kWSignLoads];
+#pragma unroll
+  for (int i = 0; i < kWCodeLoads; ++i) {
+    const int r = 16 * (kWCodeLoads * wave + i) + (lane >> 2);
+    wc_off[i] = (uint32_t)(min(n0 + r, n - 1) - n0c) * (uint32_t)kwords * 4u +
+                (uint32_t)((lane & 3) ^ ((r >> 2) & 3)) * 16u;
+  }
+#pragma unroll
+  for (int i = 0; i < kWSignLoads; ++i) {
+    const int r = 16 * (kWSignLoads * wave + i) + (lane >> 2);
+    ws_off[i] = (uint32_t)(min(n0 + r, n - 1) - n0c) * (uint32_t)swords * 4u + (uint32_t)(lane & 3) * 4u;
+  }
+  const __amdgpu_buffer_rsrc_t p_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)pbase, (short)0, (int)min((int64_t)(n - n0c) * kwords * 4, (int64_t)0x7FFFFFFF), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)sbase, (short)0, (int)min((int64_t)(n - n0c) * swords * 4, (int64_t)0x7FFFFFFF), kBufferFlags);
+  auto load_w = [&](int q, uint8_t* st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kWCodeLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(p_rsrc, (lds_ptr_t)(st + (kWCodeLoads * wave + i) * 1024),
+                                               16, wc_off[i], (uint32_t)q * 64u, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kWSignLoads; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          s_rsrc, (lds_ptr_t)(st + kWCodeBytes + (kWSignLoads * wave + i) * 256), 4, ws_off[i],
+          (uint32_t)q * 16u, 0, 0);
+  };
+
+  // ---- the lane's table and code words.
   RowLut lut;
   if constexpr (GS == 0) lut = make_row_lut(lv, scale[min(brow, n - 1)]);
-  // GS > 0: float16 max of this lane's group in step kt (its half of the step)
   const int ngroups = GS ? k / GS : 1;
   const uint16_t* hrow = GS ? scale16 + (int64_t)min(brow, n - 1) * ngroups : nullptr;
   auto load_h = [&](int kt) __attribute__((always_inline)) -> uint32_t {
     if constexpr (GS > 0)
-      return hrow[min((min(kt, nsteps - 1) * kTK + 32 * g) / GS, ngroups - 1)];
+      return hrow[min((min(kt, nsteps - 1) * kTK + 32 * h) / GS, ngroups - 1)];
     else
       return 0u;
   };
-  uint32_t h_next = 0u, h_load = 0u;  // maxima of steps kt + 1 and kt + 2
+  uint32_t h_next = 0u, h_load = 0u;  // GS > 0: maxima of steps kt + 1 and kt + 2
 
-  // Weight loads for step pair p (steps 2p, 2p + 1): thread t moves 16 code
-  // bytes (quarter t % 4) of tile rows t/4 and t/4 + 128, and sign words
-  // 2(t%2), 2(t%2) + 1 of the pair for tile row t/2.  Rows past n read row
-  // n - 1; parts past k read the row's last 16 code bytes or last sign word
-  // (only ever met by zeroed fragments or steps that are never used).
-  const int wq = tid & 3;
-  const int n0c = min(n0, n - 1);
-  const char* pbase = reinterpret_cast<const char*>(packed + (int64_t)n0c * kwords);
-  const uint32_t* sbase = sign + (int64_t)n0c * swords;
-  const uint32_t pa_off = (uint32_t)(min(n0 + (tid >> 2), n - 1) - n0c) * (uint32_t)kwords * 4u;
-  const uint32_t pb_off = (uint32_t)(min(n0 + 128 + (tid >> 2), n - 1) - n0c) * (uint32_t)kwords * 4u;
-  const uint32_t s_off = (uint32_t)(min(n0 + (tid >> 1), n - 1) - n0c) * (uint32_t)swords;
-  uint4 wv[2];
-  uint32_t wsg[2];
-  auto load_w = [&](int p) __attribute__((always_inline)) {
-    const int pc = min(p, npairs - 1);
-    const uint32_t e = (uint32_t)min(pc * 2 * kTK + 32 * wq, k - 32);  // first element of the part
-    wv[0] = *reinterpret_cast<const uint4*>(pbase + pa_off + e / 2u);
-    wv[1] = *reinterpret_cast<const uint4*>(pbase + pb_off + e / 2u);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) wsg[i] = sbase[s_off + (uint32_t)min(pc * 4 + 2 * (tid & 1) + i, swords - 1)];
+  // codes (4 words) and sign word of step kt for this lane
+  const uint32_t wr_code = (uint32_t)rr * 64u, wr_sign = (uint32_t)kWCodeBytes + (uint32_t)rr * 16u;
+  const uint32_t wr_swz = (uint32_t)((rr >> 2) & 3);
+  auto read_w = [&](int kt, const uint8_t* st, uint4& pw, uint32_t& sw) __attribute__((always_inline)) {
+    const uint32_t c = (uint32_t)(2 * (kt & 1) + h);
+    pw = *reinterpret_cast<const uint4*>(st + wr_code + ((c ^ wr_swz) << 4));
+    sw = *reinterpret_cast<const uint32_t*>(st + wr_sign + c * 4u);
   };
-  auto store_w = [&](int p) __attribute__((always_inline)) {
-    uint32_t (*st)[kWRec] = s_w[p & 1];
-    *reinterpret_cast<u32x4_t*>(&st[tid >> 2][4 * wq]) = u32x4_t{wv[0].x, wv[0].y, wv[0].z, wv[0].w};
-    *reinterpret_cast<u32x4_t*>(&st[128 + (tid >> 2)][4 * wq]) = u32x4_t{wv[1].x, wv[1].y, wv[1].z, wv[1].w};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) st[tid >> 1][16 + 2 * (tid & 1) + i] = wsg[i];
-  };
-  // This lane's codes and sign word of step kt (from stage (kt/2) & 1).
-  auto read_w = [&](int kt, uint4& pw, uint32_t& sw) __attribute__((always_inline)) {
-    const uint32_t* rec = s_w[(kt >> 1) & 1][wave * 32 + (lane & 31)];
-    const int half = kt & 1;
-    pw = *reinterpret_cast<const uint4*>(rec + 8 * half + 4 * g);
-    sw = rec[16 + 2 * half + g];
-  };
-
-  const char* xbase = reinterpret_cast<const char*>(x + (int64_t)m0 * k);
-  uint32_t x_off[XCH];
-#pragma unroll
-  for (int i = 0; i < XCH; ++i) {
-    const int c = tid + kThreads * i;
-    const int r = min(m0 + (c >> 3), m - 1) - m0;
-    x_off[i] = ((uint32_t)r * (uint32_t)k + 8u * (uint32_t)(c & 7)) * 2u;
-  }
-  auto load_a = [&](int kt, uint4 (&xa)[XCH]) __attribute__((always_inline)) {
-    const int kc = min(kt, nsteps - 1) * kTK;
-#pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      uint32_t off = x_off[i] + (uint32_t)kc * 2u;
-      if constexpr (kHalfTail) {
-        const int c = tid + kThreads * i;
-        if (kc + 8 * (c & 7) >= k) off -= 64u;  // step back into the row
-      }
-      xa[i] = *reinterpret_cast<const uint4*>(xbase + off);
+  auto decode_b = [&](int kt, int s, const uint4& pwv, uint32_t swv, bf16x8_t& b)
+      __attribute__((always_inline)) {
+    const uint32_t words[4] = {pwv.x, pwv.y, pwv.z, pwv.w};
+    uint32_t o[4];
+    decode_word_ordered<false>(words[s], swv >> (8 * s), lut, o);
+    if constexpr (kHalfTail) {
+      if (kt == nsteps - 1 && h == 1) o[0] = o[1] = o[2] = o[3] = 0u;
     }
+    b = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
   };
-  auto store_a = [&](int stage, const uint4 (&xa)[XCH]) __attribute__((always_inline)) {
-    uint16_t* base = s_a + stage * kAStage;
+  // x fragments of sub-step s of step kt: rows 32 mi + (lane & 31), chunk s + 4h
+  auto read_a = [&](const uint8_t* st, int s, bf16x8_t (&a)[8]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < XCH; ++i) {
-      const int c = tid + kThreads * i;
-      const uint4 v = sigma_order(xa[i]);
-      *reinterpret_cast<u32x4_t*>(base + a_off(c >> 3, c & 7)) = u32x4_t{v.x, v.y, v.z, v.w};
+    for (int mi = 0; mi < 8; ++mi) {
+      const int r = mi * 32 + (lane & 31);
+      a[mi] = *reinterpret_cast<const bf16x8_t*>(st + x_slot(r, s + 4 * h));
     }
   };
 
@@ -443,67 +540,76 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
 
-  auto dequant_b = [&](int kt, int s, const uint4& pwv, uint32_t swv, bf16x8_t& b)
-      __attribute__((always_inline)) {
-    const uint32_t words[4] = {pwv.x, pwv.y, pwv.z, pwv.w};
-    uint32_t o[4];
-    dequant_word(words[s], swv >> (8 * s), lut, o);
-    if constexpr (kHalfTail) {
-      if (kt == nsteps - 1 && g == 1) o[0] = o[1] = o[2] = o[3] = 0u;
-    }
-    b = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
-  };
-  auto read_a = [&](const uint16_t* sa, int s, bf16x8_t (&a)[8]) __attribute__((always_inline)) {
-#pragma unroll
-    for (int mi = 0; mi < 8; ++mi)
-      a[mi] = *reinterpret_cast<const bf16x8_t*>(sa + a_off(mi * 32 + (lane & 31), 4 * g + s));
-  };
-
-  // Step pair q is stored at step 2q - 2 (sub-step 0) from registers loaded at
-  // step 2q - 4, and first read at step 2q - 1 after that step's barrier; the
-  // stage it overwrites last served step 2q - 3, read at step 2q - 4.
-  uint4 pw;        // codes of the current step (read at the previous step's sub-step 3)
+  uint4 pw;
   uint32_t sw;
-  uint4 xa[XCH];
-  bf16x8_t a_frag[8], b_buf[2];  // one x fragment set: its registers keep the kernel clear of scratch
+  // Two B fragments: the next sub-step's decode fills one while this
+  // sub-step's MFMAs read the other, so it can run between them.
+  bf16x8_t a_frag[8], b_buf[2];
   if (nsteps > 0) {
+    // prologue: x of steps 0 .. LX - 1, weight pairs 0 .. NWS - 1
     uint32_t h0 = 0u;
     if constexpr (GS > 0) {
       h0 = load_h(0);
       h_next = load_h(1);
     }
-    load_a(0, xa);
-    load_w(0);
+#pragma unroll
+    for (int j = 0; j < LX; ++j) load_x(j, x_stage(j));
+#pragma unroll
+    for (int q = 0; q < NWS; ++q) load_w(q, w_stage(q));
     if constexpr (GS > 0) build_mant_table(lv, s_mt);
-    store_a(0, xa);
-    store_w(0);
-    load_a(1, xa);
-    load_w(1);
-    __syncthreads();
+    wait_vm<0>();
+    lds_barrier_dma();
     if constexpr (GS > 0) lut = group_lut(s_mt, h0);
-    read_w(0, pw, sw);
-    read_a(s_a, 0, a_frag);
-    dequant_b(0, 0, pw, sw, b_buf[0]);
+    read_w(0, s_w0, pw, sw);
+    decode_b(0, 0, pw, sw, b_buf[0]);
+    read_a(s_x0, 0, a_frag);
   }
 
-  auto step = [&](int kt, bool even) __attribute__((always_inline)) {
-    const int stage = kt & 1;
-    const uint16_t* sa = s_a + stage * kAStage;
+  // One k step.  pos: StepPos<u> for the u-th step of an unrolled group of kUnroll
+  // (kt % kUnroll == u, every stage a compile-time choice), or StepPos<kDynamic>.
+  constexpr int kUnroll = NXS * 2 * NWS / (NXS == NWS ? NXS : 1);  // lcm(NXS, 2 NWS)
+  static_assert(kUnroll % NXS == 0 && kUnroll % (2 * NWS) == 0, "stage periods divide the unroll");
+  auto step = [&](int kt, auto pos) __attribute__((always_inline)) {
+    constexpr int u = decltype(pos)::value;
+    const bool odd = u >= 0 ? (u & 1) : (kt & 1);
+    // stage of x of step kt + j, and of the weight pair holding step kt + j
+    auto xs = [&](int j) __attribute__((always_inline)) {
+      return x_stage(u >= 0 ? (u + j) % NXS : (kt + j) % NXS);
+    };
+    auto ws = [&](int j) __attribute__((always_inline)) {
+      return w_stage(u >= 0 ? ((u + j) / 2) % NWS : ((kt + j) / 2) % NWS);
+    };
+    // requests after the barrier that ended step kt - 1: the group max of step
+    // kt + 2 first (a plain load, waited for by the compiler where it is used),
+    // then x of step kt + LX, then (odd steps) the weights of pair
+    // (kt - 1) / 2 + NWS, into the stage of pair (kt - 1) / 2
+    if constexpr (GS > 0) h_load = load_h(kt + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(kt + LX, xs(LX));
+    if (odd) load_w((kt - 1) / 2 + NWS, ws(-1));
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
-      // The next sub-step's x fragments are read once this one's MFMAs are
-      // issued; the other wave on the SIMD covers the LDS latency.
 #pragma unroll
       for (int mi = 0; mi < 8; ++mi)
         acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag[mi], b_buf[cur], acc[mi], 0, 0, 0);
       if (s < 3) {
-        read_a(sa, s + 1, a_frag);
-        dequant_b(kt, s + 1, pw, sw, b_buf[nxt]);
+        read_a(xs(0), s + 1, a_frag);
+        decode_b(kt, s + 1, pw, sw, b_buf[nxt]);
+        // Interleave: after each MFMA, one x fragment read of the next sub-step
+        // (its register is free once that MFMA has issued), a share of the
+        // decode and (sub-step 0) of this step's load requests, so the VALU
+        // work runs while this wave's MFMAs execute.
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+          if (s == 0) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+          __builtin_amdgcn_sched_group_barrier(0x002, kTVALUPerMFMA, 0);  // VALU
+        }
       } else {
-        __syncthreads();
-        read_a(s_a + (stage ^ 1) * kAStage, 0, a_frag);
-        read_w(kt + 1, pw, sw);  // this step's words are dead after sub-step 2
+        // the next step's code words (their pair is published) and first decode
+        read_w(kt + 1, ws(1), pw, sw);
         if constexpr (GS > 0) {
           // the table of step kt + 1, when it starts a new group (every step
           // for groups of 32 and 64: the two halves of a step differ or the
@@ -511,36 +617,64 @@ __global__ __launch_bounds__(512, 1) void linear_mfma_ws(
           if (GS <= kTK || ((kt + 1) * kTK) % GS == 0) lut = group_lut(s_mt, h_next);
           h_next = h_load;
         }
-        dequant_b(kt + 1, 0, pw, sw, b_buf[nxt]);
-      }
-      if (s == 0) {
-        if constexpr (GS > 0) h_load = load_h(kt + 2);
-        store_a(stage ^ 1, xa);
-        load_a(kt + 2, xa);
-        if (even) {
-          store_w(kt / 2 + 1);
-          load_w(kt / 2 + 2);
+        decode_b(kt + 1, 0, pw, sw, b_buf[nxt]);
+        // the next step's code words first, then the decode between the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS read
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, kTVALUPerMFMA, 0);  // VALU
         }
+        // x of step kt + 1 is complete: every request issued before it is done.
+        // Issued after it: with three x stages, the x of step kt + 2 and one
+        // pair of weights; with two, the weights of this step (odd steps).
+        if constexpr (LX == 2) {
+          wait_vm<kXLoads + kWLoads>();
+        } else {
+          if (odd) wait_vm<kWLoads>();
+          else wait_vm<0>();
+        }
+        lds_barrier_dma();
+        read_a(xs(1), 0, a_frag);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);  // steps are not interleaved: that costs registers
   };
   int kt = 0;
-  for (; kt + 1 < nsteps; kt += 2) {
-    step(kt, true);
-    step(kt + 1, false);
-  }
-  if (kt < nsteps) step(kt, true);
+  for (; kt + kUnroll <= nsteps; kt += kUnroll)
+    unroll_steps<kUnroll>([&](auto pos) __attribute__((always_inline)) {
+      step(kt + decltype(pos)::value, pos);
+    });
+  for (; kt < nsteps; ++kt) step(kt, StepPos<kDynamic>{});
+  wait_vm<0>();  // no load may still be writing LDS when the block ends
 
   // 32x32 accumulator layout: register e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
-  // column l%32.
+  // column l%32.  Whole tiles store without a bound check.
   const float bv = (bias && brow < n) ? bias[brow] : 0.0f;
+  const bool whole = m0 + kTM <= m && n0 + kTN <= n;
+  if (whole && !y_bf16) {
+    float* yrow = static_cast<float*>(y) + (int64_t)(m0 + 4 * h) * n + brow;
 #pragma unroll
-  for (int mi = 0; mi < 8; ++mi)
+    for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = m0 + mi * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-      if (row < m && brow < n) store_y(y, y_bf16, (int64_t)row * n + brow, acc[mi][e] + bv);
-    }
+      for (int e = 0; e < 16; ++e)
+        yrow[(int64_t)(mi * 32 + 8 * (e >> 2) + (e & 3)) * n] = acc[mi][e] + bv;
+  } else if (whole) {
+    uint16_t* yrow = static_cast<uint16_t*>(y) + (int64_t)(m0 + 4 * h) * n + brow;
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        yrow[(int64_t)(mi * 32 + 8 * (e >> 2) + (e & 3)) * n] = (uint16_t)bf16_rne(acc[mi][e] + bv);
+  } else {
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = m0 + mi * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+        if (row < m && brow < n) store_y(y, y_bf16, (int64_t)row * n + brow, acc[mi][e] + bv);
+      }
+  }
 }
 
 }  // namespace
@@ -579,8 +713,8 @@ hipError_t launch_linear_any(const uint16_t* x, const uint32_t* packed, const ui
                        sign, scale, scale16, bias, (int)m, (int)n, (int)k, lv, y, (int)y_bf16);
   } else {
     const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
-    auto kernel = (k % kTK) ? linear_mfma_ws<true, GS> : linear_mfma_ws<false, GS>;
-    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(512), 0, stream, x,
+    auto kernel = (k % kTK) ? linear_tiled<true, GS> : linear_tiled<false, GS>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kTThreads), 0, stream, x,
                        packed, sign, scale, scale16, bias, (int)m, (int)n, (int)k, (int)tiles_m,
                        lv, y, (int)y_bf16);
   }
