@@ -59,32 +59,6 @@ __device__ __forceinline__ uint32_t plane4(const uint32_t (&p)[4], uint32_t sel7
   return (b & mask) | (a & ~mask);
 }
 
-// Dequantize one packed word (codes k0..k7) with its sign byte into four bf16
-// pairs: out = {(k0,k2), (k4,k6), (k1,k3), (k5,k7)}.  `sb` holds the sign byte
-// in bits 0..7 (higher bits are ignored).
-__device__ __forceinline__ void dequant_word(uint32_t w, uint32_t sb, const RowLut& t,
-                                             uint32_t (&out)[4]) {
-  const uint32_t se7 = w & 0x07070707u;          // codes k0 k2 k4 k6, bit 3 stripped
-  const uint32_t so7 = (w >> 4) & 0x07070707u;   // codes k1 k3 k5 k7, bit 3 stripped
-  // 0xFF bytes where the code is >= 8: replicate bit 3 of each code via the
-  // sign-copy selectors of v_perm (8 -> bit 15, 9 -> bit 31, 10 -> bit 47, 11 -> bit 63).
-  const uint32_t w4 = w << 4;
-  const uint32_t me = __builtin_amdgcn_perm(w4 << 8, w4, 0x090B080Au);
-  const uint32_t mo = __builtin_amdgcn_perm(w << 8, w, 0x090B080Au);
-  const uint32_t lo_e = plane4(t.lo, se7, me), hi_e = plane4(t.hi, se7, me);
-  const uint32_t lo_o = plane4(t.lo, so7, mo), hi_o = plane4(t.hi, so7, mo);
-  // sign bits into bit 7 of each high byte: spread bits 0,2,4,6 (even) or
-  // 1,3,5,7 (odd) of the byte to 7, 15, 23, 31 with one 24-bit multiply.
-  const uint32_t sge = __umul24((sb << 7) & 0x2A80u, 0x41041u);
-  const uint32_t sgo = __umul24((sb << 6) & 0x2A80u, 0x41041u);
-  const uint32_t hs_e = hi_e | (sge & 0x80808080u);
-  const uint32_t hs_o = hi_o | (sgo & 0x80808080u);
-  out[0] = __builtin_amdgcn_perm(hs_e, lo_e, 0x05010400u);
-  out[1] = __builtin_amdgcn_perm(hs_e, lo_e, 0x07030602u);
-  out[2] = __builtin_amdgcn_perm(hs_o, lo_o, 0x05010400u);
-  out[3] = __builtin_amdgcn_perm(hs_o, lo_o, 0x07030602u);
-}
-
 // Eight bfloat16 values of one packed word in k order: out = {(k0,k1),
 // (k2,k3), (k4,k5), (k6,k7)}.  `sb` holds the sign byte in bits 0..7.  With
 // kPlusZero a sign bit only marks a nonzero code, so code 0 always gives +0.0

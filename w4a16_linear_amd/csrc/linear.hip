@@ -416,7 +416,8 @@ __global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  // uniform across the wave: the LDS destinations of the loads are scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
   const int m0 = tile_m * kTM;
   const int n0 = tile_n * kTN;
