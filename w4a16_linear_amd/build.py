@@ -33,12 +33,27 @@ def hipcc() -> str:
     return path
 
 
+def hip_flags() -> list:
+    """hipcc flags of every HIP source (gfx950, no fast-math, packed fp32 off)."""
+    return [f"--offload-arch={ARCH}", "-x", "hip", "-Xclang", "-target-feature", "-Xclang",
+            "-packed-fp32-ops", "-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
+
+
+def device_asm(src: str) -> str:
+    """gfx950 assembly of one HIP source, compiled as the library is (the kernel
+    metadata at its end gives each kernel's registers and scratch)."""
+    cmd = [hipcc()] + hip_flags() + ["--cuda-device-only", "-S", "-o", "-", os.path.join(CSRC, src)]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"compile failed: {src}\n{r.stderr}")
+    return r.stdout
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
     common = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
     if src.endswith(".hip"):
-        cmd = [hipcc(), f"--offload-arch={ARCH}", "-x", "hip",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"] + common
+        cmd = [hipcc()] + hip_flags()
     else:
         rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
         cxx = os.environ.get("CXX") or shutil.which("g++") or "g++"
