@@ -58,8 +58,8 @@ def parse():
                     help="0: one float32 max per row; else the group-wise form (float16 max "
                          "per this many weights along k)")
     ap.add_argument("--bits", type=int, default=4, choices=[3, 4, 5, 6],
-                    help="code width; other than 4 the step is quantize -> dequantize (the "
-                         "linear layer runs on 4-bit codes)")
+                    help="code width; other than 4 the linear layer decodes into a workspace "
+                         "and multiplies the bfloat16 weights")
     ap.add_argument("--rotate", type=int, default=0, help="buffer sets (0: enough for > 768 MB)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-model-pass", action="store_true",
@@ -102,7 +102,7 @@ def algorithmic(m, n, k, w_bytes, group=0, bits=4):
     st = (bits + 1) / 8.0
     quant = {"bytes": n * k * (w_bytes + st) + sc, "flops": 0}
     dequant = {"bytes": n * k * (st + 2) + sc, "flops": 0}
-    lin = {"bytes": 0.625 * n * k + sc + 2 * m * k + 4 * m * n, "flops": 2 * m * n * k}
+    lin = {"bytes": st * n * k + sc + 2 * m * k + 4 * m * n, "flops": 2 * m * n * k}
     return {"quantize": quant, "dequantize": dequant, "linear": lin}
 
 
@@ -266,7 +266,7 @@ def main():
         print("--group and --bits other than 4 do not combine", file=sys.stderr)
         sys.exit(2)
     layers = workload_layers(args.workload)
-    kinds = ["quantize", "dequantize", "linear"] if bits == 4 else ["quantize", "dequantize"]
+    kinds = ["quantize", "dequantize", "linear"]
     stream = torch.cuda.current_stream(dev)
 
     # Per layer: host tensors once, then `rot` device sets of every buffer.
@@ -449,8 +449,7 @@ def main():
                    "layers": shapes, "alpha": alpha,
                    "scales": (f"float16 per group of {group}" if group else "float32 per row"),
                    "bits": bits,
-                   "step": ("per layer: quantize -> dequantize -> linear" if bits == 4
-                            else "per layer: quantize -> dequantize")},
+                   "step": "per layer: quantize -> dequantize -> linear"},
         "roofline": roof,
         "kernels": kern,
         "kernels_sum_us": round(sum(kk["us"] for kk in kern.values()), 3),

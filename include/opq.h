@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define OPQ_ABI_VERSION 4
+#define OPQ_ABI_VERSION 5
 
 typedef enum {
   OPQ_OK = 0,
@@ -191,8 +191,8 @@ int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
  * [n][k*b/32].  For b = 4 this is exactly the layout of opq_quantize, and
  * these calls give the same results as the 4-bit ones.
  *   bits     3, 4, 5 or 6 (OPQ_ERR_SHAPE otherwise)
- * The linear layer runs on 4-bit codes only (the W4A16 path); the other
- * widths are a storage format and an accuracy study (opq_error_sums_bits).
+ * The 4-bit linear layer (opq_linear) decodes on chip; opq_linear_bits below
+ * serves the other widths.
  */
 
 /*
@@ -222,6 +222,35 @@ int opq_dequantize_bits(const uint32_t* packed, const uint32_t* sign, const floa
  */
 int opq_error_sums_bits(const void* w, int w_dtype, int64_t n, int64_t k, int bits, float alpha,
                         double* row_sums, void* stream);
+
+/*
+ * Bytes of device workspace opq_linear_bits needs: for bits = 4 those of
+ * opq_linear_workspace_bytes (0), otherwise room for W' as bfloat16, n * k * 2
+ * bytes rounded up to 256 (0 for an empty shape).
+ */
+size_t opq_linear_bits_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits);
+
+/*
+ * The linear layer on b-bit codes: y = x W'^T (+ bias) with W' the
+ * reconstruction opq_dequantize_bits writes.  For bits = 4 this is opq_linear.
+ * For 3, 5 and 6 bits the call first writes W' (bfloat16, [n][k]) into the
+ * workspace with the b-bit dequantizer and then multiplies with bf16 MFMA and
+ * float32 accumulation, as the card's OPQLinear decodes its weights before a
+ * dense matmul ("文件结构": opq_quantize.py; "技术细节 / 推理解码").
+ *   x, bias, y, y_dtype   as for opq_linear
+ *   packed, sign, scale   as written by opq_quantize_bits for W[n][k]
+ *   workspace, workspace_bytes  device scratch of at least
+ *           opq_linear_bits_workspace_bytes(m, n, k, bits) bytes; its
+ *           contents need no initialisation and are overwritten; calls that may
+ *           run at the same time need buffers of their own
+ * Reproducible sum order; k <= 65536, n <= 2^26.  Errors: OPQ_ERR_NULL,
+ * OPQ_ERR_SHAPE (also for bits outside 3..6), OPQ_ERR_ALPHA, OPQ_ERR_ALIGN,
+ * OPQ_ERR_DTYPE, OPQ_ERR_WORKSPACE, OPQ_ERR_UNSUPPORTED, OPQ_ERR_HIP.
+ */
+int opq_linear_bits(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
+                    const float* scale, const float* bias, int64_t m, int64_t n, int64_t k, int bits,
+                    float alpha, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream);
 
 /*
  * Group-wise stored form: the card's own ("技术细节 / 存储格式": one float16

@@ -33,14 +33,14 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(opq._SIGNATURES)
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.opq_abi_version() == opq.ABI_VERSION == 4
+    assert lib.opq_abi_version() == opq.ABI_VERSION == 5
     for s in range(9):
         assert opq.status_str(s) and opq.status_str(s) != "unknown status"
     assert opq.status_str(99) == "unknown status"
@@ -173,6 +173,39 @@ def test_bits_argument_checks(lib):
     assert e(FAKE, 1, 4, 64, 2, 0.73, FAKE, None) == SHAPE
     assert e(FAKE, 1, 4, 16384 + 32, 5, 0.73, FAKE, None) == UNSUPPORTED
     assert e(FAKE, 1, 0, 64, 6, 0.73, FAKE, None) == OK
+
+
+def test_linear_bits_argument_checks(lib):
+    f = lib.opq_linear_bits
+    ws_need = lib.opq_linear_bits_workspace_bytes(8, 16, 64, 5)
+    args = dict(x=FAKE, p=FAKE, s=FAKE, sc=FAKE, b=None, m=8, n=16, k=64, bits=5, a=0.73, y=FAKE,
+                yd=0, ws=FAKE, wsb=ws_need)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return f(a["x"], a["p"], a["s"], a["sc"], a["b"], a["m"], a["n"], a["k"], a["bits"],
+                 a["a"], a["y"], a["yd"], a["ws"], a["wsb"], None)
+
+    assert ws_need == 16 * 64 * 2                    # W' as bfloat16, already a multiple of 256
+    assert lib.opq_linear_bits_workspace_bytes(8, 3, 32, 3) == 256   # 192 bytes rounded up
+    assert lib.opq_linear_bits_workspace_bytes(0, 16, 64, 6) == 0
+    assert lib.opq_linear_bits_workspace_bytes(8, 16, 64, 4) == lib.opq_linear_workspace_bytes(8, 16, 64)
+    assert call(x=None) == NULL
+    assert call(sc=None) == NULL
+    assert call(k=48) == SHAPE
+    for b in (2, 7, 0):
+        assert call(bits=b) == SHAPE, b
+    assert call(a=float("nan")) == ALPHA
+    assert call(ws=MISALIGNED) == ALIGN
+    assert call(yd=3) == DTYPE
+    assert call(wsb=ws_need - 1) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(m=0, ws=None, wsb=0) == OK
+    assert call(n=0, ws=None, wsb=0) == OK
+    assert call(k=65536 + 32, wsb=16 * (65536 + 32) * 2) == UNSUPPORTED
+    # bits = 4 is opq_linear itself (no workspace needed)
+    assert call(bits=4, ws=None, wsb=0, k=65536 + 32) == UNSUPPORTED
+    assert call(bits=4, ws=None, wsb=0, m=0) == OK
 
 
 def test_grouped_argument_checks(lib):

@@ -149,3 +149,92 @@ def test_bits_empty_calls(gpu_lib):
         torch.cuda.synchronize()
         assert np.all(bw.scale.cpu().numpy() == 0)
         assert opq.dequantize(bw, 0.73).shape == (3, 0)
+
+
+# ---------------------------------------------------------------- the linear layer on b-bit codes
+
+def _linear_bits_case(opq, m, n, k, bits, alpha, seed, bias=False, out_dtype=torch.float32,
+                      w_dtype="bf16"):
+    """opq.linear on b-bit codes against the oracle's reconstruction times x in
+    float64: codes bit for bit first, then every output within the tolerance."""
+    from test_gpu_parity import Guarded, assert_linear_close
+    w_vals, w_dev = weight_tensor(WL.student_t(seed, (n, k)), w_dtype)
+    bw = opq.quantize_bits(w_dev, alpha, bits)
+    ref = O.quantize_bits(w_vals, alpha, bits)
+    assert np.array_equal(u32(bw.packed), ref[0]) and np.array_equal(u32(bw.sign), ref[1])
+    d_ref = O.dequantize_bits(*ref, alpha, bits)
+    xt = WL.to_bf16(WL.normal(seed + 1, (m, k)))
+    b = torch.from_numpy(WL.normal(seed + 2, (n,), 0.1)) if bias else None
+    gy = Guarded((m, n), out_dtype)
+    opq.linear(xt.to(DEV), bw, alpha, bias=None if b is None else b.to(DEV), out=gy.t)
+    torch.cuda.synchronize()
+    gy.check()
+    y_ref = O.linear(bf16_bits(xt), d_ref, None if b is None else b.numpy())
+    y = gy.t.float().cpu().numpy()
+    if out_dtype == torch.bfloat16:
+        # the float32 result rounded once: within half a bf16 ulp of it, plus the linear bar
+        rms = float(np.sqrt(np.mean(y_ref ** 2))) if y_ref.size else 0.0
+        err = np.abs(y.astype(np.float64) - y_ref)
+        assert np.all(err <= 1e-2 * rms + np.abs(y_ref) * 2.0 ** -8 + 1e-30)
+        return 0.0
+    return assert_linear_close(y, y_ref)
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("m,n,k", [(1, 48, 96), (8, 256, 256), (16, 300, 544), (32, 1000, 3840),
+                                   (33, 17, 160), (64, 520, 1056), (65, 700, 1056),
+                                   (300, 513, 3872), (257, 256, 64)])
+def test_linear_bits_shapes(gpu_lib, m, n, k, bits):
+    """Skinny (m <= 64) and tiled shapes, ragged n and m, k with a final half
+    step (k % 64 = 32) and with a final part block (k % 128 != 0)."""
+    rel = _linear_bits_case(gpu_lib, m, n, k, bits, 0.73, 2100 + m + n + k + bits)
+    print(f"b={bits} m={m} n={n} k={k}: max err / rms = {rel:.2e}")
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_linear_bits_bias_bf16_out_fp32_weights(gpu_lib, bits):
+    _linear_bits_case(gpu_lib, 40, 300, 512, bits, 0.45, 2200 + bits, bias=True)
+    _linear_bits_case(gpu_lib, 130, 300, 512, bits, 1.0, 2210 + bits, bias=True,
+                      out_dtype=torch.bfloat16, w_dtype="f32")
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_linear_bits_full_size(gpu_lib, bits):
+    """The skinny workload's weight (3840 x 3840) at every width with x[32, 3840]
+    and x[4096, 3840]: every output of both paths within the tolerance."""
+    opq = gpu_lib
+    from test_gpu_parity import assert_linear_close
+    L = WL.config("skinny").layers[0]
+    w_vals, w_dev = weight_tensor(L.make_w(), "bf16")
+    bw = opq.quantize_bits(w_dev, WL.ALPHA, bits)
+    ref = O.quantize_bits(w_vals, WL.ALPHA, bits)
+    torch.cuda.synchronize()
+    assert np.array_equal(u32(bw.packed), ref[0])
+    d_ref = O.dequantize_bits(*ref, WL.ALPHA, bits)
+    for m, seed in ((32, 2001), (4096, 3001)):
+        xt = WL.to_bf16(WL.normal(seed, (m, L.k)))
+        y = opq.linear(xt.to(DEV), bw, WL.ALPHA).cpu().numpy()
+        rel = assert_linear_close(y, O.linear(bf16_bits(xt), d_ref))
+        print(f"b={bits} m={m}: max err / rms = {rel:.2e}")
+
+
+def test_linear_bits_workspace_reuse_and_empty(gpu_lib):
+    """One workspace serves calls of different widths and shapes in turn; empty
+    shapes return the bias (or nothing)."""
+    opq = gpu_lib
+    ws = torch.empty(opq.linear_workspace_bytes(200, 384, 1024, 6), dtype=torch.uint8, device=DEV)
+    outs = []
+    for bits, m, n, k in ((6, 200, 384, 1024), (3, 20, 256, 512), (5, 200, 384, 1024)):
+        _, w_dev = weight_tensor(WL.student_t(2300 + bits, (n, k)), "bf16")
+        bw = opq.quantize_bits(w_dev, 0.73, bits)
+        x = WL.to_bf16(WL.normal(2400 + bits, (m, k))).to(DEV)
+        y1 = opq.linear(x, bw, 0.73, workspace=ws)
+        y2 = opq.linear(x, bw, 0.73)     # the per-device shared workspace
+        torch.cuda.synchronize()
+        assert torch.equal(y1, y2)
+        outs.append(y1)
+    bw = opq.quantize_bits(torch.zeros((4, 0), dtype=torch.bfloat16, device=DEV), 0.73, 5)
+    bias = torch.arange(4, dtype=torch.float32, device=DEV)
+    for m in (3, 100):
+        y = opq.linear(torch.empty((m, 0), dtype=torch.bfloat16, device=DEV), bw, 0.73, bias=bias)
+        assert torch.equal(y.cpu(), bias.cpu().expand(m, 4))

@@ -147,3 +147,38 @@ def test_grouped_layers_match_oracle_and_reload(gpu_lib, gs, tmp_path):
     load_opq(fresh, path)
     assert fresh[0].group_size == gs
     assert torch.equal(y0.view(torch.int16), fresh(x).view(torch.int16))
+
+
+@pytest.mark.parametrize("bits", [3, 5, 6])
+def test_bits_layers_match_oracle_and_reload(gpu_lib, bits, tmp_path):
+    """replace_with_opq(bits=3|5|6): codes equal the oracle's b-bit codes, each
+    layer's output meets the linear bar against the oracle's reconstruction
+    (inputs of 3 x 30 and 100 x 1 tokens: the skinny and the tiled product),
+    and a save / load round trip reproduces the outputs bit for bit."""
+    model = _stack(torch.bfloat16, 7600 + bits)
+    ws = {name: (mod.weight.detach().float().cpu().numpy(), mod.bias)
+          for name, mod in model.named_modules() if isinstance(mod, nn.Linear)}
+    assert replace_with_opq(model, bits=bits, alpha=0.73) == ["0", "2", "4"]
+    seen = {}
+    for name, mod in model.named_modules():
+        if isinstance(mod, OPQLinear):
+            assert mod.bits == bits
+            mod.register_forward_hook(lambda m, i, o, nm=name: seen.__setitem__(nm, (i[0], o)))
+    refs = {}
+    for name, (w, bias) in ws.items():
+        layer = model.get_submodule(name)
+        ref = O.quantize_bits(w, 0.73, bits)
+        assert np.array_equal(layer.packed.cpu().numpy().view(np.uint32), ref[0])
+        assert np.array_equal(layer.sign_packed.cpu().numpy().view(np.uint32), ref[1])
+        refs[name] = O.dequantize_bits(*ref, 0.73, bits)
+    for shape in ((3, 30, 256), (100, 256)):
+        x = torch.from_numpy(WL.normal(7601 + len(shape), shape)).to(DEV, torch.bfloat16)
+        y0 = model(x)
+        for name, (_, bias) in ws.items():
+            _check_layer_output(*seen[name], refs[name], bias)
+    path = str(tmp_path / "bits.safetensors")
+    save_opq(model, path)
+    fresh = _stack(torch.bfloat16, 1)
+    load_opq(fresh, path)
+    assert fresh[0].bits == bits
+    assert torch.equal(y0.view(torch.int16), fresh(x).view(torch.int16))

@@ -62,8 +62,16 @@ def test_replace_refuses_host_weights_and_changes_nothing():
 
 
 def test_replace_checks_bits():
+    for bits in (2, 7, 8):
+        with pytest.raises(ValueError):
+            replace_with_opq(nn.Sequential(nn.Linear(64, 8)), bits=bits)
+    with pytest.raises(ValueError, match="4-bit"):
+        replace_with_opq(nn.Sequential(nn.Linear(64, 8)), bits=5, group_size=64)
+    # a b-bit layer's buffers follow the bit stream layout
+    lay = OPQLinear(96, 8, bits=5)
+    assert tuple(lay.packed.shape) == (8, 96 * 5 // 32) and lay.bits == 5
     with pytest.raises(ValueError):
-        replace_with_opq(nn.Sequential(nn.Linear(64, 8)), bits=3)
+        OPQLinear(96, 8, bits=6, group_size=32)
 
 
 def test_replace_skips_ineligible_layers_before_touching_weights():
@@ -110,8 +118,9 @@ def test_file_is_plain_tensors_with_a_json_header(tmp_path):
     save_opq(src, path)
     with safe_open(path, framework="pt") as f:
         meta = json.loads(f.metadata()["opq"])
-        assert meta["format"] == FORMAT and meta["bits"] == 4
-        assert meta["layers"]["0"] == {"in": 64, "out": 16, "alpha": 1.0, "bias": True, "group": 0}
+        assert meta["format"] == FORMAT
+        assert meta["layers"]["0"] == {"in": 64, "out": 16, "alpha": 1.0, "bias": True, "group": 0,
+                                       "bits": 4}
         assert sorted(f.keys()) == ["0.bias", "0.mx", "0.packed", "0.sign_packed"]
 
 

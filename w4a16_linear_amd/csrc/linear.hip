@@ -678,6 +678,225 @@ __global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
   }
 }
 
+// ---------------------------------------------------------------- dense bf16 weights
+//
+// y = x W'^T with W' already bfloat16 in memory ([n][k]).  This serves the
+// other code widths: opq_linear_bits first writes W' into a workspace with the
+// b-bit dequantizer, the way the card's OPQLinear decodes its weights before a
+// dense matmul.  The kernels are the two above with the weight operand read
+// instead of decoded.
+//
+// Tiled (m > 64): linear_tiled's tile, waves and fragments, with W' staged like
+// x (256 rows x 64 k per stage, same swizzle, buffer loads straight to LDS),
+// two stages of each.  A wave's B fragment is one ds_read_b128 per sub-step.
+
+template <bool kHalfTail>
+__global__ __launch_bounds__(kTThreads, 1) void linear_dense_tiled(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wd, const float* __restrict__ bias,
+    int m, int n, int k, int tiles_m, void* __restrict__ y, int y_bf16) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x0[kXStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x1[kXStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w0[kXStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_w1[kXStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
+  const int m0 = tile_m * kTM;
+  const int n0 = tile_n * kTN;
+  const int h = lane >> 5;
+  const int brow = n0 + wave * 32 + (lane & 31);
+  const int nsteps = (k + kTK - 1) / kTK;
+
+  // both operands: load i of wave w fills 1 KB block 4w + i of a stage (rows
+  // 8(4w + i) + l/8, chunk slot l%8), as in linear_tiled
+  const char* xbase = reinterpret_cast<const char*>(x + (int64_t)m0 * k);
+  const char* wbase = reinterpret_cast<const char*>(wd + (int64_t)n0 * k);
+  const __amdgpu_buffer_rsrc_t x_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)xbase, (short)0, (int)min((int64_t)(m - m0) * k * 2, (int64_t)0x7FFFFFFF), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)wbase, (short)0, (int)min((int64_t)(n - n0) * k * 2, (int64_t)0x7FFFFFFF), kBufferFlags);
+  uint32_t x_off[kXLoads], w_off[kXLoads];
+  int chunk[kXLoads];
+#pragma unroll
+  for (int i = 0; i < kXLoads; ++i) {
+    const int r = 8 * (kXLoads * wave + i) + (lane >> 3);
+    chunk[i] = (lane & 7) ^ ((r >> 1) & 7);
+    x_off[i] = (uint32_t)(min(m0 + r, m - 1) - m0) * (uint32_t)k * 2u + (uint32_t)chunk[i] * 16u;
+    w_off[i] = (uint32_t)(min(n0 + r, n - 1) - n0) * (uint32_t)k * 2u + (uint32_t)chunk[i] * 16u;
+  }
+  auto load = [&](int kt, uint8_t* sx, uint8_t* sw) __attribute__((always_inline)) {
+    const uint32_t soff = (uint32_t)kt * (kTK * 2);
+#pragma unroll
+    for (int i = 0; i < kXLoads; ++i) {
+      uint32_t xo = x_off[i], wo = w_off[i];
+      if constexpr (kHalfTail) {
+        // chunks past k in the final half step re-read the step's first half
+        if (kt == nsteps - 1 && chunk[i] >= 4) { xo -= 64u; wo -= 64u; }
+      }
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(x_rsrc, (lds_ptr_t)(sx + (kXLoads * wave + i) * 1024),
+                                               16, xo, soff, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(w_rsrc, (lds_ptr_t)(sw + (kXLoads * wave + i) * 1024),
+                                               16, wo, soff, 0, 0);
+    }
+  };
+  auto read_a = [&](const uint8_t* st, int s, bf16x8_t (&a)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mi = 0; mi < 8; ++mi)
+      a[mi] = *reinterpret_cast<const bf16x8_t*>(st + x_slot(mi * 32 + (lane & 31), s + 4 * h));
+  };
+  auto read_b = [&](const uint8_t* st, int kt, int s, bf16x8_t& b) __attribute__((always_inline)) {
+    b = *reinterpret_cast<const bf16x8_t*>(st + x_slot(wave * 32 + (lane & 31), s + 4 * h));
+    if constexpr (kHalfTail) {
+      if (kt == nsteps - 1 && h == 1) b = bf16x8_t{};  // the dead half of the final half step
+    }
+  };
+
+  floatx16_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[i][e] = 0.0f;
+  bf16x8_t a_frag[8], b_buf[2];
+  if (nsteps > 0) {
+    load(0, s_x0, s_w0);
+    wait_vm<0>();
+    lds_barrier_dma();
+    read_a(s_x0, 0, a_frag);
+    read_b(s_w0, 0, 0, b_buf[0]);
+  }
+  // step kt: stage kt & 1; the loads of step kt + 1 go to the other stage, which
+  // served step kt - 1, and are waited for before this step's barrier
+  auto step = [&](int kt, auto par) __attribute__((always_inline)) {
+    constexpr int p = decltype(par)::value;
+    uint8_t* sx = p ? s_x1 : s_x0;
+    uint8_t* sw = p ? s_w1 : s_w0;
+    uint8_t* nx = p ? s_x0 : s_x1;
+    uint8_t* nw = p ? s_w0 : s_w1;
+    load(kt + 1, nx, nw);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int cur = s & 1, nxt = cur ^ 1;
+#pragma unroll
+      for (int mi = 0; mi < 8; ++mi)
+        acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag[mi], b_buf[cur], acc[mi], 0, 0, 0);
+      if (s < 3) {
+        read_a(sx, s + 1, a_frag);
+        read_b(sw, kt, s + 1, b_buf[nxt]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+          if (s == 0) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+        }
+      } else {
+        wait_vm<0>();
+        lds_barrier_dma();
+        read_a(nx, 0, a_frag);
+        read_b(nw, kt + 1, 0, b_buf[nxt]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int kt = 0;
+  for (; kt + 1 < nsteps; kt += 2) {
+    step(kt, StepPos<0>{});
+    step(kt + 1, StepPos<1>{});
+  }
+  if (kt < nsteps) step(kt, StepPos<0>{});
+  wait_vm<0>();  // no load may still be writing LDS when the block ends
+
+  const float bv = (bias && brow < n) ? bias[brow] : 0.0f;
+#pragma unroll
+  for (int mi = 0; mi < 8; ++mi)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = m0 + mi * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
+      if (row < m && brow < n) store_y(y, y_bf16, (int64_t)row * n + brow, acc[mi][e] + bv);
+    }
+}
+
+// Skinny (m <= 64): linear_skinny's blocks (16 weight rows, all of k, waves
+// over 128-wide k blocks, a reduction in LDS) with lane (r, g) reading the 64
+// bytes of W' row r, k 32 g ... + 31 of each k block straight into its four A
+// fragments.
+template <int NMB>  // 16-row blocks of x (1, 2 or 4)
+__global__ __launch_bounds__((NMB <= 2 ? 16 : 8) * kWave) void linear_dense_skinny(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wd, const float* __restrict__ bias,
+    int m, int n, int k, void* __restrict__ y, int y_bf16) {
+  constexpr int W = NMB <= 2 ? 16 : 8;
+  constexpr int kXRows = 16 * NMB;
+  constexpr int kXL = kXRows / 4;                   // x loads per lane per k block
+  constexpr int kStage = kXRows * kSkBlockK;
+  constexpr int kOut = NMB * 4 * kWave;
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[W * kStage];
+  float* s_red = reinterpret_cast<float*>(s_x);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid / kWave;
+  const int n0 = blockIdx.x * kSkRows;
+  const int nkb = (k + kSkBlockK - 1) / kSkBlockK;
+  const int mine = nkb > wave ? (nkb - 1 - wave) / W + 1 : 0;
+  const int xr = lane >> 4, xc = lane & 15;
+  const int r = lane & 15, g = lane >> 4;
+  const char* wrow = reinterpret_cast<const char*>(wd + (int64_t)min(n0 + r, n - 1) * k);
+  const char* xbase = reinterpret_cast<const char*>(x);
+  uint32_t x_off[kXL];
+#pragma unroll
+  for (int i = 0; i < kXL; ++i) x_off[i] = (uint32_t)min(4 * i + xr, m - 1) * (uint32_t)k * 2u;
+
+  floatx4_t acc[NMB];
+#pragma unroll
+  for (int b = 0; b < NMB; ++b) acc[b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  uint16_t* stage = s_x + wave * kStage;
+  for (int idx = 0; idx < mine; ++idx) {
+    const int kb = (wave + W * idx) * kSkBlockK;
+    const bool live = kb + 32 * g < k;
+    const int kw = live ? kb + 32 * g : kb;          // a part past k re-reads the first
+    uint4 wv[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) wv[t] = *reinterpret_cast<const uint4*>(wrow + (int64_t)(kw + 8 * t) * 2);
+    const int kx = kb + 8 * xc < k ? kb + 8 * xc : kb;
+#pragma unroll
+    for (int i = 0; i < kXL; ++i) {
+      if (NMB == 1 && 4 * i >= m) continue;          // x rows wholly past m
+      const uint4 v = *reinterpret_cast<const uint4*>(xbase + x_off[i] + (uint32_t)kx * 2u);
+      *reinterpret_cast<u32x4_t*>(stage + xs_off(4 * i + xr, xc)) = u32x4_t{v.x, v.y, v.z, v.w};
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint4 a4 = live ? wv[t] : make_uint4(0u, 0u, 0u, 0u);
+      const bf16x8_t a = __builtin_bit_cast(bf16x8_t, a4);
+#pragma unroll
+      for (int b = 0; b < NMB; ++b) {
+        const bf16x8_t bx = *reinterpret_cast<const bf16x8_t*>(stage + xs_off(16 * b + r, 4 * g + t));
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bx, acc[b], 0, 0, 0);
+      }
+    }
+    wave_lds_sync();  // the stage is rewritten by the next k block
+  }
+  __syncthreads();
+#pragma unroll
+  for (int b = 0; b < NMB; ++b)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_red[wave * kOut + (b * 4 + e) * kWave + lane] = acc[b][e];
+  __syncthreads();
+  for (int o = tid; o < kSkRows * kXRows; o += W * kWave) {
+    const int i = o % kSkRows, mm = o / kSkRows;
+    const int gcol = n0 + i;
+    if (mm < m && gcol < n) {
+      const int src_o = ((mm >> 4) * 4 + (i & 3)) * kWave + 16 * (i >> 2) + (mm & 15);
+      float val = s_red[src_o];
+#pragma unroll
+      for (int w = 1; w < W; ++w) val += s_red[w * kOut + src_o];
+      store_y(y, y_bf16, (int64_t)mm * n + gcol, val + (bias ? bias[gcol] : 0.0f));
+    }
+  }
+}
+
 }  // namespace
 
 size_t linear_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
@@ -729,6 +948,23 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32
                          const Levels& lv, void* y, bool y_bf16, void*, hipStream_t stream) {
   return launch_linear_any<0>(x, packed, sign, scale, nullptr, bias, m, n, k, lv, y, y_bf16,
                               stream);
+}
+
+hipError_t launch_linear_dense(const uint16_t* x, const uint16_t* wd, const float* bias, int64_t m,
+                              int64_t n, int64_t k, void* y, bool y_bf16, hipStream_t stream) {
+  if (m <= kSkinnyMaxM) {
+    const int64_t blocks = (n + kSkRows - 1) / kSkRows;
+    auto kernel = m <= 16 ? linear_dense_skinny<1> : (m <= 32 ? linear_dense_skinny<2> : linear_dense_skinny<4>);
+    const unsigned th = (m <= 32 ? 16 : 8) * kWave;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(th), 0, stream, x, wd, bias, (int)m, (int)n,
+                       (int)k, y, (int)y_bf16);
+  } else {
+    const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
+    auto kernel = (k % kTK) ? linear_dense_tiled<true> : linear_dense_tiled<false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kTThreads), 0, stream, x, wd,
+                       bias, (int)m, (int)n, (int)k, (int)tiles_m, y, (int)y_bf16);
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_linear_grouped(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,

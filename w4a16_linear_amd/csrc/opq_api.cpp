@@ -249,6 +249,44 @@ int opq_dequantize_grouped(const uint32_t* packed, const uint32_t* sign, const u
                                                    w_out, static_cast<hipStream_t>(stream)));
 }
 
+size_t opq_linear_bits_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits) {
+  if (bits == 4) return opq_linear_workspace_bytes(m, n, k);
+  if (m <= 0 || n <= 0 || k <= 0 || !bits_ok(bits)) return 0;
+  return ((size_t)n * (size_t)k * 2u + 255u) & ~(size_t)255u;  // W' as bfloat16
+}
+
+int opq_linear_bits(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
+                    const float* scale, const float* bias, int64_t m, int64_t n, int64_t k, int bits,
+                    float alpha, void* y, int y_dtype, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (bits == 4)
+    return opq_linear(x, packed, sign, scale, bias, m, n, k, alpha, y, y_dtype, workspace,
+                      workspace_bytes, stream);
+  if ((m > 0 && k > 0 && !x) || (n > 0 && k > 0 && (!packed || !sign)) || (n > 0 && !scale) ||
+      (m > 0 && n > 0 && !y))
+    return OPQ_ERR_NULL;
+  if (m < 0 || !shape_ok(n, k) || !bits_ok(bits)) return OPQ_ERR_SHAPE;
+  if (!alpha_ok(alpha)) return OPQ_ERR_ALPHA;
+  if (!aligned16(x) || !aligned16(packed) || !aligned16(sign) || !aligned16(scale) ||
+      !aligned16(y) || (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)))
+    return OPQ_ERR_ALIGN;
+  if (y_dtype != OPQ_F32 && y_dtype != OPQ_BF16) return OPQ_ERR_DTYPE;
+  const size_t need = opq_linear_bits_workspace_bytes(m, n, k, bits);
+  if (workspace_bytes < need || (need > 0 && !workspace)) return OPQ_ERR_WORKSPACE;
+  if (m == 0 || n == 0) return OPQ_OK;
+  if (k > kMaxK || n > kMaxLinearN) return OPQ_ERR_UNSUPPORTED;
+  opq::DecisionPointsN dp;
+  opq::LevelsN lv;
+  if (!bits_tables(alpha, bits, dp, lv)) return OPQ_ERR_ALPHA;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  uint16_t* wd = static_cast<uint16_t*>(workspace);
+  if (k > 0) {
+    const int e = hip_status(opq::launch_dequantize_bits(packed, sign, scale, n, k, bits, lv, wd, st));
+    if (e != OPQ_OK) return e;
+  }
+  return hip_status(opq::launch_linear_dense(x, wd, bias, m, n, k, y, y_dtype == OPQ_BF16, st));
+}
+
 int opq_linear_grouped(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                        const uint16_t* scale16, const float* bias, int64_t m, int64_t n,
                        int64_t k, int64_t group, float alpha, void* y, int y_dtype,

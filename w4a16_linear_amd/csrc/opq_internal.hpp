@@ -63,6 +63,10 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32
                          const Levels& lv, void* y, bool y_bf16, void* workspace,
                          hipStream_t stream);
 
+// linear.hip: y = x W'^T (+ bias) with W' bfloat16 [n][k] in device memory
+hipError_t launch_linear_dense(const uint16_t* x, const uint16_t* wd, const float* bias, int64_t m,
+                               int64_t n, int64_t k, void* y, bool y_bf16, hipStream_t stream);
+
 // b-bit codes (3..6), codes of a row as a little-endian bit stream along k.
 // quantize.hip
 bool bits_supported(const DecisionPointsN& dp, int64_t k);

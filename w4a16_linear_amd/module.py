@@ -9,7 +9,9 @@ over a model skeleton and then overwrites its ``packed`` / ``sign_packed`` /
 ``mx`` buffers from saved files.  The buffers here keep those names.  ``mx``
 is either one float32 max per output row, or (``group_size`` set) the card's
 own form: one float16 max per group of ``group_size`` weights along the input
-dimension ("技术细节 / 存储格式").
+dimension ("技术细节 / 存储格式").  ``bits`` (the configuration section's
+``OPQ_BITS``: 3, 4, 5 or 6) sets the code width; other than 4, ``packed``
+holds the codes of a row as a bit stream along the input dimension.
 
 Every step runs in libopq's kernels: a layer whose buffers are not on the GPU
 raises instead of computing anywhere else.  Saved files are safetensors (plain
@@ -39,15 +41,17 @@ def _f32(alpha: float) -> float:
 
 
 class OPQLinear(nn.Module):
-    """y = x W'^T (+ bias) with W' held as OPQ codes: 4-bit magnitudes
-    (``packed`` [out, in/8] int32), a sign plane (``sign_packed`` [out, in/32]
-    int32) and the maxima ``mx``: float32 [out] (one per output row), or
-    float16 [out, in/group_size] with ``group_size`` in 32, 64, 128, 256.  The
-    bias, when present, is float32.  x may be bfloat16 or float32 (it is
-    rounded to bfloat16, the layer's activation type); y has x's dtype."""
+    """y = x W'^T (+ bias) with W' held as OPQ codes: `bits`-bit magnitudes
+    (``packed`` [out, in*bits/32] int32; for 4 bits eight nibbles per word), a
+    sign plane (``sign_packed`` [out, in/32] int32) and the maxima ``mx``:
+    float32 [out] (one per output row), or, for 4 bits, float16
+    [out, in/group_size] with ``group_size`` in 32, 64, 128, 256.  The bias,
+    when present, is float32.  x may be bfloat16 or float32 (it is rounded to
+    bfloat16, the layer's activation type); y has x's dtype."""
 
     def __init__(self, in_features: int, out_features: int, bias: bool = True,
-                 alpha: float = 0.73, device=None, group_size: Optional[int] = None):
+                 alpha: float = 0.73, device=None, group_size: Optional[int] = None,
+                 bits: int = 4):
         super().__init__()
         if in_features <= 0 or in_features % 32:
             raise ValueError(f"in_features must be a positive multiple of 32, got {in_features}")
@@ -57,12 +61,17 @@ class OPQLinear(nn.Module):
                                        in_features % group_size):
             raise ValueError(f"group_size must be 32, 64, 128 or 256 and divide in_features="
                              f"{in_features}, got {group_size}")
+        if bits not in (3, 4, 5, 6):
+            raise ValueError(f"bits must be 3, 4, 5 or 6, got {bits}")
+        if group_size is not None and bits != 4:
+            raise ValueError("group-wise maxima are built for 4-bit codes only")
         self.in_features = int(in_features)
         self.out_features = int(out_features)
         self.alpha = _f32(alpha)
         self.group_size = group_size
+        self.bits = int(bits)
         kw = dict(dtype=torch.int32, device=device)
-        self.register_buffer("packed", torch.zeros((out_features, in_features // 8), **kw))
+        self.register_buffer("packed", torch.zeros((out_features, in_features * bits // 32), **kw))
         self.register_buffer("sign_packed", torch.zeros((out_features, in_features // 32), **kw))
         if group_size:
             self.register_buffer("mx", torch.zeros((out_features, in_features // group_size),
@@ -80,7 +89,7 @@ class OPQLinear(nn.Module):
 
     @classmethod
     def from_linear(cls, lin: nn.Linear, alpha: float = 0.73,
-                    group_size: Optional[int] = None) -> "OPQLinear":
+                    group_size: Optional[int] = None, bits: int = 4) -> "OPQLinear":
         """Quantize an nn.Linear whose weight is on the GPU (float32 or bfloat16)."""
         w = lin.weight.detach()
         if not w.is_cuda:
@@ -89,8 +98,10 @@ class OPQLinear(nn.Module):
         if w.dtype not in (torch.float32, torch.bfloat16):
             w = w.float()
         out = cls(lin.in_features, lin.out_features, bias=lin.bias is not None, alpha=alpha,
-                  device=w.device, group_size=group_size)
-        if group_size:
+                  device=w.device, group_size=group_size, bits=bits)
+        if bits != 4:
+            opq.quantize_bits(w.contiguous(), out.alpha, bits, out=out.qweight())
+        elif group_size:
             opq.quantize_grouped(w.contiguous(), out.alpha, group_size, out=out.qweight())
         else:
             opq.quantize(w.contiguous(), out.alpha, out=out.qweight())
@@ -99,6 +110,8 @@ class OPQLinear(nn.Module):
         return out
 
     def qweight(self):
+        if self.bits != 4:
+            return opq.BitsWeight(self.packed, self.sign_packed, self.mx, self.bits)
         if self.group_size:
             return opq.GroupedWeight(self.packed, self.sign_packed, self.mx, self.group_size)
         return opq.QuantizedWeight(self.packed, self.sign_packed, self.mx)
@@ -122,7 +135,7 @@ class OPQLinear(nn.Module):
     def extra_repr(self) -> str:
         return (f"in_features={self.in_features}, out_features={self.out_features}, "
                 f"bias={self.bias is not None}, alpha={self.alpha:.8g}, "
-                f"group_size={self.group_size}")
+                f"group_size={self.group_size}, bits={self.bits}")
 
 
 # ---------------------------------------------------------------- conversion
@@ -150,10 +163,14 @@ def replace_with_opq(model: nn.Module, bits: int = 4, alpha: float = 0.73,
     None keeps one float32 max per output row; 32, 64, 128 or 256 stores the
     card's float16 max per group.  Layers whose in_features is not a multiple
     of 32 (and of the group), and names under `skip`, stay as they are.  A
-    Linear reached under several names is quantized once and shared.  All
-    eligible weights must be on the GPU: nothing is replaced otherwise."""
-    if bits != 4:
-        raise ValueError(f"only 4-bit codes are built (bits={bits})")
+    Linear reached under several names is quantized once and shared.  `bits`
+    3, 5 or 6 stores b-bit codes (per-row maxima only); their forward pass
+    decodes into a workspace before a dense product.  All eligible weights
+    must be on the GPU: nothing is replaced otherwise."""
+    if bits not in (3, 4, 5, 6):
+        raise ValueError(f"bits must be 3, 4, 5 or 6, got {bits}")
+    if group_size is not None and bits != 4:
+        raise ValueError("group-wise maxima are built for 4-bit codes only")
     if group_size is not None and group_size not in (32, 64, 128, 256):
         raise ValueError(f"group_size must be 32, 64, 128 or 256, got {group_size}")
     alpha = _f32(alpha)
@@ -165,7 +182,7 @@ def replace_with_opq(model: nn.Module, bits: int = 4, alpha: float = 0.73,
     made: Dict[int, OPQLinear] = {}
     for _, parent, cname, child in found:
         if id(child) not in made:
-            made[id(child)] = OPQLinear.from_linear(child, alpha, group_size)
+            made[id(child)] = OPQLinear.from_linear(child, alpha, group_size, bits)
         setattr(parent, cname, made[id(child)])
     return [full for full, _, _, _ in found]
 
@@ -183,7 +200,7 @@ def _opq_layers(model: nn.Module):
 def save_opq(model: nn.Module, path: str) -> List[str]:
     """Write every OPQLinear's buffers to a safetensors file; returns the
     layer names saved.  The header records the format, and per layer its
-    shape, alpha and whether it has a bias.  A layer reached under several
+    shape, alpha, code width, group size and whether it has a bias.  A layer reached under several
     names is saved once, under the first."""
     from safetensors.torch import save_file
 
@@ -191,10 +208,11 @@ def save_opq(model: nn.Module, path: str) -> List[str]:
     layers = {}
     for name, mod in _opq_layers(model):
         layers[name] = {"in": mod.in_features, "out": mod.out_features, "alpha": mod.alpha,
-                        "bias": mod.bias is not None, "group": mod.group_size or 0}
+                        "bias": mod.bias is not None, "group": mod.group_size or 0,
+                        "bits": mod.bits}
         for b in ("packed", "sign_packed", "mx") + (("bias",) if mod.bias is not None else ()):
             tensors[f"{name}.{b}"] = getattr(mod, b).detach().to("cpu").contiguous()
-    meta = {_META_KEY: json.dumps({"format": FORMAT, "bits": 4, "layers": layers})}
+    meta = {_META_KEY: json.dumps({"format": FORMAT, "layers": layers})}
     save_file(tensors, path, metadata=meta)
     return list(layers)
 
@@ -227,7 +245,8 @@ def load_opq(model: nn.Module, path: str, device=None) -> List[str]:
                                  f"{old.out_features}x{old.in_features} in the model")
             dev = torch.device(device) if device is not None else ref_dev
             new = OPQLinear(info["in"], info["out"], bias=info["bias"], alpha=info["alpha"],
-                            device=dev, group_size=info.get("group") or None)
+                            device=dev, group_size=info.get("group") or None,
+                            bits=info.get("bits", 4))
             for b in ("packed", "sign_packed", "mx") + (("bias",) if info["bias"] else ()):
                 t = f.get_tensor(f"{name}.{b}")
                 dst = getattr(new, b)

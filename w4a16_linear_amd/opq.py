@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libopq.so")
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 OPQ_F32 = 0
 OPQ_BF16 = 1
@@ -54,6 +54,13 @@ _SIGNATURES = {
     "opq_error_sums_bits": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                            ctypes.c_int64, ctypes.c_int, ctypes.c_float,
                                            ctypes.c_void_p, ctypes.c_void_p]),
+    "opq_linear_bits_workspace_bytes": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64,
+                                                          ctypes.c_int64, ctypes.c_int]),
+    "opq_linear_bits": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
     "opq_quantize_grouped": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -269,6 +276,13 @@ def dequantize(qw, alpha: float, out: Optional[torch.Tensor] = None) -> torch.Te
                                         qw.bits, alpha, _ptr(out), _stream(qw.packed.device))
         _check("opq_dequantize_bits", st)
         return out
+    if isinstance(qw, BitsWeight):
+        _check_bits(qw, n, k)
+        st = load().opq_linear_bits(_ptr(x), _ptr(qw.packed), _ptr(qw.sign), _ptr(qw.scale),
+                                    _ptr(bias), m, n, k, qw.bits, alpha, _ptr(out), y_dtype,
+                                    _ptr(workspace), ws_bytes, _stream(x.device))
+        _check("opq_linear_bits", st)
+        return out
     if isinstance(qw, GroupedWeight):
         _check_grouped(qw, n, k)
         if out is None:
@@ -289,8 +303,11 @@ def dequantize(qw, alpha: float, out: Optional[torch.Tensor] = None) -> torch.Te
     return out
 
 
-def linear_workspace_bytes(m: int, n: int, k: int) -> int:
-    return int(load().opq_linear_workspace_bytes(m, n, k))
+def linear_workspace_bytes(m: int, n: int, k: int, bits: int = 4) -> int:
+    """Workspace bytes of opq_linear (bits = 4) or opq_linear_bits."""
+    if bits == 4:
+        return int(load().opq_linear_workspace_bytes(m, n, k))
+    return int(load().opq_linear_bits_workspace_bytes(m, n, k, bits))
 
 
 def error_sums(w: torch.Tensor, alpha: float, out: Optional[torch.Tensor] = None,
@@ -348,8 +365,9 @@ def shared_workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor
 def linear(x: torch.Tensor, qw, alpha: float, bias: Optional[torch.Tensor] = None,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
-    """y[m, n] = x[m, k] W'^T (+ bias), W' made on chip from qw (a QuantizedWeight
-    or a GroupedWeight).
+    """y[m, n] = x[m, k] W'^T (+ bias), W' made from qw: a QuantizedWeight or a
+    GroupedWeight (decoded on chip) or a BitsWeight (3, 5 or 6 bits: decoded
+    into the workspace, then a dense bf16 product).
 
     out_dtype is torch.float32 or torch.bfloat16 (the float32 result rounded
     to nearest even).  `workspace`, when given, must be a zero-filled uint8
@@ -374,12 +392,19 @@ def linear(x: torch.Tensor, qw, alpha: float, bias: Optional[torch.Tensor] = Non
     _need_cuda("out", out, out.dtype, 2)
     if tuple(out.shape) != (m, n):
         raise ValueError(f"out must have shape {(m, n)}, got {tuple(out.shape)}")
-    need = linear_workspace_bytes(m, n, k)
+    need = linear_workspace_bytes(m, n, k, qw.bits if isinstance(qw, BitsWeight) else 4)
     if workspace is None:
         workspace = shared_workspace(x.device, need)
     elif not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous CUDA (HIP) tensor")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if isinstance(qw, BitsWeight):
+        _check_bits(qw, n, k)
+        st = load().opq_linear_bits(_ptr(x), _ptr(qw.packed), _ptr(qw.sign), _ptr(qw.scale),
+                                    _ptr(bias), m, n, k, qw.bits, alpha, _ptr(out), y_dtype,
+                                    _ptr(workspace), ws_bytes, _stream(x.device))
+        _check("opq_linear_bits", st)
+        return out
     if isinstance(qw, GroupedWeight):
         _check_grouped(qw, n, k)
         st = load().opq_linear_grouped(_ptr(x), _ptr(qw.packed), _ptr(qw.sign), _ptr(qw.scale16),
