@@ -253,6 +253,23 @@ int opq_linear_bits(const uint16_t* x, const uint32_t* packed, const uint32_t* s
                     void* stream);
 
 /*
+ * opq_linear_bits without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  W' goes into a fixed array that the library
+ * holds on every GPU it runs on (160 MiB, kept until the process ends); shapes
+ * needing more (n * k * 2 bytes above 160 MiB) return OPQ_ERR_UNSUPPORTED.
+ * Every call on one GPU uses that same array, so calls that may overlap on one
+ * GPU (other streams or threads) race; calls in one stream follow each other.
+ * No part of the array needs to start at zero.  bits = 4 is opq_linear, which
+ * needs no scratch.  The call allocates nothing (no hipMalloc, no allocator of
+ * any library).  Other arguments and errors as for opq_linear_bits, plus
+ * OPQ_ERR_HIP when the runtime cannot report the array's address.
+ */
+int opq_linear_bits_noalloc(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
+                            const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
+                            int bits, float alpha, void* y, int y_dtype, void* stream);
+
+/*
  * Group-wise stored form: the card's own ("技术细节 / 存储格式": one float16
  * max per group of weights; the configuration section offers groups of 32,
  * 64, 128 or 256 weights; "推理解码": the decode multiplies by that group

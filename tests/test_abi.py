@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared_functions()
-    assert len(names) == 17
+    assert len(names) == 18
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(opq._SIGNATURES)
@@ -206,6 +206,27 @@ def test_linear_bits_argument_checks(lib):
     # bits = 4 is opq_linear itself (no workspace needed)
     assert call(bits=4, ws=None, wsb=0, k=65536 + 32) == UNSUPPORTED
     assert call(bits=4, ws=None, wsb=0, m=0) == OK
+
+
+def test_linear_bits_noalloc_argument_checks(lib):
+    """The allocation-free variant checks like opq_linear_bits and refuses
+    shapes whose W' exceeds its fixed 160 MiB (without enqueuing anything)."""
+    f = lib.opq_linear_bits_noalloc
+
+    def call(x=FAKE, sc=FAKE, m=8, n=16, k=64, bits=5, a=0.73, y=FAKE, yd=0):
+        return f(x, FAKE, FAKE, sc, None, m, n, k, bits, a, y, yd, None)
+
+    assert call(x=None) == NULL
+    assert call(bits=7) == SHAPE
+    assert call(a=-1.0) == ALPHA
+    assert call(y=MISALIGNED) == ALIGN
+    assert call(yd=9) == DTYPE
+    assert call(m=0) == OK and call(n=0) == OK
+    big_n = (160 << 20) // (2 * 4096) + 1              # n * 4096 * 2 bytes just past 160 MiB
+    assert call(n=big_n, k=4096) == UNSUPPORTED
+    assert call(n=big_n, k=4096, x=None) == NULL        # argument errors keep their codes
+    assert call(n=big_n - 1, k=4096, m=0) == OK
+    assert call(bits=4, k=65536 + 32) == UNSUPPORTED    # opq_linear's own limit
 
 
 def test_grouped_argument_checks(lib):

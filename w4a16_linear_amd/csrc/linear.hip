@@ -13,6 +13,8 @@
 //    rows x all of k, the waves of a block reducing in LDS (details below).
 //  * otherwise: 256x256 output tiles with v_mfma_f32_32x32x16_bf16; x staged
 //    through LDS (details below).
+#include <mutex>
+
 #include "decode.hpp"
 #include "device_common.hpp"
 #include "group.hpp"
@@ -965,6 +967,33 @@ hipError_t launch_linear_dense(const uint16_t* x, const uint16_t* wd, const floa
                        bias, (int)m, (int)n, (int)k, (int)tiles_m, y, (int)y_bf16);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fixed scratch
+//
+// Device memory for callers that cannot allocate (code under graph capture,
+// serving loops, harnesses that forbid hipMalloc): opq_linear_bits_noalloc
+// writes its bfloat16 W' here instead of into a caller workspace.  Every GPU
+// the library runs on holds one copy, of kNoAllocScratchBytes, until the
+// process ends; calls on one GPU share it, so calls that may overlap there
+// race.  In host code `scratch` names a host-side stand-in, never the device
+// memory: kernels get the address hipGetSymbolAddress reports for the current
+// device, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+void* noalloc_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev] = p;
+  }
+  return addr[dev];
 }
 
 hipError_t launch_linear_grouped(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,

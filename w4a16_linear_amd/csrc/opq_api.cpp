@@ -287,6 +287,24 @@ int opq_linear_bits(const uint16_t* x, const uint32_t* packed, const uint32_t* s
   return hip_status(opq::launch_linear_dense(x, wd, bias, m, n, k, y, y_dtype == OPQ_BF16, st));
 }
 
+int opq_linear_bits_noalloc(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
+                            const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
+                            int bits, float alpha, void* y, int y_dtype, void* stream) {
+  if (bits == 4)  // the on-chip decoder: no scratch at all
+    return opq_linear(x, packed, sign, scale, bias, m, n, k, alpha, y, y_dtype, nullptr, 0, stream);
+  // Arguments first, as opq_linear_bits checks them: with no workspace that
+  // call never launches, and answers OPQ_ERR_WORKSPACE once all else is valid.
+  const int st = opq_linear_bits(x, packed, sign, scale, bias, m, n, k, bits, alpha, y, y_dtype,
+                                 nullptr, SIZE_MAX, nullptr);
+  if (st != OPQ_ERR_WORKSPACE) return st;  // an argument error, or an empty product
+  const size_t need = opq_linear_bits_workspace_bytes(m, n, k, bits);
+  if (need > opq::kNoAllocScratchBytes) return OPQ_ERR_UNSUPPORTED;
+  void* ws = opq::noalloc_scratch();
+  if (!ws) return OPQ_ERR_HIP;
+  return opq_linear_bits(x, packed, sign, scale, bias, m, n, k, bits, alpha, y, y_dtype, ws, need,
+                         stream);
+}
+
 int opq_linear_grouped(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                        const uint16_t* scale16, const float* bias, int64_t m, int64_t n,
                        int64_t k, int64_t group, float alpha, void* y, int y_dtype,

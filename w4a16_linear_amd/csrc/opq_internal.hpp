@@ -63,6 +63,12 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32
                          const Levels& lv, void* y, bool y_bf16, void* workspace,
                          hipStream_t stream);
 
+// linear.hip: a fixed device array per GPU (the allocation-free b-bit linear
+// layer) and its address on the current device (nullptr if the runtime
+// cannot report it)
+constexpr size_t kNoAllocScratchBytes = size_t(160) << 20;
+void* noalloc_scratch();
+
 // linear.hip: y = x W'^T (+ bias) with W' bfloat16 [n][k] in device memory
 hipError_t launch_linear_dense(const uint16_t* x, const uint16_t* wd, const float* bias, int64_t m,
                                int64_t n, int64_t k, void* y, bool y_bf16, hipStream_t stream);

@@ -61,6 +61,11 @@ _SIGNATURES = {
                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                        ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
                                        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "opq_linear_bits_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                               ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                               ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                               ctypes.c_float, ctypes.c_void_p, ctypes.c_int,
+                                               ctypes.c_void_p]),
     "opq_quantize_grouped": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_float,
                                             ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -416,4 +421,33 @@ def linear(x: torch.Tensor, qw, alpha: float, bias: Optional[torch.Tensor] = Non
                            m, n, k, alpha, _ptr(out), y_dtype, _ptr(workspace), ws_bytes,
                            _stream(x.device))
     _check("opq_linear", st)
+    return out
+
+
+def linear_noalloc(x: torch.Tensor, bw: "BitsWeight", alpha: float,
+                   bias: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                   out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """opq_linear_bits_noalloc: the b-bit linear layer with the library's fixed
+    per-GPU scratch instead of a workspace (no device allocation in the call
+    when `out` is given)."""
+    _need_cuda("x", x, torch.bfloat16, 2)
+    m, k = x.shape
+    n, kw = bw.shape
+    if kw != k:
+        raise ValueError(f"x has k={k}, weight has k={kw}")
+    _check_bits(bw, n, k)
+    if bias is not None:
+        _need_cuda("bias", bias, torch.float32, 1)
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=x.device)
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"out must be float32 or bfloat16, got {out.dtype}")
+    _need_cuda("out", out, out.dtype, 2)
+    if tuple(out.shape) != (m, n):
+        raise ValueError(f"out must have shape {(m, n)}, got {tuple(out.shape)}")
+    y_dtype = OPQ_F32 if out.dtype == torch.float32 else OPQ_BF16
+    st = load().opq_linear_bits_noalloc(_ptr(x), _ptr(bw.packed), _ptr(bw.sign), _ptr(bw.scale),
+                                        _ptr(bias), m, n, k, bw.bits, alpha, _ptr(out), y_dtype,
+                                        _stream(x.device))
+    _check("opq_linear_bits_noalloc", st)
     return out
