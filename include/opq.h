@@ -163,12 +163,12 @@ size_t opq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *   y       device out, [m][n] of float32 (y_dtype OPQ_F32) or bfloat16
  *           (OPQ_BF16: the float32 result rounded to nearest even)
  *   workspace, workspace_bytes  device scratch of at least
- *           opq_linear_workspace_bytes(m, n, k) bytes (NULL when that is 0).
- *           It must be zero-filled before its first use.  A call puts back
- *           to zero, before its work ends, every part that has to start at
- *           zero, so one buffer serves any number of calls (of any shape) in
- *           one stream.  Calls that may run at the same time (other streams)
- *           need buffers of their own.
+ *           opq_linear_workspace_bytes(m, n, k) bytes (NULL when that is 0);
+ *           the present kernels use none.  A future shape that does will
+ *           need no initialisation of it and will overwrite it, so one buffer
+ *           serves any number of calls (of any shape) in one stream; calls
+ *           that may run at the same time (other streams) need buffers of
+ *           their own.
  * The sum order is fixed for a given shape, so results are reproducible bit
  * for bit.  k <= 65536 and n <= 2^26 (OPQ_ERR_UNSUPPORTED otherwise).
  * Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN,
@@ -225,7 +225,7 @@ int opq_error_sums_bits(const void* w, int w_dtype, int64_t n, int64_t k, int bi
 
 /*
  * Bytes of device workspace opq_linear_bits needs: for bits = 4 those of
- * opq_linear_workspace_bytes (0), otherwise room for W' as bfloat16, n * k * 2
+ * opq_linear_workspace_bytes, otherwise room for W' as bfloat16, n * k * 2
  * bytes rounded up to 256 (0 for an empty shape).
  */
 size_t opq_linear_bits_workspace_bytes(int64_t m, int64_t n, int64_t k, int bits);
@@ -255,15 +255,16 @@ int opq_linear_bits(const uint16_t* x, const uint32_t* packed, const uint32_t* s
 /*
  * opq_linear_bits without a workspace argument, for callers that cannot
  * allocate device memory: code under HIP graph capture, tight serving loops,
- * harnesses that forbid hipMalloc.  W' goes into a fixed array that the library
- * holds on every GPU it runs on (160 MiB, kept until the process ends); shapes
- * needing more (n * k * 2 bytes above 160 MiB) return OPQ_ERR_UNSUPPORTED.
- * Every call on one GPU uses that same array, so calls that may overlap on one
- * GPU (other streams or threads) race; calls in one stream follow each other.
- * No part of the array needs to start at zero.  bits = 4 is opq_linear, which
- * needs no scratch.  The call allocates nothing (no hipMalloc, no allocator of
- * any library).  Other arguments and errors as for opq_linear_bits, plus
- * OPQ_ERR_HIP when the runtime cannot report the array's address.
+ * harnesses that forbid hipMalloc.  The workspace opq_linear_bits would take
+ * (W' as bfloat16 for 3, 5 and 6 bits; none for 4 bits) is a fixed array that
+ * the library holds on every GPU it runs on (160 MiB, kept until the process
+ * ends); shapes whose opq_linear_bits_workspace_bytes exceeds 160 MiB return
+ * OPQ_ERR_UNSUPPORTED.  Every call on one GPU uses that same array, so calls
+ * that may overlap on one GPU (other streams or threads) race; calls in one
+ * stream follow each other.  No part of the array needs to start at zero.
+ * The call allocates nothing (no hipMalloc, no allocator of any library).
+ * Other arguments and errors as for opq_linear_bits, plus OPQ_ERR_HIP when the
+ * runtime cannot report the array's address.
  */
 int opq_linear_bits_noalloc(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                             const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
@@ -313,10 +314,11 @@ int opq_dequantize_grouped(const uint32_t* packed, const uint32_t* sign, const u
 /*
  * The linear layer on the group-wise form: y = x W'^T (+ bias) with W' the
  * reconstruction opq_dequantize_grouped writes, made on chip; otherwise as
- * opq_linear (workspace sized by opq_linear_workspace_bytes, reproducible sum
- * order, k <= 65536, n <= 2^26).  Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA,
- * OPQ_ERR_ALIGN, OPQ_ERR_DTYPE, OPQ_ERR_WORKSPACE, OPQ_ERR_UNSUPPORTED,
- * OPQ_ERR_HIP.
+ * opq_linear (reproducible sum order, k <= 65536, n <= 2^26).  The group-wise
+ * kernels use no workspace: workspace may be NULL (or any 16-byte aligned
+ * pointer) and workspace_bytes any value.  Errors: OPQ_ERR_NULL,
+ * OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN, OPQ_ERR_DTYPE,
+ * OPQ_ERR_UNSUPPORTED, OPQ_ERR_HIP.
  */
 int opq_linear_grouped(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                        const uint16_t* scale16, const float* bias, int64_t m, int64_t n,

@@ -276,7 +276,8 @@ def test_linear_workspace_sizes(lib):
     # every shape is reduced inside its blocks: no workspace
     ws = lib.opq_linear_workspace_bytes
     for m, n, k in [(1, 3840, 3840), (32, 3840, 3840), (64, 3840, 10240), (65, 3840, 3840),
-                    (4096, 11520, 3840), (0, 3840, 3840), (32, 0, 3840), (-1, 3840, 3840)]:
+                    (4096, 11520, 3840), (0, 3840, 3840), (32, 0, 3840), (-1, 3840, 3840),
+                    (32, 3840, 65536 + 32), (32, 3840, 100)]:
         assert ws(m, n, k) == 0
 
 

@@ -127,7 +127,7 @@ int opq_dequantize(const uint32_t* packed, const uint32_t* sign, const float* sc
 }
 
 size_t opq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
-  if (m < 0 || n < 0 || k < 0) return 0;
+  if (m < 0 || !shape_ok(n, k) || k > kMaxK || n > kMaxLinearN) return 0;
   return opq::linear_workspace_bytes(m, n, k);
 }
 
@@ -143,7 +143,7 @@ int opq_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign, 
       !aligned16(y) || (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)))
     return OPQ_ERR_ALIGN;
   if (y_dtype != OPQ_F32 && y_dtype != OPQ_BF16) return OPQ_ERR_DTYPE;
-  const size_t need = opq::linear_workspace_bytes(m, n, k);
+  const size_t need = opq_linear_workspace_bytes(m, n, k);
   if (workspace_bytes < need || (need > 0 && !workspace)) return OPQ_ERR_WORKSPACE;
   if (m == 0 || n == 0) return OPQ_OK;
   if (k > kMaxK || n > kMaxLinearN) return OPQ_ERR_UNSUPPORTED;
@@ -290,14 +290,16 @@ int opq_linear_bits(const uint16_t* x, const uint32_t* packed, const uint32_t* s
 int opq_linear_bits_noalloc(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                             const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
                             int bits, float alpha, void* y, int y_dtype, void* stream) {
-  if (bits == 4)  // the on-chip decoder: no scratch at all
-    return opq_linear(x, packed, sign, scale, bias, m, n, k, alpha, y, y_dtype, nullptr, 0, stream);
-  // Arguments first, as opq_linear_bits checks them: with no workspace that
-  // call never launches, and answers OPQ_ERR_WORKSPACE once all else is valid.
+  const size_t need = opq_linear_bits_workspace_bytes(m, n, k, bits);  // 0 for invalid shapes
+  if (need == 0)  // nothing to hold; argument errors come back from the call itself
+    return opq_linear_bits(x, packed, sign, scale, bias, m, n, k, bits, alpha, y, y_dtype, nullptr,
+                           0, stream);
+  // Arguments first, as opq_linear_bits checks them: with no workspace and
+  // need > 0 that call never launches, and answers OPQ_ERR_WORKSPACE once all
+  // else is valid.
   const int st = opq_linear_bits(x, packed, sign, scale, bias, m, n, k, bits, alpha, y, y_dtype,
                                  nullptr, SIZE_MAX, nullptr);
-  if (st != OPQ_ERR_WORKSPACE) return st;  // an argument error, or an empty product
-  const size_t need = opq_linear_bits_workspace_bytes(m, n, k, bits);
+  if (st != OPQ_ERR_WORKSPACE) return st;
   if (need > opq::kNoAllocScratchBytes) return OPQ_ERR_UNSUPPORTED;
   void* ws = opq::noalloc_scratch();
   if (!ws) return OPQ_ERR_HIP;
@@ -318,9 +320,7 @@ int opq_linear_grouped(const uint16_t* x, const uint32_t* packed, const uint32_t
       !aligned16(y) || (bias && !aligned16(bias)) || (workspace && !aligned16(workspace)))
     return OPQ_ERR_ALIGN;
   if (y_dtype != OPQ_F32 && y_dtype != OPQ_BF16) return OPQ_ERR_DTYPE;
-  const size_t need = opq::linear_workspace_bytes(m, n, k);
-  if (workspace_bytes < need || (need > 0 && !workspace)) return OPQ_ERR_WORKSPACE;
-  if (m == 0 || n == 0) return OPQ_OK;
+  if (m == 0 || n == 0) return OPQ_OK;  // the group-wise kernels use no workspace
   if (k > kMaxK || n > kMaxLinearN) return OPQ_ERR_UNSUPPORTED;
   opq::DecisionPoints dp;
   if (!opq::decision_points(alpha, dp.t)) return OPQ_ERR_ALPHA;

@@ -348,14 +348,14 @@ def snr_db(weights, alpha: float, bits: int = 4) -> float:
     return float("inf") if den == 0.0 else 10.0 * float(np.log10(num / den))
 
 
-# One zero-filled workspace per device, grown on demand.  opq_linear puts the
-# parts that must start at zero back to zero, so calls in one stream can share
+# One workspace per device, grown on demand.  The linear calls overwrite what
+# they use and need nothing in it initialised, so calls in one stream can share
 # it; calls that may overlap (other streams) must pass workspaces of their own.
 _workspaces: dict = {}
 
 
 def shared_workspace(device: torch.device, nbytes: int) -> Optional[torch.Tensor]:
-    """The per-device zero-filled workspace, at least `nbytes` long (None for 0)."""
+    """The per-device workspace, at least `nbytes` long (None for 0)."""
     if nbytes <= 0:
         return None
     key = torch.device(device).index if torch.device(device).index is not None \
@@ -375,9 +375,9 @@ def linear(x: torch.Tensor, qw, alpha: float, bias: Optional[torch.Tensor] = Non
     into the workspace, then a dense bf16 product).
 
     out_dtype is torch.float32 or torch.bfloat16 (the float32 result rounded
-    to nearest even).  `workspace`, when given, must be a zero-filled uint8
-    device tensor of at least linear_workspace_bytes(m, n, k) bytes; by default
-    the per-device shared one is used.
+    to nearest even).  `workspace`, when given, must be a uint8 device tensor
+    of at least linear_workspace_bytes(m, n, k) bytes (its contents are
+    overwritten); by default the per-device shared one is used.
     """
     _need_cuda("x", x, torch.bfloat16, 2)
     m, k = x.shape
