@@ -142,6 +142,62 @@ def measured_traffic(kind, tag):
         return None
 
 
+# ------------------------------------------------------------------ streaming ceiling
+
+def ceiling_lib():
+    """libopq_ceiling.so: plain row streaming of given bytes (built with libopq)."""
+    import ctypes
+    from w4a16_linear_amd import build as B
+    if not os.path.exists(B.CEILING_LIB):
+        raise RuntimeError(f"{B.CEILING_LIB} not built: run `python -m w4a16_linear_amd.build`")
+    lib = ctypes.CDLL(B.CEILING_LIB)
+    lib.opq_ceiling_stream_rows.restype = ctypes.c_int
+    lib.opq_ceiling_stream_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+    return lib
+
+
+def row_bytes(kind, k, w_bytes, group=0, bits=4):
+    """(read, written) bytes per weight row of quantize or dequantize, each
+    rounded up to 16: the weights, the codes and signs, the row's scales."""
+    sc = 2 * (k // group) if group else 4
+    st = k * (bits + 1) // 8 + sc
+    up = lambda b: (b + 15) // 16 * 16
+    return (up(k * w_bytes), up(st)) if kind == "quantize" else (up(st), up(2 * k))
+
+
+def stream_ceiling_us(dev, stream, rows, rd, wr, reps):
+    """Microseconds per call of the streaming kernel over rows x (rd read, wr
+    written) bytes, rotating over enough buffer pairs to pass 800 MB."""
+    import numpy as np
+    import torch
+    lib = ceiling_lib()
+    per = rows * (rd + wr)
+    pairs = max(2, int(np.ceil(800e6 / max(per, 1))))
+    bufs = [(torch.empty(max(rows * rd, 16), dtype=torch.uint8, device=dev),
+             torch.empty(max(rows * wr, 16), dtype=torch.uint8, device=dev)) for _ in range(pairs)]
+    h = stream.cuda_stream
+
+    def call(i):
+        a, b = bufs[i % pairs]
+        if lib.opq_ceiling_stream_rows(a.data_ptr(), b.data_ptr(), rows, rd, wr, h) != 0:
+            raise RuntimeError("opq_ceiling_stream_rows failed")
+    for i in range(3):
+        call(i)
+    res = []
+    for b in range(7):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(reps):
+            call(b * reps + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) / reps * 1e3)
+    del bufs
+    return float(np.median(res))
+
+
 # ------------------------------------------------------------------ host description
 
 def host_description():
@@ -404,6 +460,19 @@ def main():
             del bufs
         torch.cuda.synchronize()
 
+        # The repo's own streaming kernel on the same rows and bytes: what a
+        # quantizer or dequantizer without arithmetic would take.
+        for name, rec in kern.items():
+            kind = name.split(".")[-1]
+            if kind not in ("quantize", "dequantize"):
+                continue
+            p = next(q for q in plan if q["tag"] == rec["tag"])
+            rd, wr = row_bytes(kind, p["L"].k, p["w_bytes"], group, bits)
+            c = stream_ceiling_us(dev, stream, p["L"].n, rd, wr, args.steps)
+            rec["stream_ceiling_us"] = round(c, 3)
+            rec["frac_of_stream_ceiling"] = round(c / rec["us"], 4)
+        torch.cuda.synchronize()
+
     if args.copy_mib:
         # A plain device copy of known size, for scaling the HBM byte counters.
         src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
@@ -545,6 +614,17 @@ def model_pass(args, dev):
                       "frac": round(ideal / us, 4), "GBps": round(alg / (us * 1e-6) / 1e9, 1),
                       "algorithmic_bytes": int(alg), "launches": len(shapes)}
     ideal_total = sum(v["ideal_us"] for v in kern.values())
+
+    # The streaming kernel on every layer's rows and bytes (each distinct shape
+    # timed once, counted once per layer).
+    counts = {}
+    for _, _, n, k in shapes:
+        counts[(n, k)] = counts.get((n, k), 0) + 1
+    for name in ("quantize", "dequantize"):
+        c = sum(cnt * stream_ceiling_us(dev, stream, n, *row_bytes(name, k, 2), 5)
+                for (n, k), cnt in counts.items())
+        kern[name]["stream_ceiling_us"] = round(c, 1)
+        kern[name]["frac_of_stream_ceiling"] = round(c / kern[name]["us"], 4)
 
     # SNR(alpha) - SNR(1) over the whole model (reporting only, not timed)
     def snr_db(a):

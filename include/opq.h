@@ -29,10 +29,11 @@
  *   - device pointers are memory of the current HIP device; host pointers are
  *     marked as such;
  *   - the caller owns every buffer (scratch comes in as a workspace argument);
- *     the library allocates nothing, frees nothing and synchronises nothing;
- *     its only global state is a mutex-guarded memo of the per-alpha host
- *     tables and, per kernel, a once-computed occupancy figure, so calls are
- *     reentrant and thread-safe; outputs must not overlap inputs;
+ *     no call allocates, frees or synchronises; the library's only global
+ *     state is a mutex-guarded memo of the per-alpha host tables, per kernel
+ *     a once-computed occupancy figure, and the fixed device array of
+ *     opq_linear_bits_noalloc (its address looked up once per device), so
+ *     calls are reentrant and thread-safe; outputs must not overlap inputs;
  *   - `stream` is a hipStream_t (NULL = the default stream); work is enqueued
  *     on it and the call returns at once; faults inside kernels show up at the
  *     caller's next synchronisation;

@@ -310,3 +310,22 @@ def test_host_tables_are_thread_safe():
     for t in threads:
         t.join()
     assert not bad
+
+
+def test_ceiling_library_checks_arguments():
+    """The benchmark's streaming-ceiling library loads and refuses bad
+    arguments before any launch (no GPU needed for these)."""
+    import ctypes
+    from w4a16_linear_amd import build as B
+    lib = ctypes.CDLL(B.CEILING_LIB)
+    f = lib.opq_ceiling_stream_rows
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64,
+                  ctypes.c_int64, ctypes.c_void_p]
+    assert f(FAKE, FAKE, 0, 16, 16, None) == 0           # nothing to do
+    assert f(FAKE, FAKE, 4, 24, 16, None) == 1           # not a multiple of 16
+    assert f(FAKE, FAKE, -1, 16, 16, None) == 1
+    assert f(None, FAKE, 4, 16, 16, None) == 1
+    assert f(FAKE, None, 4, 16, 16, None) == 1
+    assert f(MISALIGNED, FAKE, 4, 16, 16, None) == 1
+    assert f(FAKE, FAKE, 4, 1 << 31, 16, None) == 1

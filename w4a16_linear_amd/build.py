@@ -21,8 +21,11 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libopq.so")
+# the benchmark's streaming-ceiling kernel, a library of its own
+CEILING_LIB = os.path.join(HERE, "libopq_ceiling.so")
 
 SOURCES = ["opq_api.cpp", "tables.cpp", "quantize.hip", "dequantize.hip", "linear.hip"]
+CEILING_SOURCES = ["stream_ceiling.hip"]
 ARCH = "gfx950"
 
 
@@ -71,19 +74,26 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libopq.so; returns the library path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-lquadmath"]
+def _link(objs, lib: str, libs, verbose: bool) -> None:
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + libs
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source, link libopq.so and libopq_ceiling.so; returns the
+    path of libopq.so."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    srcs = SOURCES + CEILING_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB, ["-lquadmath"], verbose)
+    _link([objs[s] for s in CEILING_SOURCES], CEILING_LIB, [], verbose)
     return LIB
 
 

@@ -159,6 +159,19 @@ __global__ __launch_bounds__((sk_waves<NMB, GS, kPre>() * kWave)) void linear_sk
     }
   };
 
+  // The maxima the row tables are made from are requested ahead of the first
+  // k blocks.  The compiler then waits for them before the batch goes out, so
+  // only the four table waves issue their first batch a round trip late;
+  // requested after the batch, they made the table build, and the barrier
+  // after it, wait for the whole first batch (m <= 16: 7-9 % slower).
+  const bool lut_lane = GS == 0 && wave < 4 && lane < kSkRows;
+  const bool pre_lane = kPre && tid < kSkRows * ngroups;
+  float mr = 0.0f;
+  uint16_t m16_bits = 0;
+  if (lut_lane) mr = scale[min(n0 + lane, n - 1)];
+  if (pre_lane)
+    m16_bits = scale16[(int64_t)min(n0 + (tid & (kSkRows - 1)), n - 1) * ngroups + tid / kSkRows];
+
   const int nbatch = (mine + CH - 1) / CH;
 #pragma unroll
   for (int d = 0; d < D; ++d)
@@ -168,17 +181,14 @@ __global__ __launch_bounds__((sk_waves<NMB, GS, kPre>() * kWave)) void linear_sk
   // 4w .. 4w+3 of row `lane` (a wave-uniform code, so the levels stay in
   // scalar registers).
   if constexpr (GS > 0 && !kPre) build_mant_table(lv, s_mt);
-  if (kPre && tid < kSkRows * ngroups) {
+  if (pre_lane) {
     // thread t: the table of group t / 16 of row n0 + t % 16 (all sixteen
     // entries, each with a compile-time level index)
-    const float m16 = f16_value(scale16[(int64_t)min(n0 + (tid & (kSkRows - 1)), n - 1) * ngroups +
-                                        tid / kSkRows]);
-    const RowLut t = make_row_lut(lv, m16);
+    const RowLut t = make_row_lut(lv, f16_value(m16_bits));
     *reinterpret_cast<u32x4_t*>(&s_glut[8 * tid]) = u32x4_t{t.lo[0], t.lo[1], t.lo[2], t.lo[3]};
     *reinterpret_cast<u32x4_t*>(&s_glut[8 * tid + 4]) = u32x4_t{t.hi[0], t.hi[1], t.hi[2], t.hi[3]};
   }
-  if (GS == 0 && wave < 4 && lane < kSkRows) {
-    const float mr = scale[min(n0 + lane, n - 1)];
+  if (lut_lane) {
     uint32_t lo = 0u, hi = 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
