@@ -90,4 +90,38 @@ __device__ __forceinline__ void decode_word_ordered(uint32_t w, uint32_t sb, con
   out[3] = __builtin_amdgcn_perm(o57, e46, 0x07060302u);
 }
 
+// The same eight values (k order) with fewer instructions, for the linear
+// layers, where a sign on code 0 makes no difference (it may give -0.0).  The
+// codes go into two selector words as (c0, c1, c4, c5) and (c2, c3, c6, c7):
+// then the bit-3 masks come straight from shifted copies of the word, and
+// the bf16 pairs come out in k order with one permute each.  The sign bits
+// of each group move to the top of its bytes with one 24-bit multiply:
+// bits (0, 1, 4, 5) of sb placed at 5, 6, 9, 10 and multiplied by
+// 2^2 + 2^9 + 2^14 + 2^21 land on 7, 15, 23, 31 (the other partial products
+// fall elsewhere, and their one carry stops below bit 22).  ~34 VALU.
+__device__ __forceinline__ void decode_word_split(uint32_t w, uint32_t sb, const RowLut& t,
+                                                  uint32_t (&out)[4]) {
+  const uint32_t ev7 = w & 0x07070707u;         // low 3 bits of codes 0, 2, 4, 6
+  const uint32_t od7 = (w >> 4) & 0x07070707u;  // of codes 1, 3, 5, 7
+  const uint32_t a7 = __builtin_amdgcn_perm(od7, ev7, 0x06020400u);  // c0 c1 c4 c5
+  const uint32_t b7 = __builtin_amdgcn_perm(od7, ev7, 0x07030501u);  // c2 c3 c6 c7
+  // 0xFF in the bytes whose code is >= 8: its bit 3 (bit 4i + 3 of w) moved
+  // to bit 15 or 31 of one of the two sources, which selectors 8..11 repeat
+  const uint32_t ma = __builtin_amdgcn_perm(w << 8, w << 12, 0x0B090A08u);
+  const uint32_t mb = __builtin_amdgcn_perm(w, w << 4, 0x0B090A08u);
+  const uint32_t lo_a = plane4(t.lo, a7, ma), lo_b = plane4(t.lo, b7, mb);
+  uint32_t hi_a = plane4(t.hi, a7, ma), hi_b = plane4(t.hi, b7, mb);
+  // opaque: keeps each high plane one v_bfi_b32 and the sign one v_and_or_b32
+  // (left free, the combiner merges the three terms into four instructions)
+  asm volatile("" : "+v"(hi_a), "+v"(hi_b));
+  const uint32_t sa = __umul24((sb << 5) & 0x660u, 0x204204u);
+  const uint32_t sg = __umul24((sb << 3) & 0x660u, 0x204204u);
+  const uint32_t hs_a = hi_a | (sa & 0x80808080u);
+  const uint32_t hs_b = hi_b | (sg & 0x80808080u);
+  out[0] = __builtin_amdgcn_perm(hs_a, lo_a, 0x05010400u);  // (k0, k1)
+  out[1] = __builtin_amdgcn_perm(hs_b, lo_b, 0x05010400u);  // (k2, k3)
+  out[2] = __builtin_amdgcn_perm(hs_a, lo_a, 0x07030602u);  // (k4, k5)
+  out[3] = __builtin_amdgcn_perm(hs_b, lo_b, 0x07030602u);  // (k6, k7)
+}
+
 }  // namespace opq

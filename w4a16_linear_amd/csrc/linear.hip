@@ -248,7 +248,7 @@ __global__ __launch_bounds__((sk_waves<NMB, GS, kPre>() * kWave)) void linear_sk
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           uint32_t o[4];
-          decode_word_ordered<false>(words[t], sb >> (8 * t), lut, o);
+          decode_word_split(words[t], sb >> (8 * t), lut, o);
           if (!live) o[0] = o[1] = o[2] = o[3] = 0u;
           const bf16x8_t a = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
 #pragma unroll
@@ -532,7 +532,7 @@ __global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
       __attribute__((always_inline)) {
     const uint32_t words[4] = {pwv.x, pwv.y, pwv.z, pwv.w};
     uint32_t o[4];
-    decode_word_ordered<false>(words[s], swv >> (8 * s), lut, o);
+    decode_word_split(words[s], swv >> (8 * s), lut, o);
     if constexpr (kHalfTail) {
       if (kt == nsteps - 1 && h == 1) o[0] = o[1] = o[2] = o[3] = 0u;
     }
