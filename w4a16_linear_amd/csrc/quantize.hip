@@ -138,6 +138,23 @@ __device__ __forceinline__ uint32_t sign_byte(const Slot<T>& s) {
   for (int i = 7; i >= 0; --i) sb = (sb << 1) + (s.neg(i) ? 1u : 0u);
   return sb;
 }
+// bfloat16 pairs, four instructions a pair instead of six: adding 0x7FFF to a
+// half's magnitude sets its top bit exactly when the magnitude is not zero
+// (no carry crosses into the other half), so r & that & 0x80008000 keeps the
+// sign bits of the halves with w < 0 (-0.0 gives 0); v_dot4_u32_u8 then sums
+// those bytes (0x80 or 0) with weights 2^i at element i's byte.
+template <>
+__device__ __forceinline__ uint32_t sign_byte(const Slot<uint16_t>& s) {
+  constexpr uint32_t kWeights[4] = {0x02000100u, 0x08000400u, 0x20001000u, 0x80004000u};
+  uint32_t acc = 0u;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t r = s.r[j];
+    const uint32_t nz = (r & 0x7FFF7FFFu) + 0x7FFF7FFFu;
+    acc = __builtin_amdgcn_udot4(r & nz & 0x80008000u, kWeights[j], acc, false);
+  }
+  return acc >> 7;
+}
 
 // Store one chunk's packed word and the sign word shared by four lanes.
 __device__ __forceinline__ void store_chunk(uint32_t* prow, uint32_t* srow, int c, int lane,
