@@ -352,7 +352,7 @@ __global__ __launch_bounds__((sk_waves<NMB, GS, kPre>() * kWave)) void linear_sk
 // two x stages and two weight stages.
 
 constexpr int kTM = 256, kTN = 256, kTK = 64;
-constexpr int kTVALUPerMFMA = 6;  // VALU slots after each MFMA in the forced interleave
+constexpr int kTVALUPerMFMA = 4;  // VALU slots after each MFMA in the forced interleave
 constexpr int kTThreads = 512;
 constexpr int kXStageBytes = kTM * kTK * 2;        // 32 KB
 constexpr int kWCodeBytes = kTN * 64;              // codes of a step pair, 16 KB
