@@ -12,7 +12,9 @@
 // once and long rows still give many waves.  A lane turns one packed word
 // (eight codes) and a byte of the sign plane into 16 bytes of bfloat16 per
 // chunk; each wave makes its row's table.  HBM traffic is the algorithmic
-// 0.625 B read + 2 B written per weight.
+// 0.625 B read + 2 B written per weight.  The bfloat16 output is a one-touch
+// stream and is stored nontemporal, which made this write-heavy kernel 25-35 %
+// faster; the loads stay plain (nontemporal loads slowed write-heavy streams).
 //
 // Further down: the group-wise form (one float16 max per group of weights)
 // and 3/5/6-bit codes.
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void dequantize_rows(
     if (e0 < k) {
       uint32_t o[4];
       decode_word_ordered(wv[g], sv[g] >> (8 * (lane & 3)), t, o);
-      *reinterpret_cast<uint4*>(orow + e0) = make_uint4(o[0], o[1], o[2], o[3]);
+      store_stream16(orow + e0, o[0], o[1], o[2], o[3]);
     }
   }
 }
@@ -74,9 +76,16 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void dequantize_rows(
 // to every lane of the group with ds_bpermute and cut into byte planes.  Each
 // wave takes kGUnroll chunks with all their loads in flight; the grid is one
 // wave per kGUnroll chunks.
+//
+// One word per lane, so each store instruction of a wave writes 1 KB of
+// consecutive bf16 and the stores can go nontemporal: with two words per lane
+// (32 bytes per lane, written by two 16-byte stores that each cover every
+// other 16 bytes) nontemporal stores took 49 us for a 11520 x 3840 weight in
+// groups of 128, plain ones 30 us, and this layout 22 us, although it makes a
+// table per 8 codes instead of per 16.
 constexpr int kGThreads = 256;
-constexpr int kGUnroll = 2;
-constexpr int kGWords = 2;                    // packed words per lane per chunk
+constexpr int kGUnroll = 4;
+constexpr int kGWords = 1;                    // packed words per lane per chunk
 constexpr int kGChunk = kWave * 8 * kGWords;  // elements per wave per chunk
 
 // Byte planes of the table of this lane's group: the group spans LG lanes
@@ -145,7 +154,7 @@ __global__ __launch_bounds__(kGThreads) void dequantize_grouped_rows(
       for (int j = 0; j < kGWords; ++j) {
         uint32_t o[4];
         decode_word_ordered(wv[u][j], sv[u] >> (8 * j), t, o);
-        *reinterpret_cast<uint4*>(out + e0 + 8 * j) = make_uint4(o[0], o[1], o[2], o[3]);
+        store_stream16(out + e0 + 8 * j, o[0], o[1], o[2], o[3]);
       }
     }
   }
@@ -174,7 +183,11 @@ hipError_t launch_grouped(const uint32_t* packed, const uint32_t* sign, const ui
 // copies to LDS once).  A lane decodes eight codes per 512-element chunk: its
 // 8b bits of the row's bit stream start at bit 8b (lane + 64 c), a multiple of
 // 8 below 32 within their word, so they lie in two consecutive words.
-template <int B>
+// kStream: the output is the caller's (nontemporal stores, as dequantize_rows);
+// otherwise it is W' for the dense linear kernel that runs next, and plain
+// stores leave it in cache for that kernel (nontemporal ones made the b-bit
+// linear layer 4-13 % slower).
+template <int B, bool kStream>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void dequantize_bits_rows(
     const uint32_t* __restrict__ packed, const uint32_t* __restrict__ sign,
     const float* __restrict__ scale, int64_t n, int k, int segs, LevelsN lv,
@@ -221,16 +234,30 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void dequantize_bits_rows(
         if (((sb >> (i + 1)) & 1u) && q1) v1 |= 0x8000u;
         o[i / 2] = v0 | (v1 << 16);
       }
-      *reinterpret_cast<uint4*>(orow + e0) = make_uint4(o[0], o[1], o[2], o[3]);
+      if constexpr (kStream)
+        store_stream16(orow + e0, o[0], o[1], o[2], o[3]);
+      else
+        *reinterpret_cast<uint4*>(orow + e0) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
+}
+
+template <int B>
+void launch_bits_rows(dim3 grid, dim3 block, hipStream_t stream, bool stream_out,
+                      const uint32_t* p, const uint32_t* sg, const float* sc, int64_t nr, int k,
+                      int segs, const LevelsN& lv, uint16_t* o) {
+  if (stream_out)
+    hipLaunchKernelGGL((dequantize_bits_rows<B, true>), grid, block, 0, stream, p, sg, sc, nr, k, segs, lv, o);
+  else
+    hipLaunchKernelGGL((dequantize_bits_rows<B, false>), grid, block, 0, stream, p, sg, sc, nr, k, segs, lv, o);
 }
 
 }  // namespace
 
 hipError_t launch_dequantize_bits(const uint32_t* packed, const uint32_t* sign,
                                   const float* scale, int64_t n, int64_t k, int bits,
-                                  const LevelsN& lv, uint16_t* out, hipStream_t stream) {
+                                  const LevelsN& lv, uint16_t* out, bool stream_out,
+                                  hipStream_t stream) {
   if (bits != 3 && bits != 5 && bits != 6) return hipErrorInvalidValue;
   const int64_t nch = (k + kChunk - 1) / kChunk;
   const int segs = (int)(nch > 0 ? (nch + kGroup - 1) / kGroup : 1);
@@ -244,11 +271,11 @@ hipError_t launch_dequantize_bits(const uint32_t* packed, const uint32_t* sign,
     uint16_t* o = out + r0 * k;
     const dim3 grid((unsigned)blocks), block(kRowsPerBlock * kWave);
     if (bits == 3)
-      hipLaunchKernelGGL(dequantize_bits_rows<3>, grid, block, 0, stream, p, sg, sc, nr, (int)k, segs, lv, o);
+      launch_bits_rows<3>(grid, block, stream, stream_out, p, sg, sc, nr, (int)k, segs, lv, o);
     else if (bits == 5)
-      hipLaunchKernelGGL(dequantize_bits_rows<5>, grid, block, 0, stream, p, sg, sc, nr, (int)k, segs, lv, o);
+      launch_bits_rows<5>(grid, block, stream, stream_out, p, sg, sc, nr, (int)k, segs, lv, o);
     else
-      hipLaunchKernelGGL(dequantize_bits_rows<6>, grid, block, 0, stream, p, sg, sc, nr, (int)k, segs, lv, o);
+      launch_bits_rows<6>(grid, block, stream, stream_out, p, sg, sc, nr, (int)k, segs, lv, o);
   }
   return hipGetLastError();
 }

@@ -188,7 +188,7 @@ int opq_dequantize_bits(const uint32_t* packed, const uint32_t* sign, const floa
   opq::DecisionPointsN dp;
   opq::LevelsN lv;
   if (!bits_tables(alpha, bits, dp, lv)) return OPQ_ERR_ALPHA;
-  return hip_status(opq::launch_dequantize_bits(packed, sign, scale, n, k, bits, lv, w_out,
+  return hip_status(opq::launch_dequantize_bits(packed, sign, scale, n, k, bits, lv, w_out, true,
                                                 static_cast<hipStream_t>(stream)));
 }
 
@@ -281,7 +281,9 @@ int opq_linear_bits(const uint16_t* x, const uint32_t* packed, const uint32_t* s
   const hipStream_t st = static_cast<hipStream_t>(stream);
   uint16_t* wd = static_cast<uint16_t*>(workspace);
   if (k > 0) {
-    const int e = hip_status(opq::launch_dequantize_bits(packed, sign, scale, n, k, bits, lv, wd, st));
+    // W' stays in cache for the dense product that reads it next
+    const int e =
+        hip_status(opq::launch_dequantize_bits(packed, sign, scale, n, k, bits, lv, wd, false, st));
     if (e != OPQ_OK) return e;
   }
   return hip_status(opq::launch_linear_dense(x, wd, bias, m, n, k, y, y_dtype == OPQ_BF16, st));

@@ -83,7 +83,8 @@ hipError_t launch_quantize_bits(const void* w, bool w_is_bf16, int64_t n, int64_
 // dequantize.hip
 hipError_t launch_dequantize_bits(const uint32_t* packed, const uint32_t* sign,
                                   const float* scale, int64_t n, int64_t k, int bits,
-                                  const LevelsN& lv, uint16_t* out, hipStream_t stream);
+                                  const LevelsN& lv, uint16_t* out, bool stream_out,
+                                  hipStream_t stream);  // stream_out: nontemporal stores
 
 // Group-wise form (one float16 max per `gs` weights along k).
 // quantize.hip: alpha has a bucket grid and G_1 * 2^-24 is a normal binary32

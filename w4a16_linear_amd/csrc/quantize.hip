@@ -6,7 +6,9 @@
 // A block of 256 threads owns one row at a time (one wave per row in the
 // kernels for rows of up to 2048 or more than 16384 elements).  The row is read from HBM once and held
 // in VGPRs while the max is reduced, so HBM traffic is the algorithmic 2 B
-// (bf16) read + 0.625 B written per weight.
+// (bf16) read + 0.625 B written per weight.  Both streams are one-touch and go
+// nontemporal (load_once, store_stream), except in the kernels that read a long
+// row twice, whose second pass should find the row in cache.
 //
 // The file also holds the variants of the same encoder: the error sums of the
 // alpha sweep (codes reconstructed and compared instead of stored), the
@@ -59,6 +61,11 @@ struct Slot<uint16_t> {
     const uint4 v = *reinterpret_cast<const uint4*>(p);
     r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
   }
+  // The same for data read only once (nontemporal).
+  __device__ __forceinline__ void load_once(const uint16_t* p) {
+    const u32x4_t v = load_stream16(p);
+    r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+  }
   __device__ __forceinline__ void zero() { r[0] = r[1] = r[2] = r[3] = 0u; }
   // Element i widened to binary32 (exact).
   __device__ __forceinline__ float at(int i) const {
@@ -88,6 +95,13 @@ struct Slot<float> {
     const float4 b = reinterpret_cast<const float4*>(p)[1];
     r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
     r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+  }
+  __device__ __forceinline__ void load_once(const float* p) {
+    const u32x4_t a = load_stream16(p), b = load_stream16(p + 4);
+    r[0] = __uint_as_float(a.x); r[1] = __uint_as_float(a.y);
+    r[2] = __uint_as_float(a.z); r[3] = __uint_as_float(a.w);
+    r[4] = __uint_as_float(b.x); r[5] = __uint_as_float(b.y);
+    r[6] = __uint_as_float(b.z); r[7] = __uint_as_float(b.w);
   }
   __device__ __forceinline__ void zero() {
 #pragma unroll
@@ -164,8 +178,8 @@ __device__ __forceinline__ void store_chunk(uint32_t* prow, uint32_t* srow, int 
   s32 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)s32, 0xB1, 0xF, 0xF, false);
   s32 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)s32, 0x4E, 0xF, 0xF, false);
   if (valid) {
-    prow[c * kWave + lane] = word;
-    if ((lane & 3) == 0) srow[c * (kChunk / 32) + (lane >> 2)] = s32;
+    store_stream(prow + c * kWave + lane, word);
+    if ((lane & 3) == 0) store_stream(srow + c * (kChunk / 32) + (lane >> 2), s32);
   }
 }
 
@@ -343,7 +357,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int e0 = c * kChunk + lane * 8;
-      if (e0 < k) v[c].load(wr + e0); else v[c].zero();
+      if (e0 < k) v[c].load_once(wr + e0); else v[c].zero();
     }
   };
   if constexpr (NCH > 0) {
@@ -434,7 +448,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void error_rows_table(
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int e0 = c * kChunk + lane * 8;
-      if (e0 < k) v[c].load(wr + e0); else v[c].zero();
+      if (e0 < k) v[c].load_once(wr + e0); else v[c].zero();
     }
   };
   if (row < n) load_row(row);
@@ -508,8 +522,8 @@ __device__ __forceinline__ void store_word(uint32_t* prow, uint32_t* srow, int w
   s32 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)s32, 0xB1, 0xF, 0xF, false);
   s32 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)s32, 0x4E, 0xF, 0xF, false);
   if (valid) {
-    prow[wi] = word;
-    if ((lane & 3) == 0) srow[wi >> 2] = s32;
+    store_stream(prow + wi, word);
+    if ((lane & 3) == 0) store_stream(srow + (wi >> 2), s32);
   }
 }
 
@@ -542,7 +556,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       const int e0 = c * kBlockChunk + tid * 8;
-      if (e0 < k) v[buf][c].load(wr + e0); else v[buf][c].zero();
+      if (e0 < k) v[buf][c].load_once(wr + e0); else v[buf][c].zero();
     }
   };
   int64_t row = blockIdx.x;
@@ -718,7 +732,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows(
     for (int c = 0; c < NCH; ++c) {
       const int e0 = c * kChunk + lane * 8;
       if (e0 < k) {
-        v[c].load(wr + e0);
+        v[c].load_once(wr + e0);
         mx = fmaxf(mx, slot_absmax(v[c]));
       } else {
         v[c].zero();
@@ -917,7 +931,7 @@ __global__ __launch_bounds__(kGThreads) void quantize_grouped_rows(
 #pragma unroll
     for (int u = 0; u < kGUnroll; ++u) {
       const int64_t e0 = (cb + u) * kChunk + lane * 8;
-      if (e0 < total) v[u].load(w + e0); else v[u].zero();
+      if (e0 < total) v[u].load_once(w + e0); else v[u].zero();
     }
   }
 
@@ -1110,8 +1124,8 @@ __device__ __forceinline__ void store_bits(uint32_t* prow, uint32_t* srow, int b
     const int j = lane & 3;
 #pragma unroll
     for (int w = 0; w < B; ++w)
-      if ((w & 3) == j) prow[blk * B + w] = block_word<B>(f, w);
-    if (j == 0) srow[blk] = s32;
+      if ((w & 3) == j) store_stream(prow + blk * B + w, block_word<B>(f, w));
+    if (j == 0) store_stream(srow + blk, s32);
   }
 }
 
@@ -1145,7 +1159,7 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
 #pragma unroll
     for (int c = 0; c < NCT; ++c) {
       const int e0 = c * kBlockChunk + tid * 8;
-      if (e0 < k) v[buf][c].load(wr + e0); else v[buf][c].zero();
+      if (e0 < k) v[buf][c].load_once(wr + e0); else v[buf][c].zero();
     }
   };
   int64_t row = blockIdx.x;
