@@ -423,18 +423,38 @@ def _check_layer(opq, L, alpha, with_linear):
     return assert_linear_close(y, y_ref)
 
 
-@pytest.mark.parametrize("dtype,n,k", [("bf16", 6007, 3840), ("bf16", 8200, 3840),
-                                       ("f32", 6100, 2080)])
+@pytest.mark.parametrize("dtype,n,k", [("bf16", 6007, 3840), ("bf16", 8200, 5120),
+                                       ("bf16", 8200, 3840), ("f32", 6100, 2080)])
 def test_quantize_rows_around_block_per_row_bound(gpu_lib, dtype, n, k):
     """Row counts below and above the bound up to which each row gets a block
     of its own (four times the blocks resident at once; past it blocks stride
-    over rows): codes, signs and scales at sampled rows equal the oracle's."""
+    over rows; bfloat16 rows of up to 4096 elements go one to a wave from 8192
+    rows on): codes, signs and scales at sampled rows equal the oracle's."""
     opq = gpu_lib
     w32 = WL.student_t(500 + n, (n, k))
     w_vals, w_dev = weight_tensor(w32, dtype)
     del w32
     qw = opq.quantize(w_dev, WL.ALPHA)
     rows = _sample_rows(n, 256, n + k)
+    ref_rows = O.quantize(w_vals[rows], WL.ALPHA)
+    torch.cuda.synchronize()
+    assert_quant_equal(qw, ref_rows, rows)
+
+
+@pytest.mark.parametrize("n,k", [(8191, 3008), (8192, 3008), (9000, 4096), (8192, 2080)])
+def test_quantize_bf16_rows_one_to_a_wave_bound(gpu_lib, n, k):
+    """bfloat16 rows of 2049..4096 elements go one to a wave from 8192 rows on
+    and get a block each below that: both sides of the bound, whole and ragged
+    last chunks, a zero row and a row of signed zeros among the sampled rows;
+    codes, signs and scales there equal the oracle's."""
+    opq = gpu_lib
+    w32 = WL.student_t(600 + n + k, (n, k))
+    w32[n // 2] = 0.0
+    w32[n // 3, ::2] = -0.0
+    w_vals, w_dev = weight_tensor(w32, "bf16")
+    del w32
+    qw = opq.quantize(w_dev, WL.ALPHA)
+    rows = np.union1d(_sample_rows(n, 256, n + k), [n // 3, n // 2])
     ref_rows = O.quantize(w_vals[rows], WL.ALPHA)
     torch.cuda.synchronize()
     assert_quant_equal(qw, ref_rows, rows)

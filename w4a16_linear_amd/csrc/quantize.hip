@@ -337,9 +337,10 @@ __device__ __forceinline__ uint32_t encode_chunk(const Slot<T>& v, float mx, flo
 
 // Table kernel: blocks build the table, then each wave takes one row at a time
 // (rows strided over the grid).  NCH > 0: the row (k <= NCH * 512) stays in
-// registers; this is the kernel for rows of up to 2048 elements.  NCH == 0:
-// any k, the row is streamed twice (max, then encode); it takes rows longer
-// than the block kernel's 16384.
+// registers; this is the kernel for rows of up to 2048 elements, and for
+// bfloat16 rows of up to 4096 when there are many rows (see dispatch).
+// NCH == 0: any k, the row is streamed twice (max, then encode); it takes rows
+// longer than the block kernel's 16384.
 template <typename T, int NCH>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_rows_table(
     const T* __restrict__ w, int64_t n, int k, DecisionPoints dp, BucketGrid g,
@@ -865,6 +866,8 @@ hipError_t dispatch_error(const T* w, int64_t n, int64_t k, const DecisionPoints
   return hipErrorNotSupported;
 }
 
+constexpr int64_t kWaveRowsMin = 8192;
+
 template <typename T>
 hipError_t dispatch(const T* w, int64_t n, int64_t k, const DecisionPoints& dp, uint32_t* packed,
                     uint32_t* sign, float* scale, hipStream_t stream) {
@@ -872,9 +875,15 @@ hipError_t dispatch(const T* w, int64_t n, int64_t k, const DecisionPoints& dp, 
   BucketGrid g;
   // Rows of up to 2048 elements go one to a wave (below, through the table
   // kernel): a 256-thread block would leave threads idle on them (11520 x 1024
-  // bf16: 18.2 -> 10.7 us); at k = 2560 the two measure the same, from 3840
-  // the block per row is faster.
-  if (nch > 4 && bucket_grid(dp, g)) {
+  // bf16: 18.2 -> 10.7 us).  bfloat16 rows of up to 4096 elements go one to a
+  // wave as well when there are at least kWaveRowsMin of them (two rows per
+  // resident wave of that kernel, 112 VGPRs): no block barrier or LDS exchange
+  // per row (11520 x 3840 30.3-31.1 -> 27.8 us, 20480 x 3840 50.3-52.4 ->
+  // 49.0-49.4); with fewer rows the block per row is faster (3840 x 3840
+  // 11.7-12.1 against 12.5 us), four times the lanes on each row shortening
+  // the tail.
+  const bool wave_rows = sizeof(T) == 2 && nch <= 8 && n >= kWaveRowsMin;
+  if (nch > 4 && !wave_rows && bucket_grid(dp, g)) {
     const int64_t nct = (k + kBlockChunk - 1) / kBlockChunk;
     if (nct <= 2) return launch_block_rows<T, 2>(w, n, k, dp, g, packed, sign, scale, stream);
     if (nct <= 3) return launch_block_rows<T, 3>(w, n, k, dp, g, packed, sign, scale, stream);
