@@ -100,9 +100,12 @@ def algorithmic(m, n, k, w_bytes, group=0, bits=4):
     bits/8 B and signs 1/8 B per weight."""
     sc = 2 * n * (k // group) if group else 4 * n
     st = (bits + 1) / 8.0
-    quant = {"bytes": n * k * (w_bytes + st) + sc, "flops": 0}
-    dequant = {"bytes": n * k * (st + 2) + sc, "flops": 0}
-    lin = {"bytes": st * n * k + sc + 2 * m * k + 4 * m * n, "flops": 2 * m * n * k}
+    # "read": the bytes a launch reads, which is what a cache could serve on a
+    # repeat (the kernels' outputs are nontemporal stores and do not fill it)
+    quant = {"bytes": n * k * (w_bytes + st) + sc, "flops": 0, "read": n * k * w_bytes}
+    dequant = {"bytes": n * k * (st + 2) + sc, "flops": 0, "read": n * k * st + sc}
+    lin = {"bytes": st * n * k + sc + 2 * m * k + 4 * m * n, "flops": 2 * m * n * k,
+           "read": st * n * k + sc + 2 * m * k}
     return {"quantize": quant, "dequantize": dequant, "linear": lin}
 
 
@@ -168,12 +171,14 @@ def row_bytes(kind, k, w_bytes, group=0, bits=4):
 
 def stream_ceiling_us(dev, stream, rows, rd, wr, reps):
     """Microseconds per call of the streaming kernel over rows x (rd read, wr
-    written) bytes, rotating over enough buffer pairs to pass 800 MB."""
+    written) bytes, rotating over enough buffer pairs that more than 800 MB
+    is read before a pair comes back (its stores are nontemporal and leave the
+    cache to the reads)."""
     import numpy as np
     import torch
     lib = ceiling_lib()
-    per = rows * (rd + wr)
-    pairs = max(2, int(np.ceil(800e6 / max(per, 1))))
+    per = rows * max(rd, 16)
+    pairs = max(2, int(np.ceil(800e6 / per)))
     bufs = [(torch.empty(max(rows * rd, 16), dtype=torch.uint8, device=dev),
              torch.empty(max(rows * wr, 16), dtype=torch.uint8, device=dev)) for _ in range(pairs)]
     h = stream.cuda_stream
@@ -340,9 +345,11 @@ def main():
         del w32
         x_host = WL.to_bf16(L.make_x())
         alg = algorithmic(m, n, k, w_bytes, group, bits)
-        # enough sets that every HBM-bound kernel's buffers exceed 768 MB between repeats
-        least = min(alg["quantize"]["bytes"], alg["dequantize"]["bytes"],
-                    alg["linear"]["bytes"])
+        # enough sets that every kernel reads more than 800 MB (three times the
+        # 256 MB Infinity Cache) before it sees a set again: counted in bytes
+        # read, since the nontemporal outputs do not evict the inputs
+        least = min(alg["quantize"]["read"], alg["dequantize"]["read"],
+                    alg["linear"]["read"])
         rot = args.rotate or max(2, int(np.ceil(800e6 / least)))
         sets = []
         for _ in range(rot):
@@ -449,7 +456,7 @@ def main():
             if rec["bound"] != "hbm":
                 continue
             half = rec["algorithmic_bytes"] // 2
-            pairs = max(2, int(np.ceil(800e6 / (2 * half))))
+            pairs = max(2, int(np.ceil(800e6 / half)))  # > 800 MB read between repeats
             bufs = [(torch.empty(half, dtype=torch.uint8, device=dev),
                      torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(pairs)]
 

@@ -11,10 +11,11 @@
 // the stores are nontemporal, the loads too when a row reads more than it
 // writes, and up to 8192 blocks loop over the tiles.  In a sweep over tile size
 // (8-32 KB), loads in flight (4, 8), block count (2048, 8192) and cache hints
-// this form was the fastest plain streaming kernel at the layer sizes: 0.73-0.74
-// of 8 TB/s for the quantize mix (3.2 : 1 read : write) and 0.84 for the
-// dequantize mix (1 : 3.2) on a 20480 x 3840 layer.  Nontemporal loads help the
-// read-heavy mix and slow the write-heavy one.
+// this form was the fastest plain streaming kernel tried.  With inputs rotated
+// past the 256 MB Infinity Cache it moves a 20480 x 3840 layer's bytes at 0.75
+// of 8 TB/s in the quantize mix (3.2 : 1 read : write) and 0.73 in the
+// dequantize mix (1 : 3.2); gigabyte streams reach 0.79-0.88 for reads alone and
+// 0.65-0.69 for writes alone.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
