@@ -878,8 +878,8 @@ hipError_t dispatch(const T* w, int64_t n, int64_t k, const DecisionPoints& dp, 
   // bf16: 18.2 -> 10.7 us).  bfloat16 rows of up to 4096 elements go one to a
   // wave as well when there are at least kWaveRowsMin of them (two rows per
   // resident wave of that kernel, 112 VGPRs): no block barrier or LDS exchange
-  // per row (11520 x 3840 30.3-31.1 -> 27.8 us, 20480 x 3840 50.3-52.4 ->
-  // 49.0-49.4); with fewer rows the block per row is faster (3840 x 3840
+  // per row (11520 x 3840 29.1-29.3 -> 27.3-28.9 us, 20480 x 3840 49.1-50.6
+  // -> 49.1-49.2); with fewer rows the block per row is faster (3840 x 3840
   // 11.7-12.1 against 12.5 us), four times the lanes on each row shortening
   // the tail.
   const bool wave_rows = sizeof(T) == 2 && nch <= 8 && n >= kWaveRowsMin;
