@@ -276,6 +276,38 @@ def test_linear_shapes(gpu_lib, m, n, k):
     assert_linear_close(gy.t.cpu().numpy(), y_ref)
 
 
+@pytest.mark.parametrize("m,n,k,out_dtype", [(130, 1024, 8192, torch.float32),
+                                             (96, 512, 10240, torch.bfloat16),
+                                             (257, 768, 6144, torch.float32),
+                                             (65, 256, 16384, torch.bfloat16)])
+def test_linear_mid_m_row_slices(gpu_lib, m, n, k, out_dtype):
+    """Mid-size m with few weight rows and a long k: a handful of 256-row
+    tiles would each walk all of k, so the rows go through the skinny kernel
+    in slices of up to 64 (the last one ragged).  Every output against the
+    oracle, nothing written outside y, bf16 output the float32 one rounded."""
+    opq = gpu_lib
+    w_vals, w_dev = weight_tensor(WL.student_t(800 + n + k, (n, k)), "bf16")
+    qw = quantize_guarded(opq, w_dev, 0.73)
+    ref = O.quantize(w_vals, 0.73)
+    assert_quant_equal(qw, ref)
+    d_ref = O.dequantize(*ref, 0.73)
+    xt = to_bf16(WL.normal(900 + m, (m, k)))
+    bias = torch.from_numpy(WL.normal(950 + n, (n,), 0.5)).to(DEV)
+    gy = Guarded((m, n), torch.float32)
+    opq.linear(xt.to(DEV), qw, 0.73, bias=bias, out=gy.t)
+    torch.cuda.synchronize()
+    gy.check()
+    assert_linear_close(gy.t.cpu().numpy(), O.linear(bf16_bits(xt), d_ref, bias.cpu().numpy()))
+    if out_dtype == torch.bfloat16:
+        gb = Guarded((m, n), torch.bfloat16)
+        opq.linear(xt.to(DEV), qw, 0.73, bias=bias, out=gb.t)
+        torch.cuda.synchronize()
+        gb.check()
+        b32 = gy.t.cpu().numpy().view(np.uint32).astype(np.uint64)
+        assert np.array_equal(bf16_bits(gb.t.cpu()),
+                              ((b32 + 0x7FFF + ((b32 >> 16) & 1)) >> 16).astype(np.uint16))
+
+
 @pytest.mark.parametrize("alpha", [0.03, 100.0])
 @pytest.mark.parametrize("m", [8, 300])
 def test_linear_alpha_without_bucket_grid(gpu_lib, m, alpha):

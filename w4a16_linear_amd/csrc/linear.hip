@@ -920,11 +920,47 @@ size_t linear_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
 namespace {
 
+// Mid-size m (a few 256-row tiles): the tiled kernel's grid then covers few
+// CUs while each tile still walks all of k, and slices of up to 64 x rows
+// through the skinny kernel (each slice streaming the whole weight once) can
+// finish first.  Rough costs on this part, in microseconds, fitted to
+// measurements at n = 3840..20480, k = 3840..10240, m = 65..512 (both sides
+// within ~10 % at the crossover): a k step of a grid of at most one tile per
+// CU takes ~1.25; a slice ~3 plus ~0.75 per million weights.  For example 3840 x
+// 3840 weights at m = 128 take 27 us as two slices against 76 us tiled, and
+// 20480 x 3840 at m = 65 stay tiled (76 against 82 us).  Both paths are exact
+// to the same tolerance; only the order of the k sum differs.
+bool mid_m_as_slices(int64_t m, int64_t n, int64_t k) {
+  if (m <= kSkinnyMaxM) return false;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return false;
+  const int64_t tiles = ((m + kTM - 1) / kTM) * ((n + kTN - 1) / kTN);
+  const int64_t waves = (tiles + cus - 1) / cus;
+  const double tiled_us = (double)waves * (double)((k + kTK - 1) / kTK) * 1.25;
+  const double slices = (double)((m + kSkinnyMaxM - 1) / kSkinnyMaxM);
+  const double sliced_us = slices * (3.0 + 0.75e-3 * (double)n * (double)k / 1000.0);
+  return sliced_us < tiled_us;
+}
+
 template <int GS>
 hipError_t launch_linear_any(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                              const float* scale, const uint16_t* scale16, const float* bias,
                              int64_t m, int64_t n, int64_t k, const Levels& lv, void* y,
                              bool y_bf16, hipStream_t stream) {
+  if (mid_m_as_slices(m, n, k)) {
+    const int64_t ybytes = y_bf16 ? 2 : 4;
+    for (int64_t r = 0; r < m; r += kSkinnyMaxM) {
+      const int64_t mm = m - r < kSkinnyMaxM ? m - r : kSkinnyMaxM;
+      const hipError_t e = launch_linear_any<GS>(x + r * k, packed, sign, scale, scale16, bias, mm,
+                                                 n, k, lv, static_cast<char*>(y) + r * n * ybytes,
+                                                 y_bf16, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (m <= kSkinnyMaxM) {
     const int64_t blocks = (n + kSkRows - 1) / kSkRows;
     // group tables made at block start when the block's groups fit
