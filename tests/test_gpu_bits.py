@@ -192,6 +192,15 @@ def test_linear_bits_shapes(gpu_lib, m, n, k, bits):
 
 
 @pytest.mark.parametrize("bits", BITS)
+def test_linear_bits_mid_m_row_slices(gpu_lib, bits):
+    """Mid-size m with few weight rows and a long k: the dense product runs on
+    slices of up to 64 x rows (ragged last slice), float32 and bf16 output."""
+    _linear_bits_case(gpu_lib, 130, 512, 8192, bits, 0.73, 2500 + bits, bias=True)
+    _linear_bits_case(gpu_lib, 96, 256, 10240, bits, 0.73, 2510 + bits, bias=True,
+                      out_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("bits", BITS)
 def test_linear_bits_bias_bf16_out_fp32_weights(gpu_lib, bits):
     _linear_bits_case(gpu_lib, 40, 300, 512, bits, 0.45, 2200 + bits, bias=True)
     _linear_bits_case(gpu_lib, 130, 300, 512, bits, 1.0, 2210 + bits, bias=True,

@@ -1005,6 +1005,19 @@ hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32
 
 hipError_t launch_linear_dense(const uint16_t* x, const uint16_t* wd, const float* bias, int64_t m,
                               int64_t n, int64_t k, void* y, bool y_bf16, hipStream_t stream) {
+  // mid-size m as 64-row slices when cheaper, as for the on-chip decoder (the
+  // same cost model holds: W' streams at a similar rate, mostly from the
+  // Infinity Cache after the first slice)
+  if (mid_m_as_slices(m, n, k)) {
+    const int64_t ybytes = y_bf16 ? 2 : 4;
+    for (int64_t r = 0; r < m; r += kSkinnyMaxM) {
+      const int64_t mm = m - r < kSkinnyMaxM ? m - r : kSkinnyMaxM;
+      const hipError_t e = launch_linear_dense(x + r * k, wd, bias, mm, n, k,
+                                               static_cast<char*>(y) + r * n * ybytes, y_bf16, stream);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (m <= kSkinnyMaxM) {
     const int64_t blocks = (n + kSkRows - 1) / kSkRows;
     auto kernel = m <= 16 ? linear_dense_skinny<1> : (m <= 32 ? linear_dense_skinny<2> : linear_dense_skinny<4>);
