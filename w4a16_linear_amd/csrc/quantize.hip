@@ -248,6 +248,12 @@ bool bucket_grid(const DecisionPoints& dp, BucketGrid& g) {
 // are sorted, so only point y can reach in.  For a clamped u' in the bucket,
 // d = bits(u') + x = bits(u') - bits(T_y) + kGuard fits an int32:
 //   code = y + [d >= kGuard],  decided exactly unless 0 <= d <= 2 kGuard.
+// The fast encoder takes [d >= kGuard] from the carry of the 32-bit sum
+// bits(u') + x, which is set exactly when bits(u') >= bits(T_y) - kGuard (x is
+// 2^32 - (bits(T_y) - kGuard), and bits(T_y) > 2 kGuard; never for kNoPoint):
+// the two agree everywhere outside [bits(T_y) - kGuard, bits(T_y) + kGuard],
+// and inside it d <= 2 kGuard sends the element to the exact re-encode.  One
+// add with carry-out then replaces an add and a compare.
 __device__ void build_table(const DecisionPoints& dp, BucketGrid g, uint2* tab) {
   for (int b = threadIdx.x; b < g.nb; b += blockDim.x) {
     const uint32_t lo = g.b0 + ((uint32_t)b << g.shift);
@@ -315,9 +321,10 @@ __device__ __forceinline__ uint32_t encode8_fast(const Slot<T>& s, float r, cons
     const float up = __builtin_amdgcn_fmed3f(fabsf(s.at(i)) * r, ulo, 2.0f);
     const uint32_t ub = __float_as_uint(up);
     const uint2 e = table_at(tab, ub, sh3, mask8);
-    const int d = (int)(ub + e.x);
-    word = (word << 4) + e.y + (d >= (int)kGuard ? 1u : 0u);
-    nr = min(nr, (uint32_t)d);
+    uint32_t d;
+    const uint32_t up_step = __builtin_add_overflow(ub, e.x, &d) ? 1u : 0u;
+    word = (word << 4) + e.y + up_step;
+    nr = min(nr, d);
   }
   near = nr;
   return word;
@@ -1076,9 +1083,10 @@ __device__ __forceinline__ void codes8(const Slot<T>& v, float mx, float r, bool
     const float up = __builtin_amdgcn_fmed3f(fabsf(v.at(i)) * rf, ulo, 2.0f);
     const uint32_t ub = __float_as_uint(up);
     const uint2 e = table_at(tab, ub, sh3, mask8);
-    const int d = (int)(ub + e.x);
-    q[i] = e.y + (d >= (int)kGuard ? 1u : 0u);
-    nr = min(nr, (uint32_t)d);
+    uint32_t d;
+    const uint32_t up_step = __builtin_add_overflow(ub, e.x, &d) ? 1u : 0u;  // as in encode8_fast
+    q[i] = e.y + up_step;
+    nr = min(nr, d);
   }
   if (nr <= 2u * kGuard) {
 #pragma unroll
