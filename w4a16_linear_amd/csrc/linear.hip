@@ -327,9 +327,9 @@ __global__ __launch_bounds__((sk_waves<NMB, GS, kPre>() * kWave)) void linear_sk
 // for the same blocks.
 //
 // Pipeline, one barrier per k step:
-//  * x of step kt + NXS - 1 is requested right after the barrier that ends step
-//    kt - 1 (its stage last served step kt - 1), and waited for (vmcnt) before
-//    the barrier that ends step kt + NXS - 2, which publishes it;
+//  * x of step kt + NXS - 1 is requested in step kt, after the barrier that
+//    ends step kt - 1 (its stage last served step kt - 1), and waited for
+//    (vmcnt) before the barrier that ends step kt + NXS - 2, which publishes it;
 //  * the weights of pair q are requested in step 2q + 1 - 2 NWS (their stage
 //    last served pair q - NWS) and are complete long before their first use;
 //  * the code words and the first decode of step kt + 1 are done before the
@@ -340,7 +340,7 @@ __global__ __launch_bounds__((sk_waves<NMB, GS, kPre>() * kWave)) void linear_sk
 // of the weight fragment; its x slots re-read the step's first half.
 //
 // Within a sub-step each MFMA is followed by one x fragment read of the next
-// sub-step and a share of the decode (and, in sub-step 0, of the step's
+// sub-step and a share of the decode (and, in sub-steps 1 and 2, of the step's
 // requests): the decode's VALU work then runs while the wave's own MFMAs
 // execute instead of alternating with them.  Each stage is an LDS array of its
 // own and the main loop is unrolled over the stages' common period, so every
@@ -601,11 +601,24 @@ __global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
     // (kt - 1) / 2 + NWS, into the stage of pair (kt - 1) / 2
     if constexpr (GS > 0) h_load = load_h(kt + 2);
     __builtin_amdgcn_sched_barrier(0);
-    load_x(kt + LX, xs(LX));
-    if (odd) load_w((kt - 1) / 2 + NWS, ws(-1));
+    // With three x stages the step's requests go out in sub-steps 1 (x) and
+    // 2 (weights), one after every other MFMA, rather than in a burst at the
+    // start of the step, when all eight waves leave the barrier together
+    // (about 1 % faster on all three DiT shapes; the order of the requests,
+    // and so the wait counts below, are unchanged).  With two x stages the x
+    // of step kt + 1 must land within step kt: requested at its start.
+    constexpr bool kSpread = LX == 2;
+    if constexpr (!kSpread) {
+      load_x(kt + LX, xs(LX));
+      if (odd) load_w((kt - 1) / 2 + NWS, ws(-1));
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int cur = s & 1, nxt = cur ^ 1;
+      if constexpr (kSpread) {
+        if (s == 1) load_x(kt + LX, xs(LX));
+        if (s == 2 && odd) load_w((kt - 1) / 2 + NWS, ws(-1));
+      }
 #pragma unroll
       for (int mi = 0; mi < 8; ++mi)
         acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_frag[mi], b_buf[cur], acc[mi], 0, 0, 0);
@@ -614,13 +627,15 @@ __global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
         decode_b(kt, s + 1, pw, sw, b_buf[nxt]);
         // Interleave: after each MFMA, one x fragment read of the next sub-step
         // (its register is free once that MFMA has issued), a share of the
-        // decode and (sub-step 0) of this step's load requests, so the VALU
-        // work runs while this wave's MFMAs execute.
+        // decode and one of this step's load requests (sub-steps 1 and 2, after
+        // every other MFMA; with two x stages, sub-step 0), so the VALU work
+        // runs while this wave's MFMAs execute.
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-          if (s == 0) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
+          if (kSpread ? ((s == 1 || s == 2) && (i & 1)) : s == 0)
+            __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // VMEM
           __builtin_amdgcn_sched_group_barrier(0x002, kTVALUPerMFMA, 0);  // VALU
         }
       } else {
