@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-copy", action="store_true", help="leave out the same-bytes copies")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after timing, 5 plain device copies of this many MiB (counter scaling)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay each timed step (and each per-kernel batch) as a HIP graph")
     return ap.parse_args()
 
 
@@ -169,11 +171,12 @@ def row_bytes(kind, k, w_bytes, group=0, bits=4):
     return (up(k * w_bytes), up(st)) if kind == "quantize" else (up(st), up(2 * k))
 
 
-def stream_ceiling_us(dev, stream, rows, rd, wr, reps):
+def stream_ceiling_us(dev, stream, rows, rd, wr, reps, graph=False):
     """Microseconds per call of the streaming kernel over rows x (rd read, wr
     written) bytes, rotating over enough buffer pairs that more than 800 MB
     is read before a pair comes back (its stores are nontemporal and leave the
-    cache to the reads)."""
+    cache to the reads).  graph: each batch recorded as a graph and replayed,
+    as the kernels it is compared with."""
     import numpy as np
     import torch
     lib = ceiling_lib()
@@ -181,24 +184,33 @@ def stream_ceiling_us(dev, stream, rows, rd, wr, reps):
     pairs = max(2, int(np.ceil(800e6 / per)))
     bufs = [(torch.empty(max(rows * rd, 16), dtype=torch.uint8, device=dev),
              torch.empty(max(rows * wr, 16), dtype=torch.uint8, device=dev)) for _ in range(pairs)]
-    h = stream.cuda_stream
-
     def call(i):
         a, b = bufs[i % pairs]
+        h = torch.cuda.current_stream(dev).cuda_stream  # the capture stream inside a graph
         if lib.opq_ceiling_stream_rows(a.data_ptr(), b.data_ptr(), rows, rd, wr, h) != 0:
             raise RuntimeError("opq_ceiling_stream_rows failed")
     for i in range(3):
         call(i)
     res = []
     for b in range(7):
+        g = None
+        if graph:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(reps):
+                    call(b * reps + i)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for i in range(reps):
-            call(b * reps + i)
+        if g is not None:
+            g.replay()
+        else:
+            for i in range(reps):
+                call(b * reps + i)
         e1.record(stream)
         torch.cuda.synchronize()
         res.append(e0.elapsed_time(e1) / reps * 1e3)
+        del g
     del bufs
     return float(np.median(res))
 
@@ -398,6 +410,20 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
+    def capture(fn):
+        """fn() recorded as a HIP graph (the library enqueues kernels only)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        return g
+
+    # --graph: each timed step recorded once, before the timed region, as a
+    # graph of its kernels on its own buffer set; the timed region replays them.
+    graphs = None
+    if args.graph:
+        graphs = [capture(lambda i=i: step(args.warmup + i)) for i in range(args.steps)]
+        torch.cuda.synchronize()
+
     # Timed region: exactly K steps, events only at its two ends.
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -405,24 +431,34 @@ def main():
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(args.warmup + i)
+        if graphs:
+            graphs[i].replay()
+        else:
+            step(args.warmup + i)
     stop.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(stop) / args.steps
+    del graphs
 
     def timed(fn, reps):
-        """Median over 7 batches of `reps` back-to-back calls, microseconds per call."""
+        """Median over 7 batches of `reps` back-to-back calls, microseconds per call
+        (--graph: each batch recorded as one graph and replayed)."""
         per = []
         for b in range(7):
+            g = capture(lambda b=b: [fn(b * reps + i) for i in range(reps)]) if args.graph else None
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for i in range(reps):
-                fn(b * reps + i)
+            if g is not None:
+                g.replay()
+            else:
+                for i in range(reps):
+                    fn(b * reps + i)
             e1.record(stream)
             torch.cuda.synchronize()
             per.append(e0.elapsed_time(e1) / reps * 1e3)
+            del g
         return float(np.median(per))
 
     # Per-kernel duration: batches of K back-to-back launches of one kernel
@@ -475,7 +511,7 @@ def main():
                 continue
             p = next(q for q in plan if q["tag"] == rec["tag"])
             rd, wr = row_bytes(kind, p["L"].k, p["w_bytes"], group, bits)
-            c = stream_ceiling_us(dev, stream, p["L"].n, rd, wr, args.steps)
+            c = stream_ceiling_us(dev, stream, p["L"].n, rd, wr, args.steps, args.graph)
             rec["stream_ceiling_us"] = round(c, 3)
             rec["frac_of_stream_ceiling"] = round(c / rec["us"], 4)
         torch.cuda.synchronize()
@@ -525,7 +561,8 @@ def main():
                    "layers": shapes, "alpha": alpha,
                    "scales": (f"float16 per group of {group}" if group else "float32 per row"),
                    "bits": bits,
-                   "step": "per layer: quantize -> dequantize -> linear"},
+                   "step": "per layer: quantize -> dequantize -> linear",
+                   "launch": "one HIP graph per step" if args.graph else "stream launches"},
         "roofline": roof,
         "kernels": kern,
         "kernels_sum_us": round(sum(kk["us"] for kk in kern.values()), 3),
