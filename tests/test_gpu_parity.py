@@ -163,11 +163,12 @@ def test_quantize_fp32_shapes(gpu_lib, n, k):
     full_roundtrip(gpu_lib, w_vals, w_dev, 0.73)
 
 
-@pytest.mark.parametrize("dtype,n,k", [("bf16", 9001, 96), ("f32", 8500, 544), ("bf16", 8200, 2048)])
+@pytest.mark.parametrize("dtype,n,k", [("bf16", 9001, 96), ("f32", 8500, 544), ("bf16", 33000, 96),
+                                       ("f32", 33000, 544), ("bf16", 33000, 2048)])
 def test_quantize_short_rows_past_one_grid(gpu_lib, dtype, n, k):
-    """Rows of up to 2048 elements go one to a wave, on a grid of at most 8192
+    """Rows of up to 2048 elements go one to a wave, on a grid of at most 32768
     waves: more rows than that make waves take a second row (its loads issued
-    after the first row's stores)."""
+    after the first row's stores).  9001 and 8500 rows: one row per wave."""
     w = WL.student_t(400 + n, (n, k))
     w[n // 2] = 0.0
     w_vals, w_dev = weight_tensor(w, dtype)

@@ -189,7 +189,12 @@ constexpr uint32_t kGuard = 16;             // ulps around a decision point deci
 constexpr int kMaxBuckets = 1024;           // 8-byte entries
 constexpr uint32_t kNoPoint = 0x7F000000u;  // above every clamped bits(u')
 constexpr uint32_t kTop = 0x40000000u;      // bits(2.0f): u' is clamped to [floor, 2]
-constexpr int kMaxBlocks = 2048;            // grid of the table kernel (rows are strided)
+constexpr int kMaxBlocks = 2048;            // grid of the error-sum table kernel (rows are strided)
+// Grid of the code table kernel: a row to a wave up to 32768 rows, strided
+// beyond.  Measured against a cap of 2048 blocks (8192 waves, some taking two
+// rows and some one) on bf16 rows of 3840, same box, interleaved: 11520 rows
+// 26.3 -> 25.8 us, 20480 rows 41.3 -> 39.5 us.
+constexpr int kMaxRowBlocks = 8192;
 
 // Buckets b = 0 .. nb-1 cover bit patterns [b0 + (b << shift), b0 + ((b + 1) << shift));
 // the last one reaches past bits(2.0f).  b0 is a multiple of 2^shift, and the
@@ -785,7 +790,7 @@ hipError_t launch_rows(const T* w, int64_t n, int64_t k, const DecisionPoints& d
   const int64_t groups = (n + kRowsPerBlock - 1) / kRowsPerBlock;
   BucketGrid g;
   if (bucket_grid(dp, g)) {
-    const int64_t blocks = groups < kMaxBlocks ? groups : kMaxBlocks;
+    const int64_t blocks = groups < kMaxRowBlocks ? groups : kMaxRowBlocks;
     hipLaunchKernelGGL((quantize_rows_table<T, NCH>), dim3((unsigned)blocks),
                        dim3(kRowsPerBlock * kWave), 0, stream, w, n, (int)k, dp, g, packed, sign,
                        scale);
@@ -883,12 +888,12 @@ hipError_t dispatch(const T* w, int64_t n, int64_t k, const DecisionPoints& dp, 
   // Rows of up to 2048 elements go one to a wave (below, through the table
   // kernel): a 256-thread block would leave threads idle on them (11520 x 1024
   // bf16: 18.2 -> 10.7 us).  bfloat16 rows of up to 4096 elements go one to a
-  // wave as well when there are at least kWaveRowsMin of them (two rows per
-  // resident wave of that kernel, 112 VGPRs): no block barrier or LDS exchange
-  // per row (11520 x 3840 29.1-29.3 -> 27.3-28.9 us, 20480 x 3840 49.1-50.6
-  // -> 49.1-49.2); with fewer rows the block per row is faster (3840 x 3840
-  // 11.7-12.1 against 12.5 us), four times the lanes on each row shortening
-  // the tail.
+  // wave as well when there are at least kWaveRowsMin of them (at least two
+  // rows per resident wave of that kernel, 112 VGPRs): no block barrier or LDS
+  // exchange per row (11520 x 3840 29.1-29.3 -> 27.3-28.9 us, 20480 x 3840
+  // 49.1-50.6 -> 49.1-49.2); with fewer rows the block per row is faster
+  // (3840 x 3840 11.7-12.1 against 12.5 us), four times the lanes on each row
+  // shortening the tail.
   const bool wave_rows = sizeof(T) == 2 && nch <= 8 && n >= kWaveRowsMin;
   if (nch > 4 && !wave_rows && bucket_grid(dp, g)) {
     const int64_t nct = (k + kBlockChunk - 1) / kBlockChunk;
