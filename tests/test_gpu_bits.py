@@ -69,11 +69,12 @@ def test_bits_fp32_and_special_rows(gpu_lib, bits):
 
 @pytest.mark.parametrize("bits", BITS)
 @pytest.mark.parametrize("alpha", [0.45, 0.73, 1.0])
-def test_bits_near_decision_points(gpu_lib, bits, alpha):
-    """Magnitudes within a few binary32 ulps of every row boundary."""
+@pytest.mark.parametrize("k", [8192, 2048])
+def test_bits_near_decision_points(gpu_lib, bits, alpha, k):
+    """Magnitudes within a few binary32 ulps of every row boundary (k = 2048:
+    a row to a wave; 8192: a row to a block)."""
     L = (1 << bits) - 1
     t = O.decision_thresholds_f32(alpha, L)
-    k = 8192
     rows = []
     for m in (np.float32(0.0371), np.float32(1.0)):
         vals = []
@@ -117,6 +118,16 @@ def test_bits_many_rows_against_sampled_oracle(gpu_lib, bits):
     sums = opq.error_sums(w_dev, 0.73, bits=bits).cpu().numpy()
     ref = O.error_sums_bits(w_vals[rows], 0.73, bits)
     assert np.allclose(sums[rows], ref, rtol=1e-5, atol=0)
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_bits_short_rows_past_one_grid(gpu_lib, bits):
+    """33000 rows of 96: a row to a wave on a grid of at most 32768 waves, so
+    some waves take a second row; every row against the oracle."""
+    w = WL.student_t(1760 + bits, (33000, 96))
+    w[100] = 0.0
+    w_vals, w_dev = weight_tensor(w, "bf16")
+    bits_roundtrip(gpu_lib, w_vals, w_dev, 0.73, bits)
 
 
 @pytest.mark.parametrize("bits", BITS)
