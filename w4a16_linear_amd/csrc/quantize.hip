@@ -347,6 +347,34 @@ __device__ __forceinline__ uint32_t encode_chunk(const Slot<T>& v, float mx, flo
   return word;
 }
 
+// Codes of a lane's eight elements (fast path, then exact where flagged).
+template <typename T>
+__device__ __forceinline__ void codes8(const Slot<T>& v, float mx, float r, bool fast,
+                                       const uint2* tab, int sh3, uint32_t mask8, float ulo,
+                                       const float* pts, uint32_t (&q)[8]) {
+  // As encode_chunk: the fast path runs everywhere, the exact one where flagged.
+  const float rf = fast ? r : 1.0f;
+  uint32_t nr = fast ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float up = __builtin_amdgcn_fmed3f(fabsf(v.at(i)) * rf, ulo, 2.0f);
+    const uint32_t ub = __float_as_uint(up);
+    const uint2 e = table_at(tab, ub, sh3, mask8);
+    uint32_t d;
+    const uint32_t up_step = __builtin_add_overflow(ub, e.x, &d) ? 1u : 0u;  // as in encode8_fast
+    q[i] = e.y + up_step;
+    nr = min(nr, d);
+  }
+  if (nr <= 2u * kGuard) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x = v.at(i);
+      asm volatile("" : "+v"(x));
+      q[i] = code_exact(fabsf(x), mx, tab, sh3, mask8, ulo, pts);
+    }
+  }
+}
+
 // Table kernel: blocks build the table, then each wave takes one row at a time
 // (rows strided over the grid).  NCH > 0: the row (k <= NCH * 512) stays in
 // registers; this is the kernel for rows of up to 2048 elements, and for
@@ -489,12 +517,14 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void error_rows_table(
     float sw2 = 0.0f, se2 = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
-      const uint32_t word = encode_chunk(v[c], mx, r, fast, s_tab, sh3, mask8, ulo, s_pts);
+      // the codes themselves (no packed word to take apart again)
+      uint32_t q[8];
+      codes8(v[c], mx, r, fast, s_tab, sh3, mask8, ulo, s_pts, q);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float xv = v[c].at(i);
         // a nonzero code carries the weight's sign, so |w - w'| = ||w| - L[q]|
-        const float e = fabsf(xv) - __uint_as_float(s_recw[wave][(word >> (4 * i)) & 15u] << 16);
+        const float e = fabsf(xv) - __uint_as_float(s_recw[wave][q[i]] << 16);
         sw2 = fmaf(xv, xv, sw2);
         se2 = fmaf(e, e, se2);
       }
@@ -634,12 +664,14 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_block_rows(
       float sw2 = 0.0f, se2 = 0.0f;
 #pragma unroll
       for (int c = 0; c < NCT; ++c) {
-        const uint32_t word = encode_chunk(v[buf][c], mx, r, fast, s_tab, sh3, mask8, ulo, s_pts);
+        // the codes themselves (no packed word to take apart again)
+        uint32_t q[8];
+        codes8(v[buf][c], mx, r, fast, s_tab, sh3, mask8, ulo, s_pts, q);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float xv = v[buf][c].at(i);  // zero past k
           // a nonzero code carries the weight's sign, so |w - w'| = ||w| - L[q]|
-          const float e = fabsf(xv) - __uint_as_float(s_recw[wave][(word >> (4 * i)) & 15u] << 16);
+          const float e = fabsf(xv) - __uint_as_float(s_recw[wave][q[i]] << 16);
           sw2 = fmaf(xv, xv, sw2);
           se2 = fmaf(e, e, se2);
         }
@@ -1072,34 +1104,6 @@ __device__ void build_table_n(const float* pts, int L, BucketGrid g, uint2* tab)
     }
     const uint32_t x = (next != kNoPoint && next - kGuard < hi) ? kGuard - next : kGuard - kNoPoint;
     tab[((g.b0 >> g.shift) + (uint32_t)b) & (uint32_t)(g.size - 1)] = make_uint2(x, below);
-  }
-}
-
-// Codes of a lane's eight elements (fast path, then exact where flagged).
-template <typename T>
-__device__ __forceinline__ void codes8(const Slot<T>& v, float mx, float r, bool fast,
-                                       const uint2* tab, int sh3, uint32_t mask8, float ulo,
-                                       const float* pts, uint32_t (&q)[8]) {
-  // As encode_chunk: the fast path runs everywhere, the exact one where flagged.
-  const float rf = fast ? r : 1.0f;
-  uint32_t nr = fast ? 0xFFFFFFFFu : 0u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float up = __builtin_amdgcn_fmed3f(fabsf(v.at(i)) * rf, ulo, 2.0f);
-    const uint32_t ub = __float_as_uint(up);
-    const uint2 e = table_at(tab, ub, sh3, mask8);
-    uint32_t d;
-    const uint32_t up_step = __builtin_add_overflow(ub, e.x, &d) ? 1u : 0u;  // as in encode8_fast
-    q[i] = e.y + up_step;
-    nr = min(nr, d);
-  }
-  if (nr <= 2u * kGuard) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float x = v.at(i);
-      asm volatile("" : "+v"(x));
-      q[i] = code_exact(fabsf(x), mx, tab, sh3, mask8, ulo, pts);
-    }
   }
 }
 
