@@ -341,8 +341,8 @@ __global__ __launch_bounds__((sk_waves<NMB, GS, kPre>() * kWave)) void linear_sk
 //
 // Within a sub-step each MFMA is followed by one x fragment read of the next
 // sub-step and a share of the decode (and, in sub-steps 1 and 2, of the step's
-// requests): the decode's VALU work then runs while the wave's own MFMAs
-// execute instead of alternating with them.  Each stage is an LDS array of its
+// requests; in sub-step 0 with two x stages): the decode's VALU work then runs
+// while the wave's own MFMAs execute instead of alternating with them.  Each stage is an LDS array of its
 // own and the main loop is unrolled over the stages' common period, so every
 // access names its stage at compile time; the compiler then tells a read of one
 // stage from the loads in flight to another and inserts no wait for them.  The

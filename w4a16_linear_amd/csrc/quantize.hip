@@ -1291,12 +1291,11 @@ __global__ __launch_bounds__(kBlockThreads) void quantize_bits_rows(
 
 // The codes of a row to a wave, as quantize_rows_table for four bits (rows of
 // up to 2048 elements): the row (k <= NCH * 512) in the wave's registers, its
-// max reduced across the wave
-// with no block barrier, rows strided over at most kMaxRowBlocks blocks.  A
-// lane holds elements c * 512 + 8 lane .. + 7 of chunk c, so the lanes of a
-// quad hold 32 consecutive codes and store_bits packs them as the block
-// kernel does.  The decision points and the bucket table are built in LDS once
-// per block.
+// max reduced across the wave with no block barrier, rows strided over at
+// most kMaxRowBlocks blocks.  A lane holds elements c * 512 + 8 lane .. + 7 of
+// chunk c, so the lanes of a quad hold 32 consecutive codes and store_bits
+// packs them as the block kernel does.  The decision points and the bucket
+// table are built in LDS once per block.
 template <typename T, int NCH, int B>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void quantize_bits_rows_table(
     const T* __restrict__ w, int64_t n, int k, DecisionPointsN dp, BucketGrid g,
