@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define OPQ_ABI_VERSION 5
+#define OPQ_ABI_VERSION 6
 
 typedef enum {
   OPQ_OK = 0,
@@ -147,9 +147,12 @@ int opq_dequantize(const uint32_t* packed, const uint32_t* sign, const float* sc
 
 /*
  * Bytes of device workspace opq_linear needs for this shape (0 means none;
- * the workspace pointer may then be NULL).  The present kernels reduce every
- * sum inside one block and return 0 for every shape; callers that size the
- * workspace with this function keep working if a shape ever needs one.
+ * the workspace pointer may then be NULL).  Nonzero only where the tiled
+ * layer splits k: m > 128 with k a multiple of 64, whose 256 x 256 output
+ * tiles would cover at most a quarter of the 256 CUs (for example m = 1024,
+ * n = 3840), and which the call does not run as 64-row slices of x.  It then keeps S
+ * float32 partial sums per output: S * m * n * 4 bytes rounded up to 256, at
+ * most 128 MiB, S chosen from the shape alone.  0 for every other shape.
  */
 size_t opq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
 
@@ -164,12 +167,12 @@ size_t opq_linear_workspace_bytes(int64_t m, int64_t n, int64_t k);
  *   y       device out, [m][n] of float32 (y_dtype OPQ_F32) or bfloat16
  *           (OPQ_BF16: the float32 result rounded to nearest even)
  *   workspace, workspace_bytes  device scratch of at least
- *           opq_linear_workspace_bytes(m, n, k) bytes (NULL when that is 0);
- *           the present kernels use none.  A future shape that does will
- *           need no initialisation of it and will overwrite it, so one buffer
- *           serves any number of calls (of any shape) in one stream; calls
- *           that may run at the same time (other streams) need buffers of
- *           their own.
+ *           opq_linear_workspace_bytes(m, n, k) bytes (NULL when that is 0):
+ *           the split-k partial sums, added in slice order by a second kernel
+ *           on the same stream.  It needs no initialisation and is
+ *           overwritten, so one buffer serves any number of calls (of any
+ *           shape) in one stream; calls that may run at the same time (other
+ *           streams) need buffers of their own.
  * The sum order is fixed for a given shape, so results are reproducible bit
  * for bit.  k <= 65536 and n <= 2^26 (OPQ_ERR_UNSUPPORTED otherwise).
  * Errors: OPQ_ERR_NULL, OPQ_ERR_SHAPE, OPQ_ERR_ALPHA, OPQ_ERR_ALIGN,

@@ -40,7 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_text(lib):
-    assert lib.opq_abi_version() == opq.ABI_VERSION == 5
+    assert lib.opq_abi_version() == opq.ABI_VERSION == 6
     for s in range(9):
         assert opq.status_str(s) and opq.status_str(s) != "unknown status"
     assert opq.status_str(99) == "unknown status"
@@ -273,12 +273,33 @@ def test_grouped_argument_checks(lib):
 
 
 def test_linear_workspace_sizes(lib):
-    # every shape is reduced inside its blocks: no workspace
+    """Only the split-k tiled layer keeps partial sums: few 256 x 256 tiles
+    with k a multiple of 64.  Skinny, large-m, invalid and empty shapes need
+    none."""
     ws = lib.opq_linear_workspace_bytes
-    for m, n, k in [(1, 3840, 3840), (32, 3840, 3840), (64, 3840, 10240), (65, 3840, 3840),
-                    (4096, 11520, 3840), (0, 3840, 3840), (32, 0, 3840), (-1, 3840, 3840),
-                    (32, 3840, 65536 + 32), (32, 3840, 100)]:
-        assert ws(m, n, k) == 0
+    for m, n, k in [(1, 3840, 3840), (32, 3840, 3840), (64, 3840, 10240), (4096, 11520, 3840),
+                    (4096, 20480, 3840), (4096, 3840, 10240), (0, 3840, 3840), (32, 0, 3840),
+                    (-1, 3840, 3840), (32, 3840, 65536 + 32), (32, 3840, 100),
+                    (1024, 3840, 3840 + 32), (200, 300, 544), (65, 3840, 3840), (128, 3840, 3840),
+                    (2048, 3840, 3840)]:
+        assert ws(m, n, k) == 0, (m, n, k)
+    for m, n, k in [(1024, 3840, 3840), (256, 3840, 3840), (512, 1024, 8192), (130, 1024, 8192)]:
+        b = ws(m, n, k)
+        assert b % 256 == 0 and 2 * m * n * 4 <= b <= 128 << 20, (m, n, k, b)
+    # 60 tiles: 4 slices of 16, 16, 16 and 12 k steps
+    assert ws(1024, 3840, 3840) == 4 * 1024 * 3840 * 4
+
+
+def test_linear_workspace_checked(lib):
+    f = lib.opq_linear
+    need = lib.opq_linear_workspace_bytes(1024, 3840, 3840)
+
+    def call(ws, wsb):
+        return f(FAKE, FAKE, FAKE, FAKE, None, 1024, 3840, 3840, 0.73, FAKE, 0, ws, wsb, None)
+
+    assert call(None, 0) == WORKSPACE
+    assert call(FAKE, need - 1) == WORKSPACE
+    assert call(None, need) == WORKSPACE
 
 
 def test_binding_refuses_host_tensors():

@@ -363,6 +363,43 @@ def test_linear_skinny_long_k(gpu_lib, m, n, k):
     assert_linear_close(gy.t.cpu().numpy(), y_ref)
 
 
+@pytest.mark.parametrize("m,n,k", [(300, 3840, 3840), (1024, 3840, 3840), (2048, 1000, 4096),
+                                   (700, 256, 10240), (200, 3840, 3840), (130, 1024, 8192)])
+def test_linear_split_k_tiles(gpu_lib, m, n, k):
+    """The tiled layer with k split over slices (few 256 x 256 tiles, long k):
+    every output against the oracle (with bias), bf16 output the float32 one
+    rounded, nothing written past the workspace the call asks for, and the
+    same bits twice."""
+    opq = gpu_lib
+    need = opq.linear_workspace_bytes(m, n, k)
+    assert need > 0 and need % 256 == 0
+    w_vals, w_dev = weight_tensor(WL.student_t(1900 + n + k, (n, k)), "bf16")
+    qw = opq.quantize(w_dev, 0.73)
+    ref = O.quantize(w_vals, 0.73)
+    torch.cuda.synchronize()
+    assert_quant_equal(qw, ref)
+    xt = to_bf16(WL.normal(2000 + m, (m, k)))
+    bias = WL.normal(2100 + n, (n,), 0.5)
+    bias_dev = torch.from_numpy(bias).to(DEV)
+    ws = torch.full((need + 4096,), 0xA5, dtype=torch.uint8, device=DEV)
+    gy = Guarded((m, n), torch.float32)
+    opq.linear(xt.to(DEV), qw, 0.73, bias=bias_dev, out=gy.t, workspace=ws)
+    torch.cuda.synchronize()
+    gy.check()
+    assert bool((ws[need:] == 0xA5).all()), "written past the workspace size"
+    y1 = gy.t.cpu().numpy()
+    assert_linear_close(y1, O.linear(bf16_bits(xt), O.dequantize(*ref, 0.73), bias))
+    gy2 = Guarded((m, n), torch.float32)
+    opq.linear(xt.to(DEV), qw, 0.73, bias=bias_dev, out=gy2.t, workspace=ws)
+    gb = Guarded((m, n), torch.bfloat16)
+    opq.linear(xt.to(DEV), qw, 0.73, bias=bias_dev, out=gb.t, workspace=ws)
+    torch.cuda.synchronize()
+    gy2.check()
+    gb.check()
+    assert np.array_equal(gy2.t.cpu().numpy().view(np.uint32), y1.view(np.uint32))
+    assert np.array_equal(bf16_bits(gb.t.cpu()), _bf16_rne_bits(y1))
+
+
 def _bf16_rne_bits(y32):
     b = y32.astype(np.float32).view(np.uint32).astype(np.uint64)
     return ((b + 0x7FFF + ((b >> 16) & 1)) >> 16).astype(np.uint16)

@@ -13,6 +13,7 @@
 //    rows x all of k, the waves of a block reducing in LDS (details below).
 //  * otherwise: 256x256 output tiles with v_mfma_f32_32x32x16_bf16; x staged
 //    through LDS (details below).
+#include <algorithm>
 #include <mutex>
 
 #include "decode.hpp"
@@ -404,12 +405,19 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
 
-template <bool kHalfTail, int GS>
+// kSplit: block b takes tile b % T (T tiles) and the k steps [s0, s0 +
+// slice_steps) of slice b / T (s0 = slice * slice_steps, an even step, so
+// weight pairs stay whole), and writes its float32 sums without the bias to
+// plane `slice` of `part` ([S][m][n]); linear_split_reduce then adds the
+// planes in slice order.  Taken when the tiles alone would leave most CUs idle.
+template <bool kHalfTail, int GS, bool kSplit = false>
 __global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
     const uint16_t* __restrict__ x, const uint32_t* __restrict__ packed,
     const uint32_t* __restrict__ sign, const float* __restrict__ scale,
     const uint16_t* __restrict__ scale16, const float* __restrict__ bias, int m, int n, int k,
-    int tiles_m, Levels lv, void* __restrict__ y, int y_bf16) {
+    int tiles_m, Levels lv, void* __restrict__ y, int y_bf16, int slice_steps,
+    float* __restrict__ part) {
+  static_assert(!(kSplit && (kHalfTail || GS > 0)), "split-k: per-row scales, k a multiple of 64");
   constexpr int NXS = tiled_x_stages<GS>(), NWS = tiled_w_stages<GS>();
   constexpr int LX = NXS - 1;  // x of step kt + LX is requested in step kt
   // One array per stage: with the stage of every access known at compile time
@@ -433,14 +441,19 @@ __global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
   const int lane = tid & (kWave - 1);
   // uniform across the wave: the LDS destinations of the loads are scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int tile_m = blockIdx.x % tiles_m, tile_n = blockIdx.x / tiles_m;
+  const int ntiles = tiles_m * ((n + kTN - 1) / kTN);
+  const int tile = kSplit ? (int)(blockIdx.x % (unsigned)ntiles) : (int)blockIdx.x;
+  const int slice = kSplit ? (int)(blockIdx.x / (unsigned)ntiles) : 0;
+  const int tile_m = tile % tiles_m, tile_n = tile / tiles_m;
   const int m0 = tile_m * kTM;
   const int n0 = tile_n * kTN;
   const int h = lane >> 5;                         // which half of the k step
   const int rr = wave * 32 + (lane & 31);          // this lane's weight row in the tile
   const int brow = n0 + rr;
   const int kwords = k / 8, swords = k / 32;
-  const int nsteps = (k + kTK - 1) / kTK;
+  const int all_steps = (k + kTK - 1) / kTK;
+  const int s0 = kSplit ? slice * slice_steps : 0;  // first k step of this block
+  const int nsteps = kSplit ? min(slice_steps, all_steps - s0) : all_steps;
 
   // ---- loads.  x: load i of wave w fills 1 KB block 4w + i of a stage, i.e.
   // rows 8(4w + i) .. + 7; lane l the slot (row 8(4w + i) + l/8, chunk l%8).
@@ -464,7 +477,7 @@ __global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
   // chunks past k re-read the step's first half, so only values of the same x
   // row ever meet the zeroed half of the weight fragment.
   auto load_x = [&](int kt, uint8_t* st) __attribute__((always_inline)) {
-    const uint32_t soff = (uint32_t)kt * (kTK * 2);
+    const uint32_t soff = (uint32_t)(kt + s0) * (kTK * 2);
 #pragma unroll
     for (int i = 0; i < kXLoads; ++i) {
       uint32_t off = x_off[i];
@@ -502,12 +515,12 @@ __global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
 #pragma unroll
     for (int i = 0; i < kWCodeLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(p_rsrc, (lds_ptr_t)(st + (kWCodeLoads * wave + i) * 1024),
-                                               16, wc_off[i], (uint32_t)q * 64u, 0, 0);
+                                               16, wc_off[i], (uint32_t)(q + s0 / 2) * 64u, 0, 0);
 #pragma unroll
     for (int i = 0; i < kWSignLoads; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           s_rsrc, (lds_ptr_t)(st + kWCodeBytes + (kWSignLoads * wave + i) * 256), 4, ws_off[i],
-          (uint32_t)q * 16u, 0, 0);
+          (uint32_t)(q + s0 / 2) * 16u, 0, 0);
   };
 
   // ---- the lane's table and code words.
@@ -682,17 +695,20 @@ __global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
   // 32x32 accumulator layout: register e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32.  Whole tiles store without a bound check (nontemporal, as
   // store_y).
-  const float bv = (bias && brow < n) ? bias[brow] : 0.0f;
+  // split-k: float32 sums of this slice, no bias, into its plane of `part`
+  void* yo = kSplit ? static_cast<void*>(part + (int64_t)slice * m * n) : y;
+  const int ybf = kSplit ? 0 : y_bf16;
+  const float bv = (!kSplit && bias && brow < n) ? bias[brow] : 0.0f;
   const bool whole = m0 + kTM <= m && n0 + kTN <= n;
-  if (whole && !y_bf16) {
-    float* yrow = static_cast<float*>(y) + (int64_t)(m0 + 4 * h) * n + brow;
+  if (whole && !ybf) {
+    float* yrow = static_cast<float*>(yo) + (int64_t)(m0 + 4 * h) * n + brow;
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         __builtin_nontemporal_store(acc[mi][e] + bv, yrow + (int64_t)(mi * 32 + 8 * (e >> 2) + (e & 3)) * n);
   } else if (whole) {
-    uint16_t* yrow = static_cast<uint16_t*>(y) + (int64_t)(m0 + 4 * h) * n + brow;
+    uint16_t* yrow = static_cast<uint16_t*>(yo) + (int64_t)(m0 + 4 * h) * n + brow;
 #pragma unroll
     for (int mi = 0; mi < 8; ++mi)
 #pragma unroll
@@ -705,7 +721,7 @@ __global__ __launch_bounds__(kTThreads, 1) void linear_tiled(
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int row = m0 + mi * 32 + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (row < m && brow < n) store_y(y, y_bf16, (int64_t)row * n + brow, acc[mi][e] + bv);
+        if (row < m && brow < n) store_y(yo, ybf, (int64_t)row * n + brow, acc[mi][e] + bv);
       }
   }
 }
@@ -931,9 +947,49 @@ __global__ __launch_bounds__((NMB <= 2 ? 16 : 8) * kWave) void linear_dense_skin
 
 }  // namespace
 
-size_t linear_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
-
 namespace {
+
+// y[mm][c] = sum over s = 0 .. S-1 of part[s][mm][c], in that order, + bias[c]
+// (the split-k planes of linear_tiled).
+__global__ __launch_bounds__(256) void linear_split_reduce(const float* __restrict__ part,
+                                                           int nslice, int64_t count, int n,
+                                                           const float* __restrict__ bias,
+                                                           void* __restrict__ y, int y_bf16) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < count;
+       e += (int64_t)gridDim.x * 256) {
+    float v = part[e];
+    for (int s = 1; s < nslice; ++s) v += part[(int64_t)s * count + e];
+    store_y(y, y_bf16, e, v + (bias ? bias[e % n] : 0.0f));
+  }
+}
+
+constexpr int64_t kPartCUs = 256;                        // the part's CUs
+constexpr int64_t kMaxSplitBytes = int64_t(128) << 20;   // largest partial-sum workspace
+
+// Split-k of the tiled layer (per-row scales, k a multiple of 64): when its
+// tiles would cover at most a quarter of the CUs, S slices of an even number
+// of k steps each, so that about kPartCUs blocks run, each at least 8 steps
+// long.  Returns S (1: no split) and the steps per slice.  Measured against
+// the unsplit grid (or the x-row slices where the call took them), one box,
+// graph replay: n = k = 3840 at m = 256 / 512 / 1024 54 / 71 / 74 -> 32 / 45 /
+// 61 us, 1024 x 3840 x 10240 181 -> 110 us, 130 x 1024 x 8192 48 -> 27 us,
+// 512 x 1024 x 8192 152 -> 34 us.  Not taken for m <= 128 (the x-row slices
+// are faster: m = 65 20 against 28 us) or for more than 64 tiles (m = 2048,
+// n = 3840: 87 unsplit against 91 us).
+int tiled_split(int64_t m, int64_t n, int64_t k, int* slice_steps) {
+  if (m <= 2 * kSkinnyMaxM || n < 1 || k % kTK) return 1;
+  const int64_t tiles = ((m + kTM - 1) / kTM) * ((n + kTN - 1) / kTN);
+  const int64_t steps = k / kTK;
+  if (tiles * 4 > kPartCUs) return 1;
+  int64_t s = std::min(kPartCUs / tiles, steps / 8);
+  if (s < 2) return 1;
+  int64_t sps = (steps + s - 1) / s;
+  sps += sps & 1;
+  s = (steps + sps - 1) / sps;
+  if (s < 2 || s * m * n * 4 > kMaxSplitBytes) return 1;
+  if (slice_steps) *slice_steps = (int)sps;
+  return (int)s;
+}
 
 // Mid-size m (a few 256-row tiles): the tiled kernel's grid then covers few
 // CUs while each tile still walks all of k, and slices of up to 64 x rows
@@ -945,16 +1001,16 @@ namespace {
 // 3840 weights at m = 128 take 27 us as two slices against 76 us tiled, and
 // 20480 x 3840 at m = 65 stay tiled (76 against 82 us).  Both paths are exact
 // to the same tolerance; only the order of the k sum differs.
-bool mid_m_as_slices(int64_t m, int64_t n, int64_t k) {
+bool mid_m_as_slices(int64_t m, int64_t n, int64_t k, bool split_ok = false) {
   if (m <= kSkinnyMaxM) return false;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < 1)
-    return false;
+  const int64_t cus = kPartCUs;  // a function of the shape alone
   const int64_t tiles = ((m + kTM - 1) / kTM) * ((n + kTN - 1) / kTN);
   const int64_t waves = (tiles + cus - 1) / cus;
-  const double tiled_us = (double)waves * (double)((k + kTK - 1) / kTK) * 1.25;
+  double tiled_us = (double)waves * (double)((k + kTK - 1) / kTK) * 1.25;
+  int sps = 0;
+  const int split = split_ok ? tiled_split(m, n, k, &sps) : 1;
+  if (split > 1)  // a slice's steps, plus the reduce: a launch and the planes' bytes
+    tiled_us = sps * 1.25 + 12.0 + (double)split * m * n * 8 / 4e6;
   const double slices = (double)((m + kSkinnyMaxM - 1) / kSkinnyMaxM);
   const double sliced_us = slices * (3.0 + 0.75e-3 * (double)n * (double)k / 1000.0);
   return sliced_us < tiled_us;
@@ -964,14 +1020,14 @@ template <int GS>
 hipError_t launch_linear_any(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                              const float* scale, const uint16_t* scale16, const float* bias,
                              int64_t m, int64_t n, int64_t k, const Levels& lv, void* y,
-                             bool y_bf16, hipStream_t stream) {
-  if (mid_m_as_slices(m, n, k)) {
+                             bool y_bf16, float* part, hipStream_t stream) {
+  if (mid_m_as_slices(m, n, k, GS == 0)) {
     const int64_t ybytes = y_bf16 ? 2 : 4;
     for (int64_t r = 0; r < m; r += kSkinnyMaxM) {
       const int64_t mm = m - r < kSkinnyMaxM ? m - r : kSkinnyMaxM;
       const hipError_t e = launch_linear_any<GS>(x + r * k, packed, sign, scale, scale16, bias, mm,
                                                  n, k, lv, static_cast<char*>(y) + r * n * ybytes,
-                                                 y_bf16, stream);
+                                                 y_bf16, part, stream);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -1001,10 +1057,22 @@ hipError_t launch_linear_any(const uint16_t* x, const uint32_t* packed, const ui
                        sign, scale, scale16, bias, (int)m, (int)n, (int)k, lv, y, (int)y_bf16);
   } else {
     const int64_t tiles_m = (m + kTM - 1) / kTM, tiles_n = (n + kTN - 1) / kTN;
+    int sps = 0;
+    const int split = GS == 0 ? tiled_split(m, n, k, &sps) : 1;
+    if (split > 1) {
+      hipLaunchKernelGGL((linear_tiled<false, GS, (GS == 0)>), dim3((unsigned)(tiles_m * tiles_n * split)),
+                         dim3(kTThreads), 0, stream, x, packed, sign, scale, scale16, bias, (int)m,
+                         (int)n, (int)k, (int)tiles_m, lv, y, (int)y_bf16, sps, part);
+      const int64_t count = m * n;
+      const int64_t rb = std::min<int64_t>((count + 255) / 256, 8192);
+      hipLaunchKernelGGL(linear_split_reduce, dim3((unsigned)rb), dim3(256), 0, stream, part, split,
+                         count, (int)n, bias, y, (int)y_bf16);
+      return hipGetLastError();
+    }
     auto kernel = (k % kTK) ? linear_tiled<true, GS> : linear_tiled<false, GS>;
     hipLaunchKernelGGL(kernel, dim3((unsigned)(tiles_m * tiles_n)), dim3(kTThreads), 0, stream, x,
                        packed, sign, scale, scale16, bias, (int)m, (int)n, (int)k, (int)tiles_m,
-                       lv, y, (int)y_bf16);
+                       lv, y, (int)y_bf16, 0, nullptr);
   }
   return hipGetLastError();
 }
@@ -1013,9 +1081,20 @@ hipError_t launch_linear_any(const uint16_t* x, const uint32_t* packed, const ui
 
 hipError_t launch_linear(const uint16_t* x, const uint32_t* packed, const uint32_t* sign,
                          const float* scale, const float* bias, int64_t m, int64_t n, int64_t k,
-                         const Levels& lv, void* y, bool y_bf16, void*, hipStream_t stream) {
+                         const Levels& lv, void* y, bool y_bf16, void* workspace,
+                         hipStream_t stream) {
   return launch_linear_any<0>(x, packed, sign, scale, nullptr, bias, m, n, k, lv, y, y_bf16,
-                              stream);
+                              static_cast<float*>(workspace), stream);
+}
+
+// The split-k partial sums of the tiled layer (per-row scales): S planes of
+// m x n float32; none for every other path, mid-size m run as slices of x
+// rows through the skinny kernel included.
+size_t linear_workspace_bytes(int64_t m, int64_t n, int64_t k) {
+  if (m <= kSkinnyMaxM || mid_m_as_slices(m, n, k, true)) return 0;
+  const int split = tiled_split(m, n, k, nullptr);
+  if (split <= 1) return 0;
+  return ((size_t)split * (size_t)m * (size_t)n * 4u + 255u) & ~size_t(255);
 }
 
 hipError_t launch_linear_dense(const uint16_t* x, const uint16_t* wd, const float* bias, int64_t m,
@@ -1082,7 +1161,7 @@ hipError_t launch_linear_grouped(const uint16_t* x, const uint32_t* packed, cons
 #define OPQ_GROUP_CASE(G)                                                                       \
   case G:                                                                                       \
     return launch_linear_any<G>(x, packed, sign, nullptr, scale16, bias, m, n, k, lv, y, y_bf16, \
-                                stream);
+                                nullptr, stream);
   switch (gs) {
     OPQ_GROUP_CASE(32)
     OPQ_GROUP_CASE(64)

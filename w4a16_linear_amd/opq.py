@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libopq.so")
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 OPQ_F32 = 0
 OPQ_BF16 = 1
