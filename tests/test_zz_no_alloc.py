@@ -49,7 +49,9 @@ def test_noalloc_two_calls_second_smaller(gpu_lib):
 
 
 def test_noalloc_each_width_and_4bit(gpu_lib):
-    """Widths 6 and 4 (the latter is opq_linear, no scratch), larger then smaller."""
+    """Widths 6 and 4, larger then smaller.  Width 4 is opq_linear: 200 x 640 x
+    1024 splits k over the tiles and keeps its partial sums in the scratch,
+    8 x 96 x 256 needs none."""
     for bits, m, n, k in ((6, 130, 1500, 2048), (6, 33, 100, 160), (4, 200, 640, 1024),
                           (4, 8, 96, 256)):
         _case(gpu_lib, m, n, k, bits, 1.0, 2620 + bits + m)
