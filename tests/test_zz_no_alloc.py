@@ -49,11 +49,13 @@ def test_noalloc_two_calls_second_smaller(gpu_lib):
 
 
 def test_noalloc_each_width_and_4bit(gpu_lib):
-    """Widths 6 and 4, larger then smaller.  Width 4 is opq_linear: 200 x 640 x
-    1024 splits k over the tiles and keeps its partial sums in the scratch,
-    8 x 96 x 256 needs none."""
-    for bits, m, n, k in ((6, 130, 1500, 2048), (6, 33, 100, 160), (4, 200, 640, 1024),
-                          (4, 8, 96, 256)):
+    """Widths 6 and 4, larger then smaller.  Width 4 is opq_linear: 300 x 1000 x
+    4096 splits k over the tiles and keeps its partial sums in the scratch,
+    200 x 640 x 1024 and 8 x 96 x 256 need none."""
+    assert gpu_lib.linear_workspace_bytes(300, 1000, 4096) > 0
+    assert gpu_lib.linear_workspace_bytes(200, 640, 1024) == 0
+    for bits, m, n, k in ((6, 130, 1500, 2048), (6, 33, 100, 160), (4, 300, 1000, 4096),
+                          (4, 200, 640, 1024), (4, 8, 96, 256)):
         _case(gpu_lib, m, n, k, bits, 1.0, 2620 + bits + m)
 
 
