@@ -1,5 +1,6 @@
 """The library's calls under HIP graph capture: quantize, dequantize and the
-linear layer (per-row and group-wise, skinny and tiled) captured once in a
+linear layer (per-row and group-wise, skinny and tiled, and the tiled layer
+with k split over a workspace and a second, reducing kernel) captured once in a
 torch CUDA graph and replayed several times, with eager work and
 synchronisations between the replays; every replay's outputs equal the eager
 call's bit for bit (the calls enqueue kernels only, no memset or copy)."""
@@ -15,7 +16,7 @@ pytestmark = pytest.mark.gpu
 ALPHA = 0.73
 
 
-def _eager(opq, w, x_small, x_big, group):
+def _eager(opq, w, x_small, x_big, x_split, group):
     if group:
         qw = opq.quantize_grouped(w, ALPHA, group)
     else:
@@ -23,8 +24,9 @@ def _eager(opq, w, x_small, x_big, group):
     d = opq.dequantize(qw, ALPHA)
     ys = opq.linear(x_small, qw, ALPHA)
     yb = opq.linear(x_big, qw, ALPHA)
+    yk = opq.linear(x_split, qw, ALPHA)
     torch.cuda.synchronize()
-    return qw, d, ys, yb
+    return qw, d, ys, yb, yk
 
 
 @pytest.mark.parametrize("group", [0, 128])
@@ -34,7 +36,10 @@ def test_graph_replays_match_eager(gpu_lib, group):
     _, w = weight_tensor(WL.student_t(2100 + group, (n, k)), "bf16")
     x_small = WL.to_bf16(WL.normal(2200, (16, k))).to(DEV)
     x_big = WL.to_bf16(WL.normal(2201, (300, k))).to(DEV)
-    qw_ref, d_ref, ys_ref, yb_ref = _eager(opq, w, x_small, x_big, group)
+    x_split = WL.to_bf16(WL.normal(2202, (1024, k))).to(DEV)
+    if not group:  # per-row scales: the 1024-row call splits k
+        assert opq.linear_workspace_bytes(1024, n, k) > 0
+    qw_ref, d_ref, ys_ref, yb_ref, yk_ref = _eager(opq, w, x_small, x_big, x_split, group)
 
     # static outputs the captured calls write into
     if group:
@@ -46,6 +51,7 @@ def test_graph_replays_match_eager(gpu_lib, group):
     d = torch.empty_like(d_ref)
     ys = torch.empty_like(ys_ref)
     yb = torch.empty_like(yb_ref)
+    yk = torch.empty_like(yk_ref)
 
     def calls():
         if group:
@@ -55,6 +61,7 @@ def test_graph_replays_match_eager(gpu_lib, group):
         opq.dequantize(qw, ALPHA, out=d)
         opq.linear(x_small, qw, ALPHA, out=ys)
         opq.linear(x_big, qw, ALPHA, out=yb)
+        opq.linear(x_split, qw, ALPHA, out=yk)
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -67,7 +74,7 @@ def test_graph_replays_match_eager(gpu_lib, group):
     torch.cuda.synchronize()
 
     for rep in range(3):
-        for t in (qw.packed, qw.sign, d, ys, yb):
+        for t in (qw.packed, qw.sign, d, ys, yb, yk):
             t.zero_()  # eager work between replays
         torch.cuda.synchronize()
         g.replay()
@@ -81,3 +88,4 @@ def test_graph_replays_match_eager(gpu_lib, group):
         assert torch.equal(d, d_ref), rep
         assert torch.equal(ys, ys_ref), rep
         assert torch.equal(yb, yb_ref), rep
+        assert torch.equal(yk, yk_ref), rep
