@@ -406,6 +406,14 @@ def main():
             for kind in kinds:
                 launch(p, kind, i)
 
+    # Every buffer set once through each kernel before the warmup steps: the
+    # first pass over freshly allocated buffers runs several times slower than
+    # the passes after it (4.9 against 0.94 ms per FFN step), which is not the
+    # kernels' own work, and the warmup steps alone reach only the first sets.
+    for p in plan:
+        for s in range(p["rot"]):
+            for kind in kinds:
+                launch(p, kind, s)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
