@@ -182,8 +182,8 @@ def stream_ceiling_us(dev, stream, rows, rd, wr, reps, graph=False):
     lib = ceiling_lib()
     per = rows * max(rd, 16)
     pairs = max(2, int(np.ceil(800e6 / per)))
-    bufs = [(torch.empty(max(rows * rd, 16), dtype=torch.uint8, device=dev),
-             torch.empty(max(rows * wr, 16), dtype=torch.uint8, device=dev)) for _ in range(pairs)]
+    bufs = [(torch.zeros(max(rows * rd, 16), dtype=torch.uint8, device=dev),
+             torch.zeros(max(rows * wr, 16), dtype=torch.uint8, device=dev)) for _ in range(pairs)]
     def call(i):
         a, b = bufs[i % pairs]
         h = torch.cuda.current_stream(dev).cuda_stream  # the capture stream inside a graph
@@ -363,25 +363,27 @@ def main():
         least = min(alg["quantize"]["read"], alg["dequantize"]["read"],
                     alg["linear"]["read"])
         rot = args.rotate or max(2, int(np.ceil(800e6 / least)))
+        # outputs are allocated zero-filled, so that a fill kernel and not a
+        # measured kernel meets each freshly allocated buffer first
         sets = []
         for _ in range(rot):
             w = w_host.to(dev)
             if bits != 4:
-                qw = opq.BitsWeight(torch.empty((n, k * bits // 32), dtype=torch.int32, device=dev),
-                                    torch.empty((n, k // 32), dtype=torch.int32, device=dev),
-                                    torch.empty((n,), dtype=torch.float32, device=dev), bits)
+                qw = opq.BitsWeight(torch.zeros((n, k * bits // 32), dtype=torch.int32, device=dev),
+                                    torch.zeros((n, k // 32), dtype=torch.int32, device=dev),
+                                    torch.zeros((n,), dtype=torch.float32, device=dev), bits)
             elif group:
-                qw = opq.GroupedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
-                                       torch.empty((n, k // 32), dtype=torch.int32, device=dev),
-                                       torch.empty((n, k // group), dtype=torch.float16,
+                qw = opq.GroupedWeight(torch.zeros((n, k // 8), dtype=torch.int32, device=dev),
+                                       torch.zeros((n, k // 32), dtype=torch.int32, device=dev),
+                                       torch.zeros((n, k // group), dtype=torch.float16,
                                                    device=dev), group)
             else:
-                qw = opq.QuantizedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
-                                         torch.empty((n, k // 32), dtype=torch.int32, device=dev),
-                                         torch.empty((n,), dtype=torch.float32, device=dev))
-            d = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+                qw = opq.QuantizedWeight(torch.zeros((n, k // 8), dtype=torch.int32, device=dev),
+                                         torch.zeros((n, k // 32), dtype=torch.int32, device=dev),
+                                         torch.zeros((n,), dtype=torch.float32, device=dev))
+            d = torch.zeros((n, k), dtype=torch.bfloat16, device=dev)
             x = x_host.to(dev)
-            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+            y = torch.zeros((m, n), dtype=torch.float32, device=dev)
             sets.append((w, qw, d, x, y))
         plan.append({"tag": tag, "L": L, "alg": alg, "rot": rot, "sets": sets,
                      "w_bytes": w_bytes})
@@ -501,8 +503,8 @@ def main():
                 continue
             half = rec["algorithmic_bytes"] // 2
             pairs = max(2, int(np.ceil(800e6 / half)))  # > 800 MB read between repeats
-            bufs = [(torch.empty(half, dtype=torch.uint8, device=dev),
-                     torch.empty(half, dtype=torch.uint8, device=dev)) for _ in range(pairs)]
+            bufs = [(torch.zeros(half, dtype=torch.uint8, device=dev),
+                     torch.zeros(half, dtype=torch.uint8, device=dev)) for _ in range(pairs)]
 
             def cp(i):
                 dst, src = bufs[i % pairs]
@@ -526,8 +528,8 @@ def main():
 
     if args.copy_mib:
         # A plain device copy of known size, for scaling the HBM byte counters.
-        src = torch.empty(args.copy_mib << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
+        src = torch.zeros(args.copy_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.zeros_like(src)
         for _ in range(5):
             dst.copy_(src)
         torch.cuda.synchronize()
@@ -615,11 +617,11 @@ def model_pass(args, dev):
     weights, qws, outs = [], [], {}
     for _, seed, n, k in shapes:
         weights.append(WL.student_t_device(seed, (n, k), dev))
-        qws.append(opq.QuantizedWeight(torch.empty((n, k // 8), dtype=torch.int32, device=dev),
-                                       torch.empty((n, k // 32), dtype=torch.int32, device=dev),
-                                       torch.empty((n,), dtype=torch.float32, device=dev)))
+        qws.append(opq.QuantizedWeight(torch.zeros((n, k // 8), dtype=torch.int32, device=dev),
+                                       torch.zeros((n, k // 32), dtype=torch.int32, device=dev),
+                                       torch.zeros((n,), dtype=torch.float32, device=dev)))
         if (n, k) not in outs:  # one bf16 output per shape: the pass rewrites it per layer
-            outs[(n, k)] = torch.empty((n, k), dtype=torch.bfloat16, device=dev)
+            outs[(n, k)] = torch.zeros((n, k), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     nweights = sum(n * k for _, _, n, k in shapes)
     alg_q = sum(n * k * 2.625 + 4 * n for _, _, n, k in shapes)
